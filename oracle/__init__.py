@@ -1,0 +1,258 @@
+"""Python front end of the fp64 CPU oracle (``oracle/mla_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Imported by ``tests/``, by the smoke check in
+``__graft_entry__`` and by the CPU-baseline leg of ``bench.py``; never by the
+product package, which must fail rather than fall back to it.  It shares no
+code with the HIP library.
+
+Arrays cross the boundary as numpy arrays: bf16 tensors as their ``uint16``
+bit patterns (widened exactly inside the oracle), angle tables as float32,
+results as float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mla_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc: no fast-math and no contraction into FMA,
+    so every double operation is the one written in the source."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wno-unused-function", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    D = ctypes.c_double
+    lib.oracle_bf16_round.argtypes = [D]
+    lib.oracle_bf16_round.restype = D
+    lib.oracle_bf16_round_array.argtypes = [P, P, ctypes.c_size_t]
+    lib.oracle_bf16_widen_array.argtypes = [P, P, ctypes.c_size_t]
+    lib.oracle_dims.argtypes = [P, P, P]
+    lib.oracle_rope_rotate.argtypes = [P, P, I, P, I, P, P]
+    lib.oracle_rope_rotate.restype = I
+    lib.oracle_prefill.argtypes = [P, P, P, P, P, P, I, D, I, I, I, P, P, I]
+    lib.oracle_prefill.restype = I
+    lib.oracle_prefill_rows.argtypes = [P, P, P, P, P, P, I, D, I, I, I, I, P, P, P, I]
+    lib.oracle_prefill_rows.restype = I
+    lib.oracle_decode.argtypes = [P, P, P, P, P, I, I, D, I, I, I, P, P, I]
+    lib.oracle_decode.restype = I
+    lib.oracle_decode_rows.argtypes = [P, P, P, P, P, I, I, D, I, I, I, I, P, P, P, I]
+    lib.oracle_decode_rows.restype = I
+    lib.oracle_out_proj.argtypes = [P, P, I, I, I, P, I]
+    lib.oracle_out_proj.restype = I
+    lib.oracle_out_proj_rows.argtypes = [P, P, I, I, I, I, P, P, I]
+    lib.oracle_out_proj_rows.restype = I
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError(f"expected bf16 bit patterns as uint16, got {a.dtype}")
+    return a
+
+
+def _f32(a) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def dims():
+    lib = _load()
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    lib.oracle_dims(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    return a.value, b.value, c.value
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round doubles to the nearest bf16 value (ties to even), returned as doubles."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    lib.oracle_bf16_round_array(_p(x), _p(y), x.size)
+    return y
+
+
+def bf16_widen(bits) -> np.ndarray:
+    lib = _load()
+    bits = _u16(bits)
+    y = np.empty(bits.shape, dtype=np.float64)
+    lib.oracle_bf16_widen_array(_p(bits), _p(y), bits.size)
+    return y
+
+
+def rope_rotate(x_bits, R, pos):
+    """Rotate rows of 64 bf16 values (shape [..., 64]) at positions ``pos``
+    (shape [...]).  Returns (double result before rounding, bf16 bits after)."""
+    lib = _load()
+    x_bits = _u16(x_bits)
+    R = _f32(R)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    n = pos.size
+    if x_bits.size != n * 64:
+        raise ValueError("x must hold 64 values per position")
+    f64 = np.empty(x_bits.shape, dtype=np.float64)
+    b16 = np.empty(x_bits.shape, dtype=np.uint16)
+    rc = lib.oracle_rope_rotate(_p(x_bits), _p(R), R.shape[0], _p(pos), n, _p(f64), _p(b16))
+    if rc:
+        raise ValueError("position outside the angle table")
+    return f64, b16
+
+
+def prefill(q_nope, q_pe, k_nope, k_pe, v, R, scale, nthreads=None, want_lse=True):
+    """Full causal prefill.  Shapes: q_nope/k_nope/v [B,H,T,128], q_pe
+    [B,H,T,64], k_pe [B,1,T,64], R [>=T,32].  Returns out [B,T,H*128] (double)
+    and lse [B,H,T] (or None)."""
+    lib = _load()
+    q_nope, q_pe, k_nope, k_pe, v = map(_u16, (q_nope, q_pe, k_nope, k_pe, v))
+    R = _f32(R)
+    B, H, T, _ = q_nope.shape
+    _check_prefill_shapes(q_nope, q_pe, k_nope, k_pe, v, B, H, T)
+    out = np.empty((B, T, H * 128), dtype=np.float64)
+    lse = np.empty((B, H, T), dtype=np.float64) if want_lse else None
+    rc = lib.oracle_prefill(_p(q_nope), _p(q_pe), _p(k_nope), _p(k_pe), _p(v), _p(R), R.shape[0],
+                            float(scale), B, H, T, _p(out), _p(lse) if want_lse else None,
+                            nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_prefill failed ({rc})")
+    return out, lse
+
+
+def prefill_rows(q_nope, q_pe, k_nope, k_pe, v, R, scale, sel, nthreads=None):
+    """Selected rows: ``sel`` is an int array [n,3] of (b, h, t).  Returns
+    out [n,128] and lse [n]."""
+    lib = _load()
+    q_nope, q_pe, k_nope, k_pe, v = map(_u16, (q_nope, q_pe, k_nope, k_pe, v))
+    R = _f32(R)
+    B, H, T, _ = q_nope.shape
+    _check_prefill_shapes(q_nope, q_pe, k_nope, k_pe, v, B, H, T)
+    sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 3)
+    n = sel.shape[0]
+    out = np.empty((n, 128), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = lib.oracle_prefill_rows(_p(q_nope), _p(q_pe), _p(k_nope), _p(k_pe), _p(v), _p(R),
+                                 R.shape[0], float(scale), B, H, T, n, _p(sel), _p(out), _p(lse),
+                                 nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_prefill_rows failed ({rc})")
+    return out, lse
+
+
+def decode(q_nope, q_pe, k_cache, v_cache, R, q_pos, scale, nthreads=None):
+    """Decode one query per (b, h) over L cached, already rotated keys.
+    Shapes: q_nope [B,H,128], q_pe [B,H,64], k_cache [B,H,L,192], v_cache
+    [B,H,L,128].  Returns out [B,H*128] and lse [B,H]."""
+    lib = _load()
+    q_nope, q_pe, k_cache, v_cache = map(_u16, (q_nope, q_pe, k_cache, v_cache))
+    R = _f32(R)
+    B, H, L, _ = k_cache.shape
+    _check_decode_shapes(q_nope, q_pe, k_cache, v_cache, B, H, L)
+    out = np.empty((B, H * 128), dtype=np.float64)
+    lse = np.empty((B, H), dtype=np.float64)
+    rc = lib.oracle_decode(_p(q_nope), _p(q_pe), _p(k_cache), _p(v_cache), _p(R), R.shape[0],
+                           int(q_pos), float(scale), B, H, L, _p(out), _p(lse),
+                           nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_decode failed ({rc})")
+    return out, lse
+
+
+def decode_rows(q_nope, q_pe, k_cache, v_cache, R, q_pos, scale, sel, nthreads=None):
+    lib = _load()
+    q_nope, q_pe, k_cache, v_cache = map(_u16, (q_nope, q_pe, k_cache, v_cache))
+    R = _f32(R)
+    B, H, L, _ = k_cache.shape
+    _check_decode_shapes(q_nope, q_pe, k_cache, v_cache, B, H, L)
+    sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 2)
+    n = sel.shape[0]
+    out = np.empty((n, 128), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = lib.oracle_decode_rows(_p(q_nope), _p(q_pe), _p(k_cache), _p(v_cache), _p(R),
+                                R.shape[0], int(q_pos), float(scale), B, H, L, n, _p(sel),
+                                _p(out), _p(lse), nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_decode_rows failed ({rc})")
+    return out, lse
+
+
+def out_proj(x, w, nthreads=None):
+    """y = x · wᵀ with x [M,K] and w [N,K] (bf16 bits); returns y [M,N] double."""
+    lib = _load()
+    x, w = _u16(x), _u16(w)
+    M, K = x.shape
+    N, K2 = w.shape
+    if K != K2:
+        raise ValueError("inner sizes differ")
+    y = np.empty((M, N), dtype=np.float64)
+    rc = lib.oracle_out_proj(_p(x), _p(w), M, K, N, _p(y), nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_out_proj failed ({rc})")
+    return y
+
+
+def out_proj_rows(x, w, rows, nthreads=None):
+    lib = _load()
+    x, w = _u16(x), _u16(w)
+    M, K = x.shape
+    N, K2 = w.shape
+    if K != K2:
+        raise ValueError("inner sizes differ")
+    rows = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1)
+    y = np.empty((rows.size, N), dtype=np.float64)
+    rc = lib.oracle_out_proj_rows(_p(x), _p(w), M, K, N, rows.size, _p(rows), _p(y),
+                                  nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_out_proj_rows failed ({rc})")
+    return y
+
+
+def _check_prefill_shapes(q_nope, q_pe, k_nope, k_pe, v, B, H, T):
+    want = {"q_nope": (B, H, T, 128), "q_pe": (B, H, T, 64), "k_nope": (B, H, T, 128),
+            "k_pe": (B, 1, T, 64), "v": (B, H, T, 128)}
+    for name, arr in zip(want, (q_nope, q_pe, k_nope, k_pe, v)):
+        if tuple(arr.shape) != want[name]:
+            raise ValueError(f"{name} has shape {arr.shape}, expected {want[name]}")
+
+
+def _check_decode_shapes(q_nope, q_pe, k_cache, v_cache, B, H, L):
+    want = {"q_nope": (B, H, 128), "q_pe": (B, H, 64), "k_cache": (B, H, L, 192),
+            "v_cache": (B, H, L, 128)}
+    for name, arr in zip(want, (q_nope, q_pe, k_cache, v_cache)):
+        if tuple(arr.shape) != want[name]:
+            raise ValueError(f"{name} has shape {arr.shape}, expected {want[name]}")

@@ -1,0 +1,445 @@
+/*
+ * Plain fp64 CPU oracle for Kimi K2's latent-attention (MLA) attend-and-combine
+ * step.  TEST INFRASTRUCTURE ONLY: it is loaded by the tests, by the smoke
+ * check and by the benchmark's CPU-baseline leg, never by the product path.
+ * It shares no code, header, table or constant with the HIP library.
+ *
+ * What it computes is the plain definition of the step, evaluated in double
+ * precision on bf16 inputs that are widened exactly.  Sources (the pages):
+ *   [MIX]    page "Kimi K2 · Mix and project": the I/O header (A, V -> delta_attn),
+ *            the output-projection parameter table (8,192 x 7,168), the remark
+ *            that the projection is the only step mixing heads, and the code
+ *            excerpts "mla-prefill" (rotary, query/key join with the shared
+ *            rotary key, scaled scores, additive mask, fp32 softmax, value mix)
+ *            and "mla-output" (head transpose, flatten to 64*128, o_proj).
+ *   [BLOCKS] page "Kimi K2 · Transformer blocks": block-stack I/O header
+ *            (R [T positions, 32 pairs], M [T queries, T keys]) and the model-body
+ *            excerpt that numbers positions from the cached length and builds
+ *            the causal mask.
+ *   [CONFIG] page "Block input", config.json excerpt: 64 heads, nope 128,
+ *            rope 64, value 128, hidden 7168, attention_bias false, bfloat16.
+ *
+ * Rounding points (where the eager model holds a tensor in bf16 and the value
+ * is a model-visible input of the next step):
+ *   R1  rotated q_pe / k_pe are stored in the bf16 query/key tensors ([MIX],
+ *       "mla-prefill": query_states / key_states are built from them).
+ *   R2  the flattened attention output enters o_proj as bf16 ([MIX], "mla-output").
+ * Every other intermediate (scores, softmax weights, sums) stays in fp64.
+ * Rounding is round-to-nearest-even, done directly from double.
+ *
+ * Threads: independent output rows are handed out to pthreads through an
+ * atomic counter.  Each row is computed exactly as the definition states, in
+ * key order; threads change nothing in the arithmetic of a row.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* Head widths, from [CONFIG]: qk_nope_head_dim, qk_rope_head_dim, v_head_dim. */
+#define OR_NOPE 128
+#define OR_ROPE 64
+#define OR_PAIRS 32
+#define OR_VDIM 128
+
+int oracle_dims(int *d_nope, int *d_rope, int *d_v) {
+  *d_nope = OR_NOPE;
+  *d_rope = OR_ROPE;
+  *d_v = OR_VDIM;
+  return 0;
+}
+
+/* ---------------------------------------------------------------- bf16 ---- */
+
+/* Exact widening of a bf16 bit pattern (the upper half of an IEEE binary32). */
+static double widen(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Round a double to the nearest bf16 value, ties to even, without passing
+ * through binary32 (which could round twice).  bf16 keeps 8 significant bits
+ * and binary32's exponent range: spacing 2^(e-8) for |x| in [2^(e-1), 2^e),
+ * and 2^-133 for subnormals. */
+double oracle_bf16_round(double x) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e;
+  frexp(x, &e);
+  int es = e - 8;
+  if (es < -133) es = -133;
+  double q = ldexp(x, -es);
+  double r = nearbyint(q); /* default rounding mode: nearest, ties to even */
+  return ldexp(r, es);
+}
+
+/* bf16 bit pattern of oracle_bf16_round(x); finite inputs only. */
+static uint16_t bf16_bits(double x) {
+  float f = (float)oracle_bf16_round(x); /* exact: the value is a bf16 value */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+void oracle_bf16_round_array(const double *x, double *y, size_t n) {
+  for (size_t i = 0; i < n; i++) y[i] = oracle_bf16_round(x[i]);
+}
+
+void oracle_bf16_widen_array(const uint16_t *x, double *y, size_t n) {
+  for (size_t i = 0; i < n; i++) y[i] = widen(x[i]);
+}
+
+/* ------------------------------------------------------------- rotary ---- */
+
+/* Rotary step of [MIX] "mla-prefill" (the rotary embedding and its
+ * application to q_pe and k_pe; the bodies are not printed).  Reading used:
+ * pair i couples elements i and i+32 of the 64-wide rotary part ("rotate
+ * half"), the angle of pair i at position t is R[t][i] (the [BLOCKS] input
+ * R [T positions, 32 pairs]), and the pair turns by that angle:
+ *   y_i    = x_i cos - x_{i+32} sin
+ *   y_{i+32} = x_{i+32} cos + x_i sin
+ * cos and sin are taken in double of the binary32 angle.  `out` receives the
+ * double result before rounding point R1. */
+void oracle_rotate_row(const double *x, const float *R_row, double *out) {
+  for (int i = 0; i < OR_PAIRS; i++) {
+    double a = (double)R_row[i];
+    double c = cos(a), s = sin(a);
+    double lo = x[i], hi = x[i + OR_PAIRS];
+    out[i] = lo * c - hi * s;
+    out[i + OR_PAIRS] = hi * c + lo * s;
+  }
+}
+
+/* Rotate n rows of 64 bf16 values, row r at position pos[r]; writes both the
+ * unrounded double result and its bf16 (R1) bit pattern.  Returns 1 if a
+ * position is outside the table. */
+int oracle_rope_rotate(const uint16_t *x, const float *R, int r_rows, const int *pos, int n,
+                       double *out_f64, uint16_t *out_bf16) {
+  double row[OR_ROPE], rot[OR_ROPE];
+  for (int r = 0; r < n; r++) {
+    if (pos[r] < 0 || pos[r] >= r_rows) return 1;
+    for (int d = 0; d < OR_ROPE; d++) row[d] = widen(x[(size_t)r * OR_ROPE + d]);
+    oracle_rotate_row(row, R + (size_t)pos[r] * OR_PAIRS, rot);
+    for (int d = 0; d < OR_ROPE; d++) {
+      if (out_f64) out_f64[(size_t)r * OR_ROPE + d] = rot[d];
+      if (out_bf16) out_bf16[(size_t)r * OR_ROPE + d] = bf16_bits(rot[d]);
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------ thread helper ---- */
+
+typedef void (*unit_fn)(void *ctx, long unit, double *scratch);
+
+typedef struct {
+  unit_fn fn;
+  void *ctx;
+  long n_units;
+  long next; /* atomic */
+  size_t scratch_doubles;
+  int failed;
+} pool_t;
+
+static void *pool_worker(void *arg) {
+  pool_t *p = (pool_t *)arg;
+  double *scratch = (double *)malloc(p->scratch_doubles * sizeof(double) + 64);
+  if (!scratch) {
+    __atomic_store_n(&p->failed, 1, __ATOMIC_SEQ_CST);
+    return NULL;
+  }
+  for (;;) {
+    long u = __atomic_fetch_add(&p->next, 1, __ATOMIC_RELAXED);
+    if (u >= p->n_units) break;
+    p->fn(p->ctx, u, scratch);
+  }
+  free(scratch);
+  return NULL;
+}
+
+static int run_units(unit_fn fn, void *ctx, long n_units, size_t scratch_doubles, int nthreads) {
+  pool_t p = {fn, ctx, n_units, 0, scratch_doubles, 0};
+  if (nthreads <= 0) nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if ((long)nthreads > n_units) nthreads = (int)(n_units > 0 ? n_units : 1);
+  pthread_t th[256];
+  int started = 0;
+  for (int i = 1; i < nthreads; i++) {
+    if (pthread_create(&th[i], NULL, pool_worker, &p) != 0) break;
+    started = i;
+  }
+  pool_worker(&p);
+  for (int i = 1; i <= started; i++) pthread_join(th[i], NULL);
+  return p.failed ? 2 : 0;
+}
+
+/* ---------------------------------------------------------- attention ---- */
+
+/* One query row against keys 0..n_keys-1, the plain definition of [MIX]
+ * "mla-prefill" from the scores on:
+ *   s_j  = scale * (sum_{d<128} qn_d kn_jd + sum_{d<64} qr_d kr_jd)
+ *   p_j  = exp(s_j - m) / sum_k exp(s_k - m),   m = max_j s_j
+ *   o    = sum_j p_j v_j
+ *   lse  = m + log sum_k exp(s_k - m)
+ * qn (128) and qr (64, rotated and rounded) are doubles; key j's parts are
+ * kn(j), kr(j) and its value row v(j).  Masked keys are simply absent: the
+ * caller passes only the visible ones (a masked weight is exactly 0).
+ * s holds n_keys scratch doubles. */
+typedef struct {
+  const uint16_t *base;
+  long stride; /* elements between consecutive key rows */
+} rows_t;
+
+static void attend_row(const double *qn, const double *qr, rows_t kn, const double *kr_rot,
+                       long kr_stride, rows_t v, long n_keys, double scale, double *s,
+                       double *o, double *lse) {
+  double m = -INFINITY;
+  for (long j = 0; j < n_keys; j++) {
+    const uint16_t *knj = kn.base + j * kn.stride;
+    const double *krj = kr_rot + j * kr_stride;
+    double dot_n = 0.0, dot_r = 0.0;
+    for (int d = 0; d < OR_NOPE; d++) dot_n += qn[d] * widen(knj[d]);
+    for (int d = 0; d < OR_ROPE; d++) dot_r += qr[d] * krj[d];
+    s[j] = scale * (dot_n + dot_r);
+    if (s[j] > m) m = s[j];
+  }
+  double denom = 0.0;
+  for (long j = 0; j < n_keys; j++) denom += exp(s[j] - m);
+  for (int d = 0; d < OR_VDIM; d++) o[d] = 0.0;
+  for (long j = 0; j < n_keys; j++) {
+    double p = exp(s[j] - m) / denom;
+    const uint16_t *vj = v.base + j * v.stride;
+    for (int d = 0; d < OR_VDIM; d++) o[d] += p * widen(vj[d]);
+  }
+  if (lse) *lse = m + log(denom);
+}
+
+/* ------------------------------------------------------------ prefill ---- */
+
+typedef struct {
+  const uint16_t *q_nope, *q_pe, *k_nope, *v;
+  const double *kr_rot; /* [B][T][64]: rotated shared key, already rounded (R1) */
+  const float *R;
+  double scale;
+  int B, H, T;
+  const int *sel; /* NULL: every (b,h,t); else n_sel triples */
+  double *out;    /* full: [B][T][H*128]; rows: [n_sel][128] */
+  double *lse;    /* full: [B][H][T]; rows: [n_sel] */
+} prefill_ctx;
+
+static void prefill_unit(void *vctx, long unit, double *scratch) {
+  prefill_ctx *c = (prefill_ctx *)vctx;
+  int b, h, t;
+  if (c->sel) {
+    b = c->sel[3 * unit];
+    h = c->sel[3 * unit + 1];
+    t = c->sel[3 * unit + 2];
+  } else {
+    t = (int)(unit % c->T);
+    h = (int)((unit / c->T) % c->H);
+    b = (int)(unit / ((long)c->T * c->H));
+  }
+  const long bh = (long)b * c->H + h;
+  double qn[OR_NOPE], qpe[OR_ROPE], qr[OR_ROPE], o[OR_VDIM], l;
+  const uint16_t *qn_src = c->q_nope + (bh * c->T + t) * OR_NOPE;
+  const uint16_t *qp_src = c->q_pe + (bh * c->T + t) * OR_ROPE;
+  for (int d = 0; d < OR_NOPE; d++) qn[d] = widen(qn_src[d]);
+  for (int d = 0; d < OR_ROPE; d++) qpe[d] = widen(qp_src[d]);
+  /* The query sits at position t (positions start at the cached length, here
+   * 0, [BLOCKS] model body); rotate, then round (R1). */
+  oracle_rotate_row(qpe, c->R + (size_t)t * OR_PAIRS, qr);
+  for (int d = 0; d < OR_ROPE; d++) qr[d] = oracle_bf16_round(qr[d]);
+  /* Causal mask ([BLOCKS] M [T queries, T keys]; [MIX] additive mask): the
+   * query at t sees keys 0..t. */
+  rows_t kn = {c->k_nope + bh * c->T * OR_NOPE, OR_NOPE};
+  rows_t vv = {c->v + bh * c->T * OR_VDIM, OR_VDIM};
+  const double *kr = c->kr_rot + (size_t)b * c->T * OR_ROPE; /* shared by all heads */
+  attend_row(qn, qr, kn, kr, OR_ROPE, vv, (long)t + 1, c->scale, scratch, o, &l);
+  if (c->sel) {
+    for (int d = 0; d < OR_VDIM; d++) c->out[unit * OR_VDIM + d] = o[d];
+    if (c->lse) c->lse[unit] = l;
+  } else {
+    /* Head-major flatten ([MIX] "mla-output"): out[b][t][h*128 + d]. */
+    double *dst = c->out + ((size_t)b * c->T + t) * ((size_t)c->H * OR_VDIM) + (size_t)h * OR_VDIM;
+    for (int d = 0; d < OR_VDIM; d++) dst[d] = o[d];
+    if (c->lse) c->lse[bh * c->T + t] = l;
+  }
+}
+
+/* Rotate and round the shared rotary key k_pe [B][1][T][64] once per (b, t):
+ * one key rotary part serves every head ([MIX] "mla-prefill" and its
+ * description: the key's rotated part is the shared rotary key). */
+static double *rotate_shared_keys(const uint16_t *k_pe, const float *R, int B, int T) {
+  double *kr = (double *)malloc((size_t)B * T * OR_ROPE * sizeof(double));
+  if (!kr) return NULL;
+  double row[OR_ROPE], rot[OR_ROPE];
+  for (int b = 0; b < B; b++)
+    for (int t = 0; t < T; t++) {
+      const uint16_t *src = k_pe + ((size_t)b * T + t) * OR_ROPE;
+      for (int d = 0; d < OR_ROPE; d++) row[d] = widen(src[d]);
+      oracle_rotate_row(row, R + (size_t)t * OR_PAIRS, rot);
+      double *dst = kr + ((size_t)b * T + t) * OR_ROPE;
+      for (int d = 0; d < OR_ROPE; d++) dst[d] = oracle_bf16_round(rot[d]);
+    }
+  return kr;
+}
+
+/* Full prefill: out [B][T][H*128] (double, before rounding point R2),
+ * lse [B][H][T] (natural log) or NULL.  Inputs are bf16 bit patterns:
+ * q_nope [B][H][T][128], q_pe [B][H][T][64] (unrotated), k_nope [B][H][T][128],
+ * k_pe [B][1][T][64] (unrotated, shared), v [B][H][T][128]; R [r_rows][32].
+ * Returns 0, 1 on a bad size, 2 on allocation failure. */
+int oracle_prefill(const uint16_t *q_nope, const uint16_t *q_pe, const uint16_t *k_nope,
+                   const uint16_t *k_pe, const uint16_t *v, const float *R, int r_rows,
+                   double scale, int B, int H, int T, double *out, double *lse, int nthreads) {
+  if (B <= 0 || H <= 0 || T <= 0 || T > r_rows) return 1;
+  double *kr = rotate_shared_keys(k_pe, R, B, T);
+  if (!kr) return 2;
+  prefill_ctx c = {q_nope, q_pe, k_nope, v, kr, R, scale, B, H, T, NULL, out, lse};
+  int rc = run_units(prefill_unit, &c, (long)B * H * T, (size_t)T, nthreads);
+  free(kr);
+  return rc;
+}
+
+/* Selected rows only: sel holds n_sel (b, h, t) triples; out [n_sel][128],
+ * lse [n_sel] or NULL.  Each row is the same exact computation as in
+ * oracle_prefill. */
+int oracle_prefill_rows(const uint16_t *q_nope, const uint16_t *q_pe, const uint16_t *k_nope,
+                        const uint16_t *k_pe, const uint16_t *v, const float *R, int r_rows,
+                        double scale, int B, int H, int T, int n_sel, const int *sel,
+                        double *out, double *lse, int nthreads) {
+  if (B <= 0 || H <= 0 || T <= 0 || T > r_rows || n_sel < 0) return 1;
+  for (int i = 0; i < n_sel; i++)
+    if (sel[3 * i] < 0 || sel[3 * i] >= B || sel[3 * i + 1] < 0 || sel[3 * i + 1] >= H ||
+        sel[3 * i + 2] < 0 || sel[3 * i + 2] >= T)
+      return 1;
+  double *kr = rotate_shared_keys(k_pe, R, B, T);
+  if (!kr) return 2;
+  prefill_ctx c = {q_nope, q_pe, k_nope, v, kr, R, scale, B, H, T, sel, out, lse};
+  int rc = run_units(prefill_unit, &c, (long)n_sel, (size_t)T, nthreads);
+  free(kr);
+  return rc;
+}
+
+/* ------------------------------------------------------------- decode ---- */
+
+/* One new query per sequence against a cache of L keys that are already
+ * rotated (the cache stores the keys after rotation: in [MIX] "mla-prefill"
+ * the cache update comes after the rotary step).  Cache rows are
+ * [nope(128) | rope(64)] for keys and 128 for values.  The query is rotated at
+ * position q_pos.  All L cached keys are visible. */
+typedef struct {
+  const uint16_t *q_nope, *q_pe, *k_cache, *v_cache;
+  const float *R;
+  int q_pos;
+  double scale;
+  int B, H, L;
+  const int *sel; /* NULL or n_sel (b, h) pairs */
+  double *out;    /* full: [B][H*128]; rows: [n_sel][128] */
+  double *lse;    /* full: [B][H]; rows: [n_sel] */
+} decode_ctx;
+
+static void decode_unit(void *vctx, long unit, double *scratch) {
+  decode_ctx *c = (decode_ctx *)vctx;
+  int b, h;
+  if (c->sel) {
+    b = c->sel[2 * unit];
+    h = c->sel[2 * unit + 1];
+  } else {
+    h = (int)(unit % c->H);
+    b = (int)(unit / c->H);
+  }
+  const long bh = (long)b * c->H + h;
+  double qn[OR_NOPE], qpe[OR_ROPE], qr[OR_ROPE], o[OR_VDIM], l;
+  for (int d = 0; d < OR_NOPE; d++) qn[d] = widen(c->q_nope[bh * OR_NOPE + d]);
+  for (int d = 0; d < OR_ROPE; d++) qpe[d] = widen(c->q_pe[bh * OR_ROPE + d]);
+  oracle_rotate_row(qpe, c->R + (size_t)c->q_pos * OR_PAIRS, qr);
+  for (int d = 0; d < OR_ROPE; d++) qr[d] = oracle_bf16_round(qr[d]);
+  const long krow = OR_NOPE + OR_ROPE;
+  const uint16_t *kc = c->k_cache + bh * c->L * krow;
+  /* Widen the cached rotary parts of this head (already bf16 values). */
+  double *kr = scratch + c->L;
+  for (long j = 0; j < c->L; j++)
+    for (int d = 0; d < OR_ROPE; d++) kr[j * OR_ROPE + d] = widen(kc[j * krow + OR_NOPE + d]);
+  rows_t kn = {kc, krow};
+  rows_t vv = {c->v_cache + bh * c->L * OR_VDIM, OR_VDIM};
+  attend_row(qn, qr, kn, kr, OR_ROPE, vv, c->L, c->scale, scratch, o, &l);
+  if (c->sel) {
+    for (int d = 0; d < OR_VDIM; d++) c->out[unit * OR_VDIM + d] = o[d];
+    if (c->lse) c->lse[unit] = l;
+  } else {
+    double *dst = c->out + (size_t)b * c->H * OR_VDIM + (size_t)h * OR_VDIM;
+    for (int d = 0; d < OR_VDIM; d++) dst[d] = o[d];
+    if (c->lse) c->lse[bh] = l;
+  }
+}
+
+/* Full decode: q_nope [B][H][128], q_pe [B][H][64] (unrotated), k_cache
+ * [B][H][L][192] (rotated), v_cache [B][H][L][128]; out [B][H*128] double;
+ * lse [B][H] or NULL. */
+int oracle_decode(const uint16_t *q_nope, const uint16_t *q_pe, const uint16_t *k_cache,
+                  const uint16_t *v_cache, const float *R, int r_rows, int q_pos, double scale,
+                  int B, int H, int L, double *out, double *lse, int nthreads) {
+  if (B <= 0 || H <= 0 || L <= 0 || q_pos < 0 || q_pos >= r_rows) return 1;
+  decode_ctx c = {q_nope, q_pe, k_cache, v_cache, R, q_pos, scale, B, H, L, NULL, out, lse};
+  return run_units(decode_unit, &c, (long)B * H, (size_t)L * (1 + OR_ROPE), nthreads);
+}
+
+/* Selected (b, h) pairs only: out [n_sel][128], lse [n_sel] or NULL. */
+int oracle_decode_rows(const uint16_t *q_nope, const uint16_t *q_pe, const uint16_t *k_cache,
+                       const uint16_t *v_cache, const float *R, int r_rows, int q_pos,
+                       double scale, int B, int H, int L, int n_sel, const int *sel, double *out,
+                       double *lse, int nthreads) {
+  if (B <= 0 || H <= 0 || L <= 0 || q_pos < 0 || q_pos >= r_rows || n_sel < 0) return 1;
+  for (int i = 0; i < n_sel; i++)
+    if (sel[2 * i] < 0 || sel[2 * i] >= B || sel[2 * i + 1] < 0 || sel[2 * i + 1] >= H) return 1;
+  decode_ctx c = {q_nope, q_pe, k_cache, v_cache, R, q_pos, scale, B, H, L, sel, out, lse};
+  return run_units(decode_unit, &c, (long)n_sel, (size_t)L * (1 + OR_ROPE), nthreads);
+}
+
+/* ------------------------------------------------------------- o_proj ---- */
+
+/* Output projection ([MIX] "mla-output" and the parameter table: an
+ * 8,192 -> 7,168 linear map without bias, [CONFIG] attention_bias false).
+ * The weight is held as a linear layer holds it, w [N][K] (one row of K
+ * inputs per output feature), and y[m][n] = sum_k x[m][k] w[n][k], summed in
+ * k order in double.  x is the bf16 attention output (rounding point R2). */
+typedef struct {
+  const uint16_t *x, *w;
+  int M, K, N;
+  const int *rows; /* NULL: all rows; else n_rows indices into x */
+  double *y;       /* [M or n_rows][N] */
+} oproj_ctx;
+
+static void oproj_unit(void *vctx, long unit, double *scratch) {
+  oproj_ctx *c = (oproj_ctx *)vctx;
+  long m = c->rows ? c->rows[unit] : unit;
+  const uint16_t *xr = c->x + m * (long)c->K;
+  for (int k = 0; k < c->K; k++) scratch[k] = widen(xr[k]);
+  for (int n = 0; n < c->N; n++) {
+    const uint16_t *wr = c->w + (long)n * c->K;
+    double acc = 0.0;
+    for (int k = 0; k < c->K; k++) acc += scratch[k] * widen(wr[k]);
+    c->y[unit * (long)c->N + n] = acc;
+  }
+}
+
+int oracle_out_proj(const uint16_t *x, const uint16_t *w, int M, int K, int N, double *y,
+                    int nthreads) {
+  if (M <= 0 || K <= 0 || N <= 0) return 1;
+  oproj_ctx c = {x, w, M, K, N, NULL, y};
+  return run_units(oproj_unit, &c, (long)M, (size_t)K, nthreads);
+}
+
+int oracle_out_proj_rows(const uint16_t *x, const uint16_t *w, int M, int K, int N, int n_rows,
+                         const int *rows, double *y, int nthreads) {
+  if (M <= 0 || K <= 0 || N <= 0 || n_rows < 0) return 1;
+  for (int i = 0; i < n_rows; i++)
+    if (rows[i] < 0 || rows[i] >= M) return 1;
+  oproj_ctx c = {x, w, M, K, N, rows, y};
+  return run_units(oproj_unit, &c, (long)n_rows, (size_t)K, nthreads);
+}
