@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA attend-and-combine hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  prefill  B=4, T=4096, 64 heads: rotary prologue + causal flash attention
+           (mla_attend_prefill), then o_proj on the [16384, 8192] output;
+  decode   B=64, L=8192 cached keys, query at position 8192: split attention +
+           merge (mla_attend_decode), then o_proj on the [64, 8192] output.
+Inputs are generated on the GPU before the timed region and stay resident.
+Every call is timed with HIP events on the stream the library launches on.
+
+Prints ONE JSON line.  `value` is the causal prefill attention throughput
+(algorithmic flops 2*(128+64+128)*T(T+1)/2*B*H per call / call time).  The
+decode figure (algorithmic bytes: every cached K/V byte once, plus q and the
+output / call time) and the o_proj figures sit beside it.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, REPO)
+
+PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBPS = 8000.0      # HBM3E
+METRIC = "MLA prefill TFLOP/s (causal) + % bf16 MFMA peak; decode HBM GB/s, 1 GPU"
+
+
+def prefill_flops(B, H, T):
+    return 2.0 * (128 + 64 + 128) * T * (T + 1) / 2 * B * H
+
+
+def decode_bytes(B, H, L):
+    return B * H * (L * (192 + 128) * 2 + (128 + 64) * 2 + 128 * 2)
+
+
+def oproj_flops(M, K, N):
+    return 2.0 * M * K * N
+
+
+def oproj_bytes(M, K, N):
+    return (M * K + N * K + M * N) * 2
+
+
+def cpu_baseline(d, B, H, T, R, scale, budget_s):
+    """Time the oracle on a bounded sample of the prefill workload: every row
+    of sequence 0 for the first n heads, n chosen from a one-head
+    calibration so the sample takes about budget_s seconds."""
+    import numpy as np
+    import oracle
+    from transformer_attention_mla_amd import inputs
+
+    threads = oracle.default_threads()
+
+    def head_inputs(n):
+        sl = lambda t: inputs.bits(t[0:1, 0:n])
+        return (sl(d["q_nope"]), sl(d["q_pe"]), sl(d["k_nope"]), inputs.bits(d["k_pe"][0:1]),
+                sl(d["v"]))
+
+    def run(n):
+        qn, qp, kn, kp, v = head_inputs(n)
+        rows = np.arange(T, dtype=np.int32)
+        sel = np.stack([np.zeros(n * T, np.int32), np.repeat(np.arange(n, dtype=np.int32), T),
+                        np.tile(rows, n)], 1)
+        t0 = time.perf_counter()
+        oracle.prefill_rows(qn, qp, kn, kp, v, R, scale, sel, nthreads=threads)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    n = max(1, min(H, int(budget_s / max(t1, 1e-3))))
+    tn = t1 if n == 1 else run(n)
+    flops = prefill_flops(1, n, T)
+    return {"value": flops / tn / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"prefill rows of sequence 0, heads 0..{n - 1} (all {T} rows each) of the "
+                      f"B={B} T={T} workload; {flops / 1e9:.1f} GFLOP in {tn:.2f} s, fp64",
+            "seconds": round(tn, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--decode-splits", type=int, default=0)
+    ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path to measure.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_attention_mla_amd as mla
+    from transformer_attention_mla_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    scale = float(inputs.SOFTMAX_SCALE)
+    wp, wd = inputs.WORKLOADS[3], inputs.WORKLOADS[5]
+    B, H, T = wp["B"], wp["H"], wp["T"]
+    Bd, Hd, L, q_pos = wd["B"], wd["H"], wd["L"], wd["q_pos"]
+    K_O, N_O = H * 128, inputs.D_MODEL
+    do_p = args.only in ("prefill", "all")
+    do_d = args.only in ("decode", "all")
+
+    # ---- inputs, resident in HBM before timing
+    print("generating inputs", file=sys.stderr, flush=True)
+    w_o = inputs.out_proj_weight(N_O, K_O, workload=3, device=dev)
+    if do_p:
+        d = inputs.prefill_inputs(B, H, T, workload=3, device=dev)
+        attn_out = torch.empty((B, T, H * 128), dtype=torch.bfloat16, device=dev)
+        y_p = torch.empty((B * T, N_O), dtype=torch.bfloat16, device=dev)
+        ws_p = torch.empty(mla.mla_prefill_workspace_bytes(B, H, T), dtype=torch.uint8, device=dev)
+        ws_op = torch.empty(max(16, mla.mla_out_proj_workspace_bytes(B * T, K_O, N_O)),
+                            dtype=torch.uint8, device=dev)
+    if do_d:
+        dd = inputs.decode_inputs(Bd, Hd, L, q_pos, workload=5, device=dev)
+        dec_out = torch.empty((Bd, Hd * 128), dtype=torch.bfloat16, device=dev)
+        y_d = torch.empty((Bd, N_O), dtype=torch.bfloat16, device=dev)
+        ws_d = torch.empty(max(16, mla.mla_decode_workspace_bytes(Bd, Hd, L, args.decode_splits)),
+                           dtype=torch.uint8, device=dev)
+        ws_od = torch.empty(max(16, mla.mla_out_proj_workspace_bytes(Bd, K_O, N_O)),
+                            dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    names = []
+    if do_p:
+        names += ["prefill_attention", "prefill_oproj"]
+    if do_d:
+        names += ["decode_attention", "decode_oproj"]
+    n_ev = args.steps
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_ev)] for k in names}
+
+    def step(i=None):
+        def timed(name, fn):
+            if i is not None:
+                ev[name][i][0].record()
+            fn()
+            if i is not None:
+                ev[name][i][1].record()
+        if do_p:
+            timed("prefill_attention", lambda: mla.mla_attend_prefill(
+                d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], d["R"], scale,
+                out=attn_out, workspace=ws_p))
+            timed("prefill_oproj", lambda: mla.mla_out_proj(
+                attn_out.view(B * T, K_O), w_o, y=y_p, workspace=ws_op))
+        if do_d:
+            timed("decode_attention", lambda: mla.mla_attend_decode(
+                dd["q_nope"], dd["q_pe"], dd["k_cache"], dd["v_cache"], dd["R"], q_pos, scale,
+                num_splits=args.decode_splits, out=dec_out, workspace=ws_d))
+            timed("decode_oproj", lambda: mla.mla_out_proj(dec_out, w_o, y=y_d, workspace=ws_od))
+
+    print("warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("timing", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {k: sorted(a.elapsed_time(b) for a, b in ev[k]) for k in names}
+    avg = {k: sum(v) / len(v) for k, v in ms.items()}
+    med = {k: v[len(v) // 2] for k, v in ms.items()}
+    print("timed: " + ", ".join(f"{k} {avg[k]:.3f} ms" for k in names), file=sys.stderr, flush=True)
+
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    cfg = {"workload": "", "heads": H}
+    parts = []
+    if do_p:
+        fa = prefill_flops(B, H, T)
+        fo = oproj_flops(B * T, K_O, N_O)
+        ta = avg["prefill_attention"] / 1e3
+        to = avg["prefill_oproj"] / 1e3
+        res["value"] = fa / ta / 1e12
+        res["unit"] = "TFLOP/s"
+        res["prefill"] = {
+            "attention_ms": avg["prefill_attention"], "attention_ms_median": med["prefill_attention"],
+            "attention_tflops": fa / ta / 1e12, "attention_frac_peak": fa / ta / 1e12 / PEAK_BF16_TFLOPS,
+            "oproj_ms": avg["prefill_oproj"], "oproj_tflops": fo / to / 1e12,
+            "oproj_frac_peak": fo / to / 1e12 / PEAK_BF16_TFLOPS,
+            "attention_plus_oproj_tflops": (fa + fo) / (ta + to) / 1e12}
+        res["roofline"] = {"bound": "mfma", "achieved": fa / ta / 1e12, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": fa / ta / 1e12 / PEAK_BF16_TFLOPS,
+                           "traffic": None, "kernel": "prefill_kernel (+ rope_prep_kernel)",
+                           "per_launch": f"{fa:.4e} causal flops"}
+        parts.append(f"prefill B={B} T={T} H={H} causal + o_proj [{B * T}x{K_O}]x[{K_O}x{N_O}]")
+        cfg.update({"prefill_batch": B, "prefill_seq_len": T})
+    if do_d:
+        bd = decode_bytes(Bd, Hd, L)
+        td = avg["decode_attention"] / 1e3
+        tod = avg["decode_oproj"] / 1e3
+        bo = oproj_bytes(Bd, K_O, N_O)
+        res["decode"] = {
+            "attention_ms": avg["decode_attention"], "attention_ms_median": med["decode_attention"],
+            "hbm_gbps": bd / td / 1e9, "frac_hbm": bd / td / 1e9 / PEAK_HBM_GBPS,
+            "splits": mla.mla_decode_splits(Bd, Hd, L, args.decode_splits),
+            "oproj_ms": avg["decode_oproj"], "oproj_gbps": bo / tod / 1e9}
+        res["roofline_decode"] = {"bound": "hbm", "achieved": bd / td / 1e9, "peak": PEAK_HBM_GBPS,
+                                  "unit": "GB/s", "frac": bd / td / 1e9 / PEAK_HBM_GBPS,
+                                  "traffic": None, "kernel": "decode_split_kernel",
+                                  "per_launch": f"{bd} bytes"}
+        parts.append(f"decode B={Bd} L={L} H={Hd} q_pos={q_pos} + o_proj [{Bd}x{K_O}]x[{K_O}x{N_O}]")
+        cfg.update({"decode_batch": Bd, "decode_kv_len": L})
+        if not do_p:
+            res["value"] = bd / td / 1e9
+            res["unit"] = "GB/s"
+            res["roofline"] = res.pop("roofline_decode")
+    cfg["workload"] = "; ".join(parts)
+    res["config"] = cfg
+
+    if do_p and not args.no_cpu_baseline:
+        print("cpu baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(d, B, H, T, d["R"].cpu().numpy(), scale, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

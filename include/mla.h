@@ -1,0 +1,166 @@
+/*
+ * mla.h — C ABI of the MI355X (gfx950) library for Kimi K2's latent-attention
+ * (MLA) attend-and-combine step.
+ *
+ * What the calls compute (the pages' notation):
+ *   page "Kimi K2 · Mix and project", code excerpt "mla-prefill": the 64-wide
+ *   rotary parts of query and key are rotated; each head's 192-wide query and
+ *   key are the 128-wide non-rotated part followed by the rotated part, the
+ *   key's rotated part being one tensor shared by every head; scores
+ *   Q·Kᵀ·softmax_scale get the additive causal mask, a float32 softmax over
+ *   keys, and mix the 128-wide values.  Excerpt "mla-output": head outputs are
+ *   transposed to [B, T, 64·128] (head-major) and go through o_proj, an
+ *   8,192 → 7,168 linear map without bias (the parameter table of that page;
+ *   the page's explanation: the only step that mixes heads).
+ *   page "Kimi K2 · Transformer blocks", I/O header: R [T positions, 32 pairs]
+ *   and the causal mask M [T queries, T keys]; the model-body excerpt numbers
+ *   positions from the cached length (0 for a prefill without cache).
+ *   page "Block input", config.json: 64 heads, qk_nope_head_dim 128,
+ *   qk_rope_head_dim 64, v_head_dim 128, attention_bias false, bfloat16.
+ *
+ * Conventions shared by every call
+ *   - Tensors are contiguous, row-major.  "bf16" arguments point at IEEE
+ *     bfloat16 values (their 16-bit patterns; mla_bf16 below).
+ *   - Every pointer argument is DEVICE memory owned by the caller; the library
+ *     allocates nothing, keeps no pointer after the call returns and has no
+ *     global state besides a per-device architecture check.
+ *   - Pointers must be 16-byte aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     runs asynchronously; the library never synchronises.
+ *   - All validation happens before anything is enqueued.  On any error
+ *     nothing is enqueued and no output byte is written.  The library never
+ *     aborts or throws across this boundary.
+ *   - Outputs are fully overwritten; inputs are read only.  Outputs may not
+ *     overlap inputs or each other (MLA_ERR_ALIAS).
+ *   - Rotary reading: pair i (0..31) couples elements i and i+32 of the
+ *     64-wide rotary part; at position t it turns by angle R[t][i]:
+ *       y_i = x_i·cos − x_{i+32}·sin,  y_{i+32} = x_{i+32}·cos + x_i·sin.
+ *     Rotated parts are rounded to bf16 (they are bf16 query/key tensors).
+ *   - Rounding of every float → bf16 store is round-to-nearest-even.
+ *   - Thread safety: calls are reentrant; concurrent calls on different
+ *     streams are independent.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* 16-bit pattern of an IEEE bfloat16 value. */
+typedef uint16_t mla_bf16;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,      /* a required pointer is NULL */
+  MLA_ERR_DIM = 2,       /* a size is <= 0, inconsistent, or exceeds the angle table */
+  MLA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  MLA_ERR_ALIAS = 4,     /* an output overlaps an input or another output */
+  MLA_ERR_WORKSPACE = 5, /* workspace missing or smaller than required */
+  MLA_ERR_SCALE = 6,     /* softmax_scale is not finite or not > 0 */
+  MLA_ERR_DEVICE = 7,    /* the current device is not gfx950 (or none) */
+  MLA_ERR_LAUNCH = 8,    /* the runtime reported an error when enqueueing */
+  MLA_ERR_FLAGS = 9      /* unknown bits in `flags` */
+} mla_status;
+
+#define MLA_ABI_VERSION 1
+
+/* flags bit: store `out` / `y` as float32 instead of bf16.  The arithmetic is
+ * identical; only the final store differs, so a bf16 result equals the
+ * round-to-nearest-even of its float32 twin. */
+#define MLA_OUT_F32 0x1u
+
+/* Version of this ABI (MLA_ABI_VERSION). */
+int mla_abi_version(void);
+
+/* Static, NUL-terminated name of a status code ("MLA_OK", ...); "unknown
+ * status" for other values.  Never NULL. */
+const char *mla_status_string(int status);
+
+/* -------------------------------------------------------------- prefill --
+ * Causal prefill attention over positions 0..T-1 (no cache), all heads.
+ *
+ *   q_nope  [B, H, T, 128] bf16   non-rotated query part
+ *   q_pe    [B, H, T, 64]  bf16   rotary query part, NOT yet rotated
+ *   k_nope  [B, H, T, 128] bf16   non-rotated key part
+ *   k_pe    [B, 1, T, 64]  bf16   rotary key part, NOT yet rotated, shared by all heads
+ *   v       [B, H, T, 128] bf16   values
+ *   R       [r_rows, 32]   float  angle table in radians, row t = position t; T <= r_rows
+ *   softmax_scale                 score multiplier (Kimi K2: 192^-0.5), finite and > 0
+ *   workspace                     device scratch of >= mla_prefill_workspace_bytes(B,H,T)
+ *                                 bytes (cos/sin table and the rotated shared key)
+ *   out     [B, T, H*128]  bf16, or float32 with MLA_OUT_F32; element
+ *                          [b][t][h*128+d] is head h's output (head-major flatten)
+ *   lse     [B, H, T] float natural-log sum of exp of the scaled, masked scores
+ *                     per row, or NULL
+ *
+ * Row t of head h is softmax_j≤t(scale·(q_nope·k_noperᵀ + rot(q_pe)·rot(k_pe)ᵀ))·V.
+ * B, H, T >= 1 with any tails.  The softmax is evaluated online in float32 in
+ * base 2; the weights that multiply V are rounded to bf16 and the row sum is
+ * accumulated from those same rounded weights.
+ */
+size_t mla_prefill_workspace_bytes(int B, int H, int T);
+
+int mla_attend_prefill(const mla_bf16 *q_nope, const mla_bf16 *q_pe, const mla_bf16 *k_nope,
+                       const mla_bf16 *k_pe, const mla_bf16 *v, const float *R, int r_rows,
+                       float softmax_scale, int B, int H, int T, void *workspace,
+                       size_t workspace_bytes, void *out, float *lse, uint32_t flags,
+                       void *stream);
+
+/* --------------------------------------------------------------- decode --
+ * One new query per sequence against L cached keys (page "Kimi K2 · Mix and
+ * project", excerpt "mla-prefill": the cache stores keys after the rotary step,
+ * as [non-rotated 128 | rotated 64], and values).
+ *
+ *   q_nope  [B, H, 128]     bf16   non-rotated query part
+ *   q_pe    [B, H, 64]      bf16   rotary query part, NOT yet rotated; rotated at q_pos
+ *   k_cache [B, H, L, 192]  bf16   cached keys, already rotated
+ *   v_cache [B, H, L, 128]  bf16   cached values
+ *   R       [r_rows, 32]    float  angle table; 0 <= q_pos < r_rows
+ *   num_splits                     key-range splits per (b, h); 0 = library's choice,
+ *                                  otherwise 1..L (larger values are clamped to L)
+ *   workspace                      >= mla_decode_workspace_bytes(B, H, L, num_splits)
+ *                                  bytes (0 bytes, NULL allowed, when one split is used)
+ *   out     [B, H*128]      bf16, or float32 with MLA_OUT_F32 (head-major)
+ *   lse     [B, H]          float natural-log row lse, or NULL
+ *
+ * Every one of the L keys is visible.  Split partials (running max, sum and
+ * unnormalised output in float32) are merged by the log-sum-exp rule.
+ */
+size_t mla_decode_workspace_bytes(int B, int H, int L, int num_splits);
+
+/* Number of splits the library uses for (B, H, L, num_splits). */
+int mla_decode_splits(int B, int H, int L, int num_splits);
+
+int mla_attend_decode(const mla_bf16 *q_nope, const mla_bf16 *q_pe, const mla_bf16 *k_cache,
+                      const mla_bf16 *v_cache, const float *R, int r_rows, int q_pos,
+                      float softmax_scale, int B, int H, int L, int num_splits, void *workspace,
+                      size_t workspace_bytes, void *out, float *lse, uint32_t flags,
+                      void *stream);
+
+/* --------------------------------------------------------------- o_proj --
+ * y = x · w_oᵀ, the 8,192 → 7,168 output projection without bias (page "Kimi
+ * K2 · Mix and project", parameter table and excerpt "mla-output").
+ *
+ *   x     [M, K]  bf16   flattened attention output (K = heads·128)
+ *   w_o   [N, K]  bf16   the linear layer's weight as the layer stores it:
+ *                        row n holds the K input weights of output feature n
+ *   y     [M, N]  bf16, or float32 with MLA_OUT_F32
+ *   workspace     >= mla_out_proj_workspace_bytes(M, K, N) bytes; the library
+ *                 splits K for small M and keeps float32 partials there
+ *
+ * M, N >= 1, K >= 1 and a multiple of 128.  Accumulation is float32.
+ */
+size_t mla_out_proj_workspace_bytes(int M, int K, int N);
+
+int mla_out_proj(const mla_bf16 *x, const mla_bf16 *w_o, void *y, int M, int K, int N,
+                 void *workspace, size_t workspace_bytes, uint32_t flags, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

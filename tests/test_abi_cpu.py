@@ -1,0 +1,131 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/mla.h declares, and rejects bad arguments with the documented status
+codes before touching the device.
+
+Pointers passed here are fake, aligned addresses that are never dereferenced:
+every call below fails validation (which happens before any HIP call), so no
+work is ever enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_attention_mla_amd as mla
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla.h")
+
+OK, NULL, DIM, ALIGN, ALIAS, WORKSPACE, SCALE, DEVICE, LAUNCH, FLAGS = range(10)
+GB = 1 << 30
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert {"mla_attend_prefill", "mla_attend_decode", "mla_out_proj"} <= set(names)
+    lib = mla.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings():
+    assert mla.mla_abi_version() == 1
+    for code in range(10):
+        s = mla.mla_status_string(code)
+        assert s.startswith("MLA_")
+    assert mla.mla_status_string(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    assert mla.mla_prefill_workspace_bytes(4, 64, 4096) == 4096 * 32 * 8 + 4 * 4096 * 64 * 2
+    assert mla.mla_prefill_workspace_bytes(0, 64, 10) == 0
+    assert mla.mla_decode_splits(64, 64, 8192, 0) == 1
+    assert mla.mla_decode_workspace_bytes(64, 64, 8192, 0) == 0
+    assert mla.mla_decode_splits(1, 1, 100, 7) == 7
+    assert mla.mla_decode_splits(1, 1, 5, 64) == 5
+    assert mla.mla_decode_workspace_bytes(2, 3, 100, 4) == 2 * 3 * 4 * 136 * 4
+    s = mla.mla_decode_splits(1, 64, 8192, 0)
+    assert s > 1 and mla.mla_decode_workspace_bytes(1, 64, 8192, 0) == 64 * s * 136 * 4
+    assert mla.mla_out_proj_workspace_bytes(16384, 8192, 7168) == 0
+    assert mla.mla_out_proj_workspace_bytes(64, 8192, 7168) > 0
+    assert mla.mla_out_proj_workspace_bytes(64, 100, 7168) == 0  # K not a multiple of 128
+
+
+# Fake device addresses: 16-byte aligned, disjoint, 1 GiB apart.
+A = [ctypes.c_void_p((i + 1) * 16 * GB) for i in range(12)]
+
+
+def prefill(**kw):
+    a = dict(q_nope=A[0], q_pe=A[1], k_nope=A[2], k_pe=A[3], v=A[4], R=A[5], r_rows=64,
+             scale=0.07, B=1, H=2, T=64, ws=A[6], ws_bytes=1 << 20, out=A[7], lse=None,
+             flags=0)
+    a.update(kw)
+    return mla.lib().mla_attend_prefill(a["q_nope"], a["q_pe"], a["k_nope"], a["k_pe"], a["v"],
+                                        a["R"], a["r_rows"], a["scale"], a["B"], a["H"], a["T"],
+                                        a["ws"], a["ws_bytes"], a["out"], a["lse"], a["flags"],
+                                        None)
+
+
+def decode(**kw):
+    a = dict(q_nope=A[0], q_pe=A[1], kc=A[2], vc=A[3], R=A[4], r_rows=10, q_pos=9, scale=0.07,
+             B=1, H=2, L=100, splits=1, ws=None, ws_bytes=0, out=A[5], lse=None, flags=0)
+    a.update(kw)
+    return mla.lib().mla_attend_decode(a["q_nope"], a["q_pe"], a["kc"], a["vc"], a["R"],
+                                       a["r_rows"], a["q_pos"], a["scale"], a["B"], a["H"],
+                                       a["L"], a["splits"], a["ws"], a["ws_bytes"], a["out"],
+                                       a["lse"], a["flags"], None)
+
+
+def oproj(**kw):
+    a = dict(x=A[0], w=A[1], y=A[2], M=16384, K=8192, N=7168, ws=None, ws_bytes=0, flags=0)
+    a.update(kw)
+    return mla.lib().mla_out_proj(a["x"], a["w"], a["y"], a["M"], a["K"], a["N"], a["ws"],
+                                  a["ws_bytes"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_nope=None), NULL), (dict(k_pe=None), NULL), (dict(R=None), NULL), (dict(out=None), NULL),
+    (dict(flags=2), FLAGS),
+    (dict(B=0), DIM), (dict(H=-1), DIM), (dict(T=0), DIM), (dict(T=65), DIM), (dict(r_rows=0), DIM),
+    (dict(scale=0.0), SCALE), (dict(scale=-1.0), SCALE), (dict(scale=float("nan")), SCALE),
+    (dict(scale=float("inf")), SCALE),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE),
+    (dict(q_pe=ctypes.c_void_p(2 * 16 * GB + 8)), ALIGN), (dict(lse=ctypes.c_void_p(12 * GB + 4)), ALIGN),
+    (dict(out=ctypes.c_void_p(1 * 16 * GB + 4096)), ALIAS),     # out inside q_nope
+    (dict(ws=A[7]), ALIAS),                                   # workspace == out
+    (dict(lse=ctypes.c_void_p(7 * 16 * GB + 1024)), ALIAS),    # lse inside workspace
+])
+def test_prefill_rejects(kw, code):
+    assert prefill(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kc=None), NULL), (dict(out=None), NULL),
+    (dict(flags=4), FLAGS),
+    (dict(L=0), DIM), (dict(q_pos=10), DIM), (dict(q_pos=-1), DIM), (dict(splits=-1), DIM),
+    (dict(scale=0.0), SCALE),
+    (dict(splits=4), WORKSPACE), (dict(splits=4, ws=A[6], ws_bytes=100), WORKSPACE),
+    (dict(vc=ctypes.c_void_p(4 * 16 * GB + 2)), ALIGN),
+    (dict(out=ctypes.c_void_p(3 * 16 * GB + 256)), ALIAS),
+    (dict(splits=4, ws=A[5], ws_bytes=1 << 20), ALIAS),
+])
+def test_decode_rejects(kw, code):
+    assert decode(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(y=None), NULL),
+    (dict(flags=8), FLAGS),
+    (dict(M=0), DIM), (dict(N=0), DIM), (dict(K=100), DIM), (dict(K=0), DIM),
+    (dict(M=64), WORKSPACE),
+    (dict(y=ctypes.c_void_p(1 * 16 * GB + 8)), ALIGN),
+    (dict(y=ctypes.c_void_p(2 * 16 * GB + 64)), ALIAS),
+])
+def test_oproj_rejects(kw, code):
+    assert oproj(**kw) == code

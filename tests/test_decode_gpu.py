@@ -1,0 +1,120 @@
+"""GPU parity of mla_attend_decode (split kernel + log-sum-exp merge) against
+the fp64 oracle, over split counts, ragged key counts and probes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_mla_amd as mla
+from transformer_attention_mla_amd import inputs
+
+from _gpu_helpers import (SCALE, SUM_TOL, TOL, bits, check_bf16_close, check_bf16_is_rne_of_f32,
+                          check_close, say, to_host64)
+
+pytestmark = pytest.mark.gpu
+
+
+def run(d, dev, **kw):
+    g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in d.items()}
+    out, lse = mla.mla_attend_decode(g["q_nope"], g["q_pe"], g["k_cache"], g["v_cache"], g["R"],
+                                     g["q_pos"], SCALE, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_full(d):
+    return oracle.decode(bits(d["q_nope"]), bits(d["q_pe"]), bits(d["k_cache"]), bits(d["v_cache"]),
+                         d["R"].cpu().numpy(), d["q_pos"], SCALE)
+
+
+@pytest.mark.parametrize("B,H,L", [(1, 1, 1), (2, 3, 17), (1, 2, 100), (3, 2, 1000), (2, 64, 300)])
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7, 64])
+def test_decode_parity(B, H, L, splits, gpu_device):
+    say(f"decode parity B={B} H={H} L={L} splits={splits}")
+    d = inputs.decode_inputs(B, H, L, q_pos=L + 5)
+    want, want_lse = oracle_full(d)
+    out32, lse = run(d, gpu_device, num_splits=splits, out_f32=True, want_lse=True)
+    out16, _ = run(d, gpu_device, num_splits=splits)
+    check_close(to_host64(out32), want, TOL, "float32 output vs oracle")
+    check_bf16_is_rne_of_f32(out16, out32)
+    check_bf16_close(out16, want, "bf16 output vs oracle")
+    check_close(to_host64(lse), want_lse, TOL, "lse vs oracle")
+
+
+@pytest.mark.parametrize("L,splits", [(1, 1), (777, 1), (777, 5), (8192, 0), (8192, 64)])
+def test_decode_weights_sum_to_one_and_counts(L, splits, gpu_device):
+    B, H = 2, 3
+    say(f"decode probes L={L} splits={splits}")
+    d = inputs.decode_inputs(B, H, L, q_pos=L)
+    d1 = dict(d)
+    d1["v_cache"] = torch.ones_like(d["v_cache"])
+    out32, _ = run(d1, gpu_device, num_splits=splits, out_f32=True)
+    err = (out32.double() - 1).abs().max().item()
+    say(f"  max |out - 1| = {err:.3e}")
+    assert err <= SUM_TOL
+    d0 = dict(d)
+    d0["q_nope"] = torch.zeros_like(d["q_nope"])
+    d0["q_pe"] = torch.zeros_like(d["q_pe"])
+    out, lse = run(d0, gpu_device, num_splits=splits, out_f32=True, want_lse=True)
+    counts = torch.round(torch.exp(lse.double())).to(torch.int64).cpu()
+    assert torch.all(counts == L)
+    want = d["v_cache"].double().mean(dim=2).reshape(B, H * 128).numpy()
+    check_close(to_host64(out), want, TOL, "mean of V")
+
+
+def test_decode_split_counts_agree(gpu_device):
+    B, H, L = 2, 4, 3000
+    d = inputs.decode_inputs(B, H, L, q_pos=L)
+    ref, ref_lse = run(d, gpu_device, num_splits=1, out_f32=True, want_lse=True)
+    for s in (2, 3, 7, 16, 64, 5000):
+        out, lse = run(d, gpu_device, num_splits=s, out_f32=True, want_lse=True)
+        assert (out - ref).abs().max().item() <= SUM_TOL
+        assert (lse - ref_lse).abs().max().item() <= SUM_TOL
+
+
+def test_decode_matches_prefill_last_row(gpu_device):
+    """A cache built from a prefill's keys (rotated by the oracle) and the
+    prefill's last query: decode must reproduce that prefill row."""
+    B, H, L = 1, 3, 200
+    say("decode vs prefill last row")
+    d = inputs.prefill_inputs(B, H, L + 1, workload=0)
+    R = d["R"].numpy()
+    pos = np.broadcast_to(np.arange(L + 1, dtype=np.int32), (B, L + 1)).copy()
+    _, kr = oracle.rope_rotate(bits(d["k_pe"]).reshape(B, L + 1, 64), R, pos)
+    kr = torch.from_numpy(kr.view(np.int16)).view(torch.bfloat16).reshape(B, 1, L + 1, 64)
+    kc = torch.cat([d["k_nope"], kr.expand(B, H, L + 1, 64)], dim=-1).contiguous()
+    dd = dict(q_nope=d["q_nope"][:, :, L].contiguous(), q_pe=d["q_pe"][:, :, L].contiguous(),
+              k_cache=kc, v_cache=d["v"], R=d["R"], q_pos=L)
+    dout, _ = run(dd, gpu_device, out_f32=True)
+    g = {k: v.to(gpu_device) for k, v in d.items()}
+    pout, _ = mla.mla_attend_prefill(g["q_nope"], g["q_pe"], g["k_nope"], g["k_pe"], g["v"], g["R"],
+                                     SCALE, out_f32=True)
+    torch.cuda.synchronize()
+    check_close(to_host64(dout), to_host64(pout[:, L]), 1e-3, "decode vs prefill row")
+    want, _ = oracle.prefill_rows(bits(d["q_nope"]), bits(d["q_pe"]), bits(d["k_nope"]),
+                                  bits(d["k_pe"]), bits(d["v"]), R, SCALE,
+                                  np.array([[0, h, L] for h in range(H)], np.int32))
+    check_close(to_host64(dout).reshape(H, 128), want, TOL, "decode vs oracle prefill row")
+
+
+def test_decode_workload5_sampled(gpu_device):
+    """B=64, 64 heads, 8192 cached keys, query at position 8192, in the
+    configuration the benchmark times; sampled (b, h) pairs against the oracle."""
+    w = inputs.WORKLOADS[5]
+    B, H, L, q_pos = w["B"], w["H"], w["L"], w["q_pos"]
+    say("decode workload 5 sampled")
+    d = inputs.decode_inputs(B, H, L, q_pos, workload=5, device=gpu_device)
+    out32, lse = mla.mla_attend_decode(d["q_nope"], d["q_pe"], d["k_cache"], d["v_cache"], d["R"],
+                                       q_pos, SCALE, out_f32=True, want_lse=True)
+    out16, _ = mla.mla_attend_decode(d["q_nope"], d["q_pe"], d["k_cache"], d["v_cache"], d["R"],
+                                     q_pos, SCALE)
+    torch.cuda.synchronize()
+    check_bf16_is_rne_of_f32(out16, out32)
+    R = d["R"].cpu().numpy()
+    for b, h in [(0, 0), (63, 63), (17, 5), (40, 33)]:
+        o, l = oracle.decode(bits(d["q_nope"][b:b + 1, h:h + 1]), bits(d["q_pe"][b:b + 1, h:h + 1]),
+                             bits(d["k_cache"][b:b + 1, h:h + 1]), bits(d["v_cache"][b:b + 1, h:h + 1]),
+                             R, q_pos, SCALE)
+        check_close(to_host64(out32[b, h * 128:(h + 1) * 128]), o[0], TOL, f"b={b} h={h}")
+        check_close(np.array([lse[b, h].item()]), l[0], TOL, f"b={b} h={h} lse")
+        check_bf16_close(out16[b, h * 128:(h + 1) * 128], o[0], f"b={b} h={h} bf16")

@@ -1,0 +1,86 @@
+"""GPU parity of mla_out_proj (and of the attention + o_proj chain) against
+the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_mla_amd as mla
+from transformer_attention_mla_amd import inputs
+
+from _gpu_helpers import (SCALE, TOL, bits, check_bf16_close, check_bf16_is_rne_of_f32,
+                          check_close, say, to_host64)
+
+pytestmark = pytest.mark.gpu
+
+
+def xw(M, K, N, seed):
+    x = inputs.normal_bf16((M, K), seed)
+    w = inputs.normal_bf16((N, K), seed + 1, std=0.02)
+    return x, w
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (17, 256, 100), (130, 1024, 300), (64, 8192, 7168),
+                                   (200, 512, 7168), (5, 8192, 33), (300, 128, 129)])
+def test_oproj_parity(M, K, N, gpu_device):
+    say(f"o_proj parity M={M} K={K} N={N}")
+    x, w = xw(M, K, N, 10 + M)
+    want = oracle.out_proj(bits(x), bits(w))
+    xg, wg = x.to(gpu_device), w.to(gpu_device)
+    y32 = mla.mla_out_proj(xg, wg, out_f32=True)
+    y16 = mla.mla_out_proj(xg, wg)
+    torch.cuda.synchronize()
+    check_close(to_host64(y32), want, TOL, "float32 output vs oracle")
+    check_bf16_is_rne_of_f32(y16, y32)
+    check_bf16_close(y16, want, "bf16 output vs oracle")
+
+
+@pytest.mark.parametrize("M", [1024, 16384])
+def test_oproj_large_sampled(M, gpu_device):
+    K, N = 8192, 7168
+    say(f"o_proj sampled M={M}")
+    x = inputs.normal_bf16((M, K), 77, device=gpu_device)
+    w = inputs.out_proj_weight(N, K, workload=3, device=gpu_device)
+    y32 = mla.mla_out_proj(x, w, out_f32=True)
+    y16 = mla.mla_out_proj(x, w)
+    torch.cuda.synchronize()
+    check_bf16_is_rne_of_f32(y16, y32)
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 30)])).astype(np.int32)
+    want = oracle.out_proj_rows(bits(x), bits(w), rows)
+    got = to_host64(y32[torch.from_numpy(rows).long().to(gpu_device)])
+    check_close(got, want, TOL, f"{len(rows)} sampled rows")
+
+
+def test_oproj_selection_weight_exact(gpu_device):
+    M, K, N = 70, 1024, 600
+    x = inputs.normal_bf16((M, K), 5)
+    w = torch.zeros((N, K), dtype=torch.bfloat16)
+    w[torch.arange(N), torch.arange(N)] = 1
+    y = mla.mla_out_proj(x.to(gpu_device), w.to(gpu_device))
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu(), x[:, :N])
+
+
+def test_attention_then_oproj_workload1(gpu_device):
+    """The whole step at the 64-position workload: bf16 attention output into
+    o_proj, against the oracle's projection of its own bf16-rounded output."""
+    w_ = inputs.WORKLOADS[1]
+    B, H, T = w_["B"], w_["H"], w_["T"]
+    say("attention + o_proj, workload 1")
+    d = inputs.prefill_inputs(B, H, T, workload=1)
+    wo = inputs.out_proj_weight(workload=1)
+    o, _ = oracle.prefill(bits(d["q_nope"]), bits(d["q_pe"]), bits(d["k_nope"]), bits(d["k_pe"]),
+                          bits(d["v"]), d["R"].numpy(), SCALE, want_lse=False)
+    o16 = oracle.bf16_round(o).reshape(B * T, H * 128)
+    o16_bits = bits(torch.from_numpy(o16).to(torch.bfloat16))
+    want = oracle.out_proj(o16_bits, bits(wo))
+    g = {k: v.to(gpu_device) for k, v in d.items()}
+    attn, _ = mla.mla_attend_prefill(g["q_nope"], g["q_pe"], g["k_nope"], g["k_pe"], g["v"], g["R"],
+                                     SCALE)
+    y32 = mla.mla_out_proj(attn.view(B * T, H * 128), wo.to(gpu_device), out_f32=True)
+    torch.cuda.synchronize()
+    check_close(to_host64(y32), want, TOL, "delta_attn (float32 store) vs oracle")
+    # o_proj alone on the GPU's own bf16 attention output
+    want_chain = oracle.out_proj(bits(attn.view(B * T, H * 128)), bits(wo))
+    check_close(to_host64(y32), want_chain, 1e-3, "o_proj on the GPU's attention output")

@@ -1,0 +1,210 @@
+"""GPU parity of mla_attend_prefill against the fp64 oracle.
+
+Gates (floating point): the float32-store output is within 1e-2 max-abs of
+the oracle's unrounded output; the bf16 output is bit-identical to the
+round-to-nearest-even of the float32 output and within 1e-2 plus half a bf16
+spacing of the oracle; lse within 1e-2.  Gates (exact): with V = 1 every
+output is 1 within 1e-5 (the weights that multiply V sum to the normaliser);
+with zero queries exp(lse) rounds to the exact number of visible keys
+(causal predicate and tile skipping); outputs of rows before a perturbed
+position are bit-identical; head permutation permutes outputs bit-exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_mla_amd as mla
+from transformer_attention_mla_amd import inputs
+
+from _gpu_helpers import (SCALE, SUM_TOL, TOL, bits, check_bf16_close, check_bf16_is_rne_of_f32,
+                          check_close, say, to_host64)
+
+pytestmark = pytest.mark.gpu
+
+
+def run(d, dev, **kw):
+    g = {k: v.to(dev) for k, v in d.items()}
+    out, lse = mla.mla_attend_prefill(g["q_nope"], g["q_pe"], g["k_nope"], g["k_pe"], g["v"], g["R"],
+                                      SCALE, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_full(d):
+    return oracle.prefill(bits(d["q_nope"]), bits(d["q_pe"]), bits(d["k_nope"]), bits(d["k_pe"]),
+                          bits(d["v"]), d["R"].numpy(), SCALE)
+
+
+SHAPES = [(1, 1, 1), (1, 3, 17), (2, 3, 63), (1, 2, 64), (1, 3, 65), (1, 2, 129), (3, 1, 100),
+          (1, 5, 200), (1, 64, 64), (2, 4, 1000)]
+
+
+@pytest.mark.parametrize("B,H,T", SHAPES)
+def test_prefill_parity(B, H, T, gpu_device):
+    say(f"prefill parity B={B} H={H} T={T}")
+    d = inputs.prefill_inputs(B, H, T, workload=0)
+    want, want_lse = oracle_full(d)
+    out32, lse = run(d, gpu_device, out_f32=True, want_lse=True)
+    out16, lse16 = run(d, gpu_device, want_lse=True)
+    check_close(to_host64(out32), want, TOL, "float32 output vs oracle")
+    check_bf16_is_rne_of_f32(out16, out32)
+    check_bf16_close(out16, want, "bf16 output vs oracle")
+    check_close(to_host64(lse), want_lse, TOL, "lse vs oracle")
+    assert torch.equal(lse, lse16)
+    out32b, _ = run(d, gpu_device, out_f32=True)
+    assert torch.equal(out32, out32b), "prefill is not deterministic"
+
+
+def test_prefill_workload1_full(gpu_device):
+    """The 64-position, 64-head workload, every row."""
+    B, H, T = 1, 64, 64
+    say("prefill workload 1 full")
+    d = inputs.prefill_inputs(B, H, T, workload=1)
+    want, want_lse = oracle_full(d)
+    out32, lse = run(d, gpu_device, out_f32=True, want_lse=True)
+    out16, _ = run(d, gpu_device)
+    check_close(to_host64(out32), want, TOL, "float32 output vs oracle")
+    check_bf16_is_rne_of_f32(out16, out32)
+    check_bf16_close(out16, want, "bf16 output vs oracle")
+    check_close(to_host64(lse), want_lse, TOL, "lse vs oracle")
+
+
+def test_prefill_workload2_full(gpu_device):
+    """The 1024-position, 64-head workload, every row."""
+    B, H, T = 1, 64, 1024
+    say("prefill workload 2 full")
+    d = inputs.prefill_inputs(B, H, T, workload=2)
+    want, want_lse = oracle_full(d)
+    out32, lse = run(d, gpu_device, out_f32=True, want_lse=True)
+    out16, _ = run(d, gpu_device)
+    check_close(to_host64(out32), want, TOL, "float32 output vs oracle")
+    check_bf16_is_rne_of_f32(out16, out32)
+    check_bf16_close(out16, want, "bf16 output vs oracle")
+    check_close(to_host64(lse), want_lse, TOL, "lse vs oracle")
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 2, 1), (2, 3, 129), (1, 4, 1000)])
+def test_prefill_weights_sum_to_one(B, H, T, gpu_device):
+    say(f"prefill V=1 probe B={B} H={H} T={T}")
+    d = inputs.prefill_inputs(B, H, T, workload=0)
+    d["v"] = torch.ones_like(d["v"])
+    out32, _ = run(d, gpu_device, out_f32=True)
+    err = (out32.double() - 1).abs().max().item()
+    say(f"  max |out - 1| = {err:.3e}")
+    assert err <= SUM_TOL
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 3, 65), (2, 2, 257), (1, 2, 2000)])
+def test_prefill_count_probe(B, H, T, gpu_device):
+    """Zero queries: every visible key has weight exp(0) = 1, so exp(lse)
+    must round to t + 1 (bit-exact integer check of mask and tiles)."""
+    say(f"prefill count probe B={B} H={H} T={T}")
+    d = inputs.prefill_inputs(B, H, T, workload=0)
+    d["q_nope"].zero_()
+    d["q_pe"].zero_()
+    out32, lse = run(d, gpu_device, out_f32=True, want_lse=True)
+    counts = torch.round(torch.exp(lse.double())).to(torch.int64).cpu()
+    want = torch.arange(1, T + 1).expand(B, H, T)
+    assert torch.equal(counts, want)
+    # and the outputs are the causal prefix means of V
+    v = d["v"].double()
+    means = torch.cumsum(v, dim=2) / torch.arange(1, T + 1, dtype=torch.float64)[None, None, :, None]
+    want_out = means.transpose(1, 2).reshape(B, T, H * 128).numpy()
+    check_close(to_host64(out32), want_out, TOL, "prefix means")
+
+
+def test_prefill_future_perturbation(gpu_device):
+    B, H, T, t0 = 1, 3, 300, 140
+    say("prefill future perturbation")
+    d = inputs.prefill_inputs(B, H, T, workload=0)
+    out1, lse1 = run(d, gpu_device, out_f32=True, want_lse=True)
+    d2 = {k: v.clone() for k, v in d.items()}
+    g = torch.Generator().manual_seed(99)
+    for k in ("k_nope", "k_pe", "v"):
+        x = d2[k]
+        x[:, :, t0 + 1:] = torch.randn(x[:, :, t0 + 1:].shape, generator=g).to(torch.bfloat16)
+    out2, lse2 = run(d2, gpu_device, out_f32=True, want_lse=True)
+    assert torch.equal(out1[:, :t0 + 1], out2[:, :t0 + 1])
+    assert torch.equal(lse1[:, :, :t0 + 1], lse2[:, :, :t0 + 1])
+    assert not torch.equal(out1[:, t0 + 1:], out2[:, t0 + 1:])
+
+
+def test_prefill_head_permutation(gpu_device):
+    B, H, T = 1, 6, 150
+    say("prefill head permutation")
+    d = inputs.prefill_inputs(B, H, T, workload=0)
+    perm = torch.tensor([3, 0, 5, 1, 4, 2])
+    dp = dict(d)
+    for k in ("q_nope", "q_pe", "k_nope", "v"):
+        dp[k] = d[k][:, perm].contiguous()
+    out, lse = run(d, gpu_device, out_f32=True, want_lse=True)
+    outp, lsep = run(dp, gpu_device, out_f32=True, want_lse=True)
+    assert torch.equal(outp.view(B, T, H, 128), out.view(B, T, H, 128)[:, :, perm.to(out.device)])
+    assert torch.equal(lsep, lse[:, perm.to(lse.device)])
+
+
+def test_prefill_single_position_returns_v(gpu_device):
+    d = inputs.prefill_inputs(2, 3, 1, workload=0)
+    out, _ = run(d, gpu_device)
+    assert torch.equal(out.cpu().view(2, 1, 3, 128), d["v"].transpose(1, 2))
+
+
+def test_prefill_one_hot_head(gpu_device):
+    B, H, T, h = 1, 4, 70, 2
+    d = inputs.prefill_inputs(B, H, T, workload=0)
+    v = torch.zeros_like(d["v"])
+    v[:, h] = d["v"][:, h]
+    d["v"] = v
+    out, _ = run(d, gpu_device, out_f32=True)
+    o = out.view(B, T, H, 128).cpu()
+    assert torch.all(o[:, :, [i for i in range(H) if i != h]] == 0)
+    assert torch.all(o[:, :, h].abs().sum(-1) > 0)
+
+
+def test_prefill_longer_angle_table(gpu_device):
+    """R may have more rows than T; only rows 0..T-1 are used."""
+    B, H, T = 1, 2, 90
+    d = inputs.prefill_inputs(B, H, T, workload=0, r_rows=500)
+    want, _ = oracle_full(d)
+    out32, _ = run(d, gpu_device, out_f32=True)
+    check_close(to_host64(out32), want, TOL, "float32 output vs oracle (r_rows > T)")
+
+
+def sampled_rows(T, n_rand, rng):
+    rows = set(range(min(128, T))) | set(range(max(0, T - 128), T))
+    rows |= set(rng.integers(0, T, n_rand).tolist())
+    return np.array(sorted(rows), np.int32)
+
+
+@pytest.mark.parametrize("workload", [3, 4])
+def test_prefill_large_workloads_sampled(workload, gpu_device):
+    """Workloads 3 (B=4, T=4096) and 4 (B=1, T=16384, YaRN angles) in the
+    configuration the benchmark times; the oracle computes sampled rows
+    (first 128, last 128 and 256 random per sampled head) exactly."""
+    w = inputs.WORKLOADS[workload]
+    B, H, T = w["B"], w["H"], w["T"]
+    say(f"prefill workload {workload} sampled B={B} H={H} T={T}")
+    d = inputs.prefill_inputs(B, H, T, workload=workload, device=gpu_device)
+    out32, lse = mla.mla_attend_prefill(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"],
+                                        d["R"], SCALE, out_f32=True, want_lse=True)
+    out16, _ = mla.mla_attend_prefill(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"],
+                                      d["R"], SCALE)
+    torch.cuda.synchronize()
+    check_bf16_is_rne_of_f32(out16, out32)
+    rng = np.random.default_rng(workload)
+    R = d["R"].cpu().numpy()
+    worst = 0.0
+    for b, h in [(0, 0), (B - 1, H - 1), (B // 2, 17)]:
+        sl = lambda t: bits(t[b:b + 1, h:h + 1]) if t.shape[1] == H else bits(t[b:b + 1])
+        rows = sampled_rows(T, 256, rng)
+        sel = np.stack([np.zeros_like(rows), np.zeros_like(rows), rows], 1)
+        o, l = oracle.prefill_rows(sl(d["q_nope"]), sl(d["q_pe"]), sl(d["k_nope"]), sl(d["k_pe"]),
+                                   sl(d["v"]), R, SCALE, sel)
+        got = to_host64(out32[b, torch.from_numpy(rows).long().to(gpu_device), h * 128:(h + 1) * 128])
+        worst = max(worst, check_close(got, o, TOL, f"b={b} h={h} {len(rows)} rows"))
+        gl = to_host64(lse[b, h, torch.from_numpy(rows).long().to(gpu_device)])
+        check_close(gl, l, TOL, f"b={b} h={h} lse")
+        g16 = out16[b, torch.from_numpy(rows).long().to(gpu_device), h * 128:(h + 1) * 128]
+        check_bf16_close(g16, o, f"b={b} h={h} bf16")
+    say(f"  worst {worst:.3e}")

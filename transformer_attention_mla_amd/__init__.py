@@ -1,0 +1,239 @@
+"""Python binding of ``libmla.so``: Kimi K2 latent-attention (MLA)
+attend-and-combine on MI355X (gfx950).
+
+The functions carry the C-ABI names (see ``include/mla.h``) and only marshal
+arguments: they check torch tensors (device, dtype, layout, shapes), allocate
+outputs and workspaces through torch when the caller passes none, hand raw
+device pointers and the current HIP stream to the library, and raise
+``MlaError`` (a ``ValueError``) on a nonzero status.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MLA_OUT_F32", "MlaError", "lib", "mla_abi_version", "mla_status_string",
+    "mla_prefill_workspace_bytes", "mla_attend_prefill", "mla_decode_splits",
+    "mla_decode_workspace_bytes", "mla_attend_decode", "mla_out_proj_workspace_bytes",
+    "mla_out_proj", "NOPE", "ROPE", "VDIM", "PAIRS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+
+MLA_OUT_F32 = 0x1
+NOPE, ROPE, VDIM, PAIRS = 128, 64, 128, 32
+
+_lib = None
+
+
+class MlaError(ValueError):
+    """A nonzero status from the library (mirrors the pages' ValueError on bad shapes)."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {mla_status_string(status)}")
+
+
+def lib():
+    """The loaded ``libmla.so`` with ctypes signatures.  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m transformer_attention_mla_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, U, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_float
+    L.mla_abi_version.argtypes = []
+    L.mla_abi_version.restype = I
+    L.mla_status_string.argtypes = [I]
+    L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_prefill_workspace_bytes.argtypes = [I, I, I]
+    L.mla_prefill_workspace_bytes.restype = Z
+    L.mla_attend_prefill.argtypes = [P, P, P, P, P, P, I, F, I, I, I, P, Z, P, P, U, P]
+    L.mla_attend_prefill.restype = I
+    L.mla_decode_splits.argtypes = [I, I, I, I]
+    L.mla_decode_splits.restype = I
+    L.mla_decode_workspace_bytes.argtypes = [I, I, I, I]
+    L.mla_decode_workspace_bytes.restype = Z
+    L.mla_attend_decode.argtypes = [P, P, P, P, P, I, I, F, I, I, I, I, P, Z, P, P, U, P]
+    L.mla_attend_decode.restype = I
+    L.mla_out_proj_workspace_bytes.argtypes = [I, I, I]
+    L.mla_out_proj_workspace_bytes.restype = Z
+    L.mla_out_proj.argtypes = [P, P, P, I, I, I, P, Z, U, P]
+    L.mla_out_proj.restype = I
+    _lib = L
+    return L
+
+
+def mla_abi_version() -> int:
+    return lib().mla_abi_version()
+
+
+def mla_status_string(status: int) -> str:
+    return lib().mla_status_string(int(status)).decode()
+
+
+def mla_prefill_workspace_bytes(B: int, H: int, T: int) -> int:
+    return lib().mla_prefill_workspace_bytes(B, H, T)
+
+
+def mla_decode_splits(B: int, H: int, L: int, num_splits: int = 0) -> int:
+    return lib().mla_decode_splits(B, H, L, num_splits)
+
+
+def mla_decode_workspace_bytes(B: int, H: int, L: int, num_splits: int = 0) -> int:
+    return lib().mla_decode_workspace_bytes(B, H, L, num_splits)
+
+
+def mla_out_proj_workspace_bytes(M: int, K: int, N: int) -> int:
+    return lib().mla_out_proj_workspace_bytes(M, K, N)
+
+
+# ------------------------------------------------------------------ helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(t, name, dtype, shape, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _workspace(workspace, nbytes, device):
+    torch = _torch()
+    if nbytes == 0:
+        return workspace, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ------------------------------------------------------------------ calls
+
+def mla_attend_prefill(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, out=None, lse=None,
+                       want_lse=False, out_f32=False, workspace=None, stream=None):
+    """Causal prefill attention.  Shapes: q_nope/k_nope/v [B,H,T,128] bf16,
+    q_pe [B,H,T,64] bf16 (unrotated), k_pe [B,1,T,64] bf16 (unrotated, shared
+    by heads), R [r_rows,32] float32 (angles, r_rows >= T).  Returns
+    (out [B,T,H*128] bf16 or float32, lse [B,H,T] float32 or None)."""
+    torch = _torch()
+    if q_nope.dim() != 4:
+        raise ValueError("q_nope must be [B, H, T, 128]")
+    B, H, T, _ = q_nope.shape
+    dev = q_nope.device
+    bf = torch.bfloat16
+    _check(q_nope, "q_nope", bf, (B, H, T, NOPE), dev)
+    _check(q_pe, "q_pe", bf, (B, H, T, ROPE), dev)
+    _check(k_nope, "k_nope", bf, (B, H, T, NOPE), dev)
+    _check(k_pe, "k_pe", bf, (B, 1, T, ROPE), dev)
+    _check(v, "v", bf, (B, H, T, VDIM), dev)
+    if R.dim() != 2:
+        raise ValueError("R must be [r_rows, 32]")
+    _check(R, "R", torch.float32, (R.shape[0], PAIRS), dev)
+    odt = torch.float32 if out_f32 else bf
+    if out is None:
+        out = torch.empty((B, T, H * VDIM), dtype=odt, device=dev)
+    _check(out, "out", odt, (B, T, H * VDIM), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H, T), dev)
+    workspace, ws_bytes = _workspace(workspace, mla_prefill_workspace_bytes(B, H, T), dev)
+    rc = lib().mla_attend_prefill(_ptr(q_nope), _ptr(q_pe), _ptr(k_nope), _ptr(k_pe), _ptr(v),
+                                  _ptr(R), R.shape[0], float(softmax_scale), B, H, T,
+                                  _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                                  MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_attend_prefill")
+    return out, lse
+
+
+def mla_attend_decode(q_nope, q_pe, k_cache, v_cache, R, q_pos, softmax_scale, *, num_splits=0,
+                      out=None, lse=None, want_lse=False, out_f32=False, workspace=None,
+                      stream=None):
+    """Decode attention for one new query per (b, h).  Shapes: q_nope [B,H,128],
+    q_pe [B,H,64] (unrotated; rotated at q_pos), k_cache [B,H,L,192] (rotated
+    keys), v_cache [B,H,L,128], R [r_rows,32].  Returns (out [B,H*128], lse [B,H] or None)."""
+    torch = _torch()
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, H, L, 192]")
+    B, H, L, _ = k_cache.shape
+    dev = k_cache.device
+    bf = torch.bfloat16
+    _check(q_nope, "q_nope", bf, (B, H, NOPE), dev)
+    _check(q_pe, "q_pe", bf, (B, H, ROPE), dev)
+    _check(k_cache, "k_cache", bf, (B, H, L, NOPE + ROPE), dev)
+    _check(v_cache, "v_cache", bf, (B, H, L, VDIM), dev)
+    if R.dim() != 2:
+        raise ValueError("R must be [r_rows, 32]")
+    _check(R, "R", torch.float32, (R.shape[0], PAIRS), dev)
+    odt = torch.float32 if out_f32 else bf
+    if out is None:
+        out = torch.empty((B, H * VDIM), dtype=odt, device=dev)
+    _check(out, "out", odt, (B, H * VDIM), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H), dev)
+    need = mla_decode_workspace_bytes(B, H, L, num_splits)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
+    rc = lib().mla_attend_decode(_ptr(q_nope), _ptr(q_pe), _ptr(k_cache), _ptr(v_cache), _ptr(R),
+                                 R.shape[0], int(q_pos), float(softmax_scale), B, H, L,
+                                 int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                                 MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_attend_decode")
+    return out, lse
+
+
+def mla_out_proj(x, w_o, *, y=None, out_f32=False, workspace=None, stream=None):
+    """y = x · w_oᵀ with x [M,K] bf16 and w_o [N,K] bf16 (a linear layer's
+    weight, one row per output feature).  Returns y [M,N] bf16 or float32."""
+    torch = _torch()
+    if x.dim() != 2 or w_o.dim() != 2:
+        raise ValueError("x must be [M, K] and w_o [N, K]")
+    M, K = x.shape
+    N = w_o.shape[0]
+    dev = x.device
+    bf = torch.bfloat16
+    _check(x, "x", bf, (M, K), dev)
+    _check(w_o, "w_o", bf, (N, K), dev)
+    odt = torch.float32 if out_f32 else bf
+    if y is None:
+        y = torch.empty((M, N), dtype=odt, device=dev)
+    _check(y, "y", odt, (M, N), dev)
+    workspace, ws_bytes = _workspace(workspace, mla_out_proj_workspace_bytes(M, K, N), dev)
+    rc = lib().mla_out_proj(_ptr(x), _ptr(w_o), _ptr(y), M, K, N, _ptr(workspace), ws_bytes,
+                            MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_out_proj")
+    return y

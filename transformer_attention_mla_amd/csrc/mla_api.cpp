@@ -1,0 +1,261 @@
+// C ABI of the MLA library (declared in include/mla.h): argument validation,
+// workspace layout and kernel launches on the caller's stream.
+//
+// Error convention: the page "Kimi K2 · Mix and project" (code excerpt
+// "mla-prefill") raises ValueError when the score or mask shapes are not
+// (bsz, heads, q_len, kv_len) / (bsz, 1, q_len, kv_len) and asserts that a mask
+// exists.  Here every such check becomes a status code returned before any
+// work is enqueued; nothing is thrown or aborted across the boundary.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+using mla::kNope;
+using mla::kQK;
+using mla::kRope;
+using mla::kV;
+
+constexpr long long kMaxDim = 1LL << 24;      // any single size
+constexpr long long kMaxElems = 1LL << 40;    // any tensor
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Outputs may not overlap inputs or each other.
+bool any_alias(const Range* in, int n_in, const Range* out, int n_out) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(out[i], in[j])) return true;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(out[i], out[j])) return true;
+  }
+  return false;
+}
+
+bool dims_ok(long long a, long long b, long long c, long long d) {
+  if (a <= 0 || b <= 0 || c <= 0 || d <= 0) return false;
+  if (a > kMaxDim || b > kMaxDim || c > kMaxDim || d > kMaxDim) return false;
+  return a * b <= kMaxElems && a * b * c <= kMaxElems && a * b * c * d <= kMaxElems;
+}
+
+// The kernels are built for gfx950 only; check the current device once.
+int check_device() {
+  static std::atomic<int> cache[64];  // 0 unknown, 1 gfx950, 2 other
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MLA_ERR_DEVICE;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 1) return MLA_OK;
+    if (c == 2) return MLA_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? MLA_OK : MLA_ERR_DEVICE;
+}
+
+size_t decode_ws_bytes(int B, int H, int splits) {
+  if (splits <= 1) return 0;
+  return (size_t)B * H * splits * mla::kDecodePart * sizeof(float);
+}
+
+size_t oproj_ws_bytes(int M, int N, int splits) {
+  if (splits <= 1) return 0;
+  return (size_t)splits * M * N * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_DIM: return "MLA_ERR_DIM: invalid or inconsistent size";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: pointer not 16-byte aligned";
+    case MLA_ERR_ALIAS: return "MLA_ERR_ALIAS: an output overlaps an input or another output";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_SCALE: return "MLA_ERR_SCALE: softmax_scale must be finite and > 0";
+    case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: current device is not gfx950";
+    case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: kernel launch failed";
+    case MLA_ERR_FLAGS: return "MLA_ERR_FLAGS: unknown flag bits";
+    default: return "unknown status";
+  }
+}
+
+// ------------------------------------------------------------------ prefill
+
+size_t mla_prefill_workspace_bytes(int B, int H, int T) {
+  if (!dims_ok(B, H, T, kQK)) return 0;
+  return mla::prefill_workspace_layout(B, T).total;
+}
+
+int mla_attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16* k_nope,
+                       const mla_bf16* k_pe, const mla_bf16* v, const float* R, int r_rows,
+                       float softmax_scale, int B, int H, int T, void* workspace,
+                       size_t workspace_bytes, void* out, float* lse, uint32_t flags,
+                       void* stream) {
+  if (!q_nope || !q_pe || !k_nope || !k_pe || !v || !R || !out) return MLA_ERR_NULL;
+  if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
+  if (!dims_ok(B, H, T, kQK) || r_rows <= 0 || r_rows > kMaxDim || T > r_rows) return MLA_ERR_DIM;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_SCALE;
+  const mla::PrefillWorkspace ws = mla::prefill_workspace_layout(B, T);
+  if (!workspace || workspace_bytes < ws.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(k_nope) || !aligned16(k_pe) ||
+      !aligned16(v) || !aligned16(R) || !aligned16(out) || !aligned16(lse) || !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  const size_t bht = (size_t)B * H * T;
+  const size_t out_elt = (flags & MLA_OUT_F32) ? 4 : 2;
+  const Range in[] = {{q_nope, bht * kNope * 2}, {q_pe, bht * kRope * 2}, {k_nope, bht * kNope * 2},
+                      {k_pe, (size_t)B * T * kRope * 2}, {v, bht * kV * 2},
+                      {R, (size_t)r_rows * mla::kPairs * 4}};
+  const Range outs[] = {{out, bht * kV * out_elt}, {lse, lse ? bht * 4 : 0}, {workspace, ws.total}};
+  if (any_alias(in, 6, outs, 3)) return MLA_ERR_ALIAS;
+  const int dev = check_device();
+  if (dev != MLA_OK) return dev;
+
+  mla::PrefillParams p;
+  p.q_nope = q_nope;
+  p.q_pe = q_pe;
+  p.k_nope = k_nope;
+  p.k_pe = k_pe;
+  p.v = v;
+  p.R = R;
+  p.cs = reinterpret_cast<float2*>(static_cast<char*>(workspace) + ws.cs_off);
+  p.kpe_rot = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + ws.kpe_off);
+  p.out = out;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.T = T;
+  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // start from a clean error state
+  if (mla::launch_rope_prep(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  if (mla::launch_prefill(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+// ------------------------------------------------------------------- decode
+
+int mla_decode_splits(int B, int H, int L, int num_splits) {
+  if (!dims_ok(B, H, L, kQK) || num_splits < 0) return 0;
+  return mla::decode_choose_splits(B, H, L, num_splits);
+}
+
+size_t mla_decode_workspace_bytes(int B, int H, int L, int num_splits) {
+  const int s = mla_decode_splits(B, H, L, num_splits);
+  if (s <= 0) return 0;
+  return decode_ws_bytes(B, H, s);
+}
+
+int mla_attend_decode(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16* k_cache,
+                      const mla_bf16* v_cache, const float* R, int r_rows, int q_pos,
+                      float softmax_scale, int B, int H, int L, int num_splits, void* workspace,
+                      size_t workspace_bytes, void* out, float* lse, uint32_t flags,
+                      void* stream) {
+  if (!q_nope || !q_pe || !k_cache || !v_cache || !R || !out) return MLA_ERR_NULL;
+  if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
+  if (!dims_ok(B, H, L, kQK) || r_rows <= 0 || r_rows > kMaxDim || q_pos < 0 || q_pos >= r_rows ||
+      num_splits < 0)
+    return MLA_ERR_DIM;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_SCALE;
+  const int splits = mla::decode_choose_splits(B, H, L, num_splits);
+  const size_t need = decode_ws_bytes(B, H, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(R) || !aligned16(out) || !aligned16(lse) || !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  const size_t bh = (size_t)B * H;
+  const size_t out_elt = (flags & MLA_OUT_F32) ? 4 : 2;
+  const Range in[] = {{q_nope, bh * kNope * 2}, {q_pe, bh * kRope * 2},
+                      {k_cache, bh * L * kQK * 2}, {v_cache, bh * L * kV * 2},
+                      {R, (size_t)r_rows * mla::kPairs * 4}};
+  const Range outs[] = {{out, bh * kV * out_elt}, {lse, lse ? bh * 4 : 0},
+                        {need ? workspace : nullptr, need}};
+  if (any_alias(in, 5, outs, 3)) return MLA_ERR_ALIAS;
+  const int dev = check_device();
+  if (dev != MLA_OK) return dev;
+
+  mla::DecodeParams p;
+  p.q_nope = q_nope;
+  p.q_pe = q_pe;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.R = R;
+  p.q_pos = q_pos;
+  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  p.B = B;
+  p.H = H;
+  p.L = L;
+  p.splits = splits;
+  p.part = static_cast<float*>(need ? workspace : nullptr);
+  p.out = out;
+  p.lse = lse;
+  p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
+  (void)hipGetLastError();
+  if (mla::launch_decode(p, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+// ------------------------------------------------------------------- o_proj
+
+size_t mla_out_proj_workspace_bytes(int M, int K, int N) {
+  if (!dims_ok(M, K, N, 1) || K % 128 != 0) return 0;
+  return oproj_ws_bytes(M, N, mla::oproj_choose_splits(M, K, N));
+}
+
+int mla_out_proj(const mla_bf16* x, const mla_bf16* w_o, void* y, int M, int K, int N,
+                 void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  if (!x || !w_o || !y) return MLA_ERR_NULL;
+  if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
+  if (!dims_ok(M, K, N, 1) || K % 128 != 0 || (long long)M * N > kMaxElems) return MLA_ERR_DIM;
+  const int splits = mla::oproj_choose_splits(M, K, N);
+  const size_t need = oproj_ws_bytes(M, N, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w_o) || !aligned16(y) || !aligned16(workspace)) return MLA_ERR_ALIGN;
+  const size_t out_elt = (flags & MLA_OUT_F32) ? 4 : 2;
+  const Range in[] = {{x, (size_t)M * K * 2}, {w_o, (size_t)N * K * 2}};
+  const Range outs[] = {{y, (size_t)M * N * out_elt}, {need ? workspace : nullptr, need}};
+  if (any_alias(in, 2, outs, 2)) return MLA_ERR_ALIAS;
+  const int dev = check_device();
+  if (dev != MLA_OK) return dev;
+
+  mla::OprojParams p;
+  p.x = x;
+  p.w = w_o;
+  p.y = y;
+  p.part = static_cast<float*>(need ? workspace : nullptr);
+  p.M = M;
+  p.K = K;
+  p.N = N;
+  p.splits = splits;
+  p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
+  (void)hipGetLastError();
+  if (mla::launch_oproj(p, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+}  // extern "C"

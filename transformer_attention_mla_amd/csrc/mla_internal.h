@@ -1,0 +1,95 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer of the
+// MLA library.  Not installed; the public interface is include/mla.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Head widths of Kimi K2's latent attention (config.json on the page "Block
+// input": qk_nope_head_dim, qk_rope_head_dim, v_head_dim).
+constexpr int kNope = 128;
+constexpr int kRope = 64;
+constexpr int kPairs = 32;
+constexpr int kQK = kNope + kRope;  // 192
+constexpr int kV = 128;
+
+constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- prefill --
+struct PrefillWorkspace {
+  size_t cs_off, cs_bytes;    // float2 [T][32]: (cos, sin) of R[t][i]
+  size_t kpe_off, kpe_bytes;  // bf16 [B][T][64]: rotated shared key
+  size_t total;
+};
+
+inline PrefillWorkspace prefill_workspace_layout(int B, int T) {
+  PrefillWorkspace w;
+  w.cs_off = 0;
+  w.cs_bytes = align_up((size_t)T * kPairs * 8, 256);
+  w.kpe_off = w.cs_off + w.cs_bytes;
+  w.kpe_bytes = align_up((size_t)B * T * kRope * 2, 256);
+  w.total = w.kpe_off + w.kpe_bytes;
+  return w;
+}
+
+struct PrefillParams {
+  const uint16_t* q_nope;
+  const uint16_t* q_pe;
+  const uint16_t* k_nope;
+  const uint16_t* k_pe;
+  const uint16_t* v;
+  const float* R;
+  float2* cs;          // workspace
+  uint16_t* kpe_rot;   // workspace
+  void* out;
+  float* lse;
+  int B, H, T;
+  float scale_log2;    // softmax_scale * log2(e)
+  int out_f32;
+};
+
+hipError_t launch_rope_prep(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+// ----------------------------------------------------------------- decode --
+struct DecodeParams {
+  const uint16_t* q_nope;
+  const uint16_t* q_pe;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const float* R;
+  int q_pos;
+  float scale_log2;
+  int B, H, L;
+  int splits;
+  float* part;  // workspace [B][H][splits][kDecodePart] when splits > 1
+  void* out;
+  float* lse;
+  int out_f32;
+};
+
+// One split partial: running max (base-2 scaled units), sum, 128 outputs,
+// padded to 136 floats (544 bytes, a multiple of 16).
+constexpr int kDecodePart = 136;
+
+int decode_choose_splits(int B, int H, int L, int requested);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+// ----------------------------------------------------------------- o_proj --
+struct OprojParams {
+  const uint16_t* x;  // [M][K]
+  const uint16_t* w;  // [N][K]
+  void* y;            // [M][N]
+  float* part;        // [splits][M][N] when splits > 1
+  int M, K, N;
+  int splits;
+  int out_f32;
+};
+
+int oproj_choose_splits(int M, int K, int N);
+hipError_t launch_oproj(const OprojParams& p, hipStream_t stream);
+
+}  // namespace mla
