@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--decode-splits", type=int, default=0)
     ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before the steps, run a plain streaming kernel over 1 GiB (read 1 GiB, "
+                         "write 1 GiB) three times, to scale hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -156,6 +159,13 @@ def main():
                 num_splits=args.decode_splits, out=dec_out, workspace=ws_d))
             timed("decode_oproj", lambda: mla.mla_out_proj(dec_out, w_o, y=y_d, workspace=ws_od))
 
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     print("warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()

@@ -8,286 +8,380 @@
 // is stored transposed to [B, T, heads·128], head-major.  Page "Kimi K2 ·
 // Transformer blocks": causal mask M [T queries, T keys], positions 0..T-1.
 //
-// Design (one workgroup = G heads × BQ queries of one sequence):
-//   * Each wave owns 32 queries of one head.  It computes Sᵀ = K·Qᵀ with
-//     v_mfma_f32_32x32x16_bf16: the key tile is the A operand (from LDS) and
-//     the query the B operand (kept in registers for the whole key loop, with
-//     q_pe rotated in registers on load).  In the transposed product every lane
-//     holds 16 scores of ONE query, so the row max/sum of the online softmax
-//     are per-lane values plus one exchange between the two half-waves.
-//   * The 192-long contraction is 8 MFMA k-steps over k_nope and 4 over the
-//     rotated shared key; the rotated key tile is staged into LDS once per
-//     workgroup and read by every head of the workgroup.
-//   * Oᵀ += Vᵀ·Pᵀ: the bf16-rounded weights stay in registers as the B operand;
-//     the order in which the A lanes fetch key rows is permuted so that the
-//     accumulator layout of Sᵀ is exactly the B-operand layout of Pᵀ (no data
-//     movement).  V is stored transposed in LDS ([dim][key]).
-//   * Online softmax in base 2 with softmax_scale·log2(e) folded into one FMA;
-//     the running sum is accumulated from the same bf16-rounded weights that
-//     enter the PV product, so the weights that multiply V sum exactly to the
-//     normaliser up to float32 summation order.
-//   * Causal tiles: a workgroup loads only key tiles up to its last query;
-//     a wave skips tiles entirely after its queries and masks (j > i) only on
-//     tiles that straddle its diagonal.  The longest query tiles are issued
-//     first so the causal triangle does not leave an idle tail.
+// Work decomposition
+//   * A workgroup (8 waves) owns 2 heads × 128 queries of one sequence; each
+//     wave owns 32 queries of one head.  It processes a pair of query tiles,
+//     i and NQ-1-i, one after the other, so every workgroup does the same
+//     amount of causal work.  Workgroups of the same (sequence, head pair) are
+//     placed on the same XCD and issued together, so that XCD's L2 serves
+//     their shared key/value stream.
+//   * Per key tile (64 keys) the workgroup stages k_nope of both heads, the
+//     rotated shared rotary key (once for both heads) and V of both heads in
+//     LDS, with asynchronous buffer→LDS copies into a second buffer while the
+//     current tile is multiplied.
+//
+// Per wave and key tile
+//   * Sᵀ = K·Qᵀ with v_mfma_f32_32x32x16_bf16: the key tile is the A operand
+//     (LDS), the query the B operand (registers for the whole pass; q_pe is
+//     rotated on load).  In the transposed product every lane holds scores of
+//     ONE query, so the softmax statistics are per-lane values plus one
+//     exchange between half-waves.  192 = 8 k-steps over k_nope + 4 over the
+//     shared rotated key.
+//   * Key rows are stored in LDS in the order the A lanes read them, chosen so
+//     that the Sᵀ accumulator registers are directly the B-operand layout of
+//     Pᵀ in Oᵀ += Vᵀ·Pᵀ (no data movement between the two products).
+//   * Vᵀ fragments come from V's natural [key][dim] layout with the gfx950
+//     transposing LDS read ds_read_b64_tr_b16.
+//   * Online softmax in base 2, softmax_scale·log2(e) folded into one FMA.  The
+//     reference maximum is only raised when a tile's maximum exceeds it by
+//     more than 8 (weights then stay <= 2^8); the result is the same softmax.
+//     The row sum is accumulated (v_dot2_f32_bf16 against ones) from the same
+//     bf16-rounded weights that enter the PV product.
 #include "mla_device.h"
 #include "mla_internal.h"
 
 namespace mla {
 namespace {
 
-constexpr int BK = 64;             // keys per tile
-constexpr int VT_STRIDE = BK + 8;  // Vᵀ LDS row stride in elements (144 B: conflict-free reads)
+constexpr int G = 2;          // heads per workgroup
+constexpr int WPH = 4;        // waves per head
+constexpr int NW = G * WPH;   // 8 waves
+constexpr int NT = 64 * NW;   // 512 threads
+constexpr int BQ = 32 * WPH;  // 128 queries per head per tile
+constexpr int BK = 64;        // keys per tile
+constexpr float TAU = 8.0f;   // lazy-rescale threshold (log2 units)
 
-// XOR swizzle of the 16-byte chunks of a key row in LDS.  Lanes that read the
-// same logical chunk of different key rows land on distinct bank groups.
-__device__ __forceinline__ int kswz(int key) {
-  return (key & 3) | (((key >> 3) & 1) << 2) | (((key >> 2) & 1) << 3);
-}
+// LDS stage layout (bytes)
+constexpr int K_ROW = 272;                  // 256 B of k_nope + 16 B pad (17 slots)
+constexpr int K_HEAD = BK * K_ROW;          // 17408
+constexpr int KP_ROW = 144;                 // 128 B of rotated key + 16 B pad (9 slots)
+constexpr int V_ROW = 256;                  // natural layout, 64 B blocks XOR-swizzled
+constexpr int V_HEAD = BK * V_ROW;          // 16384
+constexpr int KOFF = 0;
+constexpr int KPOFF = KOFF + G * K_HEAD;    // 34816
+constexpr int VOFF = KPOFF + BK * KP_ROW;   // 44032
+constexpr int STAGE = VOFF + G * V_HEAD;    // 76800
 
-// Tile-local key fetched by A-operand lane R (0..31) of a 32-key block.  The
-// accumulator register r of lane (n, h) holds row (r/4)*8 + h*4 + r%4; with
-// this order that row is key (r/4 >> 1)*16 + h*8 + (r/4 & 1)*4 + r%4, so lane
-// half h holds keys h*8..h*8+7 of each 16-key chunk in 8 consecutive
-// registers -- the B-operand layout of the PV product.
+// DMA work per stage, in 1 KiB chunks (one wave-instruction of 64 x 16 B each).
+constexpr int DK = (BK * 17) / 64;           // 17 per head
+constexpr int DKP = (BK * 9) / 64;           // 9
+constexpr int DV = (BK * 16) / 64;           // 16 per head
+
+static_assert(BK * 17 % 64 == 0 && BK * 9 % 64 == 0, "slot counts must fill whole wave loads");
+
+// Tile-local key held in LDS row R of a 32-key block: the key that A-operand
+// lane R fetches.  Accumulator register r of lane (n, h) is row
+// (r/4)*8 + h*4 + r%4; with this order it holds key (r/4 >> 1)*16 + h*8 +
+// (r/4 & 1)*4 + r%4, so lane half h owns keys h*8..h*8+7 of every 16-key
+// chunk in 8 consecutive registers -- the B-operand layout of the PV product.
 __device__ __forceinline__ int akey(int R) {
   const int g4 = R >> 3, h = (R >> 2) & 1, i = R & 3;
   return (g4 >> 1) * 16 + h * 8 + (g4 & 1) * 4 + i;
 }
 
-template <int G, int WPH>
-struct Cfg {
-  static constexpr int NW = G * WPH;
-  static constexpr int NT = 64 * NW;
-  static constexpr int BQ = 32 * WPH;
-  static constexpr int SK = G * BK * kNope;   // k_nope tiles, per head
-  static constexpr int SKP = BK * kRope;      // shared rotated key tile
-  static constexpr int SVT = G * kV * VT_STRIDE;
-  static constexpr int LDS_BYTES = 2 * (SK + SKP + SVT);
-};
+__shared__ __attribute__((aligned(16))) uint8_t lds_a[STAGE];
+__shared__ __attribute__((aligned(16))) uint8_t lds_b[STAGE];
 
-template <int G, int WPH>
-__global__ __launch_bounds__(64 * G * WPH) void prefill_kernel(PrefillParams p) {
-  using C = Cfg<G, WPH>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::SK + C::SKP + C::SVT];
-  uint16_t* sK = smem;
-  uint16_t* sKP = sK + C::SK;
-  uint16_t* sVt = sKP + C::SKP;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wave_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 16, (int)voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 ds_read_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
+__global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 31;
   const int hf = lane >> 5;
 
   const int H = p.H, T = p.T;
   const int HG = (H + G - 1) / G;
-  const int NQ = (T + C::BQ - 1) / C::BQ;
-  const int per_q = p.B * HG;
-  const int id = blockIdx.x;
-  const int qt = NQ - 1 - id / per_q;  // longest query tiles first
-  const int rem = id % per_q;
-  const int b = rem / HG;
-  const int hg = rem % HG;
+  const int NQ = (T + BQ - 1) / BQ;
+  const int NP = (NQ + 1) / 2;  // query-tile pairs
+  const int U = p.B * HG;       // (sequence, head pair) units
 
+  // ---- XCD-aware placement: workgroup P runs on XCD P % 8; give each XCD whole
+  // units, and issue a unit's pairs back to back.
+  int unit, pair;
+  {
+    const int P = blockIdx.x;
+    if (U % 8 == 0) {
+      const int x = P % 8, o = P / 8;
+      unit = x + 8 * (o / NP);
+      pair = o % NP;
+    } else {
+      unit = P / NP;
+      pair = P % NP;
+    }
+  }
+  const int b = unit / HG;
+  const int hg = unit % HG;
   const int g = wave / WPH;
   const int qb = wave % WPH;
   const int head = hg * G + g;
   const bool head_ok = head < H;
-  const int headc = head_ok ? head : H - 1;
-  const int q0 = qt * C::BQ + qb * 32;  // first query of this wave
-  const int myq = q0 + ln;
-  const int myqc = myq < T ? myq : T - 1;
 
-  // ---- query fragments: B operand of Sᵀ = K·Qᵀ, k-step kb covers dims
-  // kb*16 + hf*8 .. +7 of the 192-wide query (0..7 nope, 8..11 rotary).
-  bf16x8 qf[12];
-  {
-    const size_t qrow = ((size_t)b * H + headc) * T + myqc;
-    const uint16_t* qn = p.q_nope + qrow * kNope;
+  // ---- asynchronous tile copies.  The stage buffer is a sequence of 1 KiB
+  // chunks (k_nope head 0 | head 1 | rotated key | V head 0 | head 1); wave w
+  // copies chunks w, w+8, ... of each region.  Every lane's byte offset inside
+  // its sequence's tensor is fixed up to the tile start, added per tile.  One
+  // buffer descriptor per tensor and sequence: rows past the end of the tensor
+  // read as zero; rows past T inside it belong to the next head and are masked.
+  constexpr int NCK = G * DK, NCKP = DKP, NCV = G * DV;  // 34, 9, 32 chunks
+  constexpr int IK = (NCK + NW - 1) / NW, IKP = (NCKP + NW - 1) / NW, IV = (NCV + NW - 1) / NW;
+  uint32_t voffK[IK], voffKP[IKP], voffV[IV];
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) qf[kb] = as_bf16x8(ld_global_16(qn + kb * 16 + hf * 8));
-    const uint16_t* qp = p.q_pe + qrow * kRope;
-    u32x4 x[4];
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) x[pp] = ld_global_16(qp + pp * 16 + hf * 8);
-    const float2* csr = p.cs + (size_t)myqc * kPairs;
-    // Rotary dims pp*16 + hf*8 + e (pp = 0, 1) pair with the dims 32 higher
-    // (pp + 2): rotate in float32 and round to bf16.
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      bf16x8 ylo, yhi;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 c = csr[pp * 16 + hf * 8 + e];
-        const uint32_t wl = x[pp][e >> 1], wh = x[pp + 2][e >> 1];
-        const float lo = (e & 1) ? bf16hi(wl) : bf16lo(wl);
-        const float hi = (e & 1) ? bf16hi(wh) : bf16lo(wh);
-        ylo[e] = f32_to_bf16(fmaf(lo, c.x, -(hi * c.y)));
-        yhi[e] = f32_to_bf16(fmaf(hi, c.x, lo * c.y));
-      }
-      qf[8 + pp] = ylo;
-      qf[10 + pp] = yhi;
-    }
+  for (int i = 0; i < IK; ++i) {
+    const int j = wave + NW * i;
+    const int gg = j / DK;
+    const int hh = min(hg * G + gg, H - 1);
+    const int s = (j % DK) * 64 + lane;
+    const int R = s / 17;
+    int c = s % 17;
+    if (c == 16) c = 15;  // pad slot: harmless duplicate
+    voffK[i] = ((uint32_t)hh * (uint32_t)T + (uint32_t)((R >> 5) * 32 + akey(R & 31))) * 256u + c * 16;
   }
+#pragma unroll
+  for (int i = 0; i < IKP; ++i) {
+    const int s = (wave + NW * i) * 64 + lane;
+    const int R = s / 9;
+    int c = s % 9;
+    if (c == 8) c = 7;
+    voffKP[i] = (uint32_t)(((R >> 5) * 32 + akey(R & 31)) * 128 + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < IV; ++i) {
+    const int j = wave + NW * i;
+    const int gg = j / DV;
+    const int hh = min(hg * G + gg, H - 1);
+    const int s = (j % DV) * 64 + lane;
+    const int row = s / 16;
+    const int c = (s % 16) ^ ((row & 3) << 2);
+    voffV[i] = ((uint32_t)hh * (uint32_t)T + (uint32_t)row) * 256u + c * 16;
+  }
+  const uint32_t seq_bytes = (uint32_t)((size_t)H * T * 256);
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.k_nope + (size_t)b * H * T * kNope, seq_bytes);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.v + (size_t)b * H * T * kV, seq_bytes);
+  const __amdgpu_buffer_rsrc_t rKP = make_rsrc(p.kpe_rot + (size_t)b * T * kRope, (uint32_t)T * 128u);
 
-  const int kend = min(T, qt * C::BQ + C::BQ);  // keys visible to this workgroup
-  const int nkt = (kend + BK - 1) / BK;
+  auto issue_tile = [&](uint8_t* buf, int kt) {
+    const uint32_t k0 = (uint32_t)(kt * BK);
+#pragma unroll
+    for (int i = 0; i < IK; ++i) {
+      const int j = wave + NW * i;
+      if (j < NCK) dma16(rK, buf + KOFF + j * 1024, voffK[i] + k0 * 256u);
+    }
+#pragma unroll
+    for (int i = 0; i < IKP; ++i) {
+      const int j = wave + NW * i;
+      if (j < NCKP) dma16(rKP, buf + KPOFF + j * 1024, voffKP[i] + k0 * 128u);
+    }
+#pragma unroll
+    for (int i = 0; i < IV; ++i) {
+      const int j = wave + NW * i;
+      if (j < NCV) dma16(rV, buf + VOFF + j * 1024, voffV[i] + k0 * 256u);
+    }
+  };
+
+  // Zero both stages once, so rows that a copy leaves unwritten hold finite values.
+  for (int o = tid * 16; o < STAGE; o += NT * 16) {
+    *reinterpret_cast<u32x4*>(lds_a + o) = u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(lds_b + o) = u32x4{0, 0, 0, 0};
+  }
+  __syncthreads();
+
+  // Per-lane LDS addresses for the products.
+  const int k_lane = g * K_HEAD + ln * K_ROW + hf * 16;         // + j*32*K_ROW + kb*32
+  const int kp_lane = ln * KP_ROW + hf * 16;                     // + j*32*KP_ROW + kb*32
+  const int q16 = lane >> 4, s16 = lane & 15;
+  // ds_read_b64_tr_b16: lane s of a 16-lane group addresses key row
+  // (q16/2)*8 + t*4 + s/4 of a 16-key chunk, dims (q16%2)*16 + (s%4)*4 .. +3 of a
+  // 32-dim block; lane i of the group then receives dim (q16%2)*16 + i of the
+  // block for those four keys.
+  const int v_row = (q16 >> 1) * 8 + (s16 >> 2);
+  int v_lane[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    v_lane[db] = g * V_HEAD + v_row * V_ROW +
+                 (((db ^ (s16 >> 2)) * 4 + (q16 & 1) * 2 + ((s16 & 3) >> 1)) * 16) + (s16 & 1) * 8;
+
   const float cl2 = p.scale_log2;
-  const int r_key = akey(ln);
+  const uint32_t ones = 0x3f803f80u;  // bf16 pair (1, 1)
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-  float m_run = -INFINITY;  // running max of scaled scores (base-2 units)
-  float l_run = 0.f;        // this lane's share of the running sum
-  f32x16 acc[4] = {};       // Oᵀ: dims db*32 + (r/4)*8 + hf*4 + r%4, query ln
+  const int npass = (pair == NQ - 1 - pair) ? 1 : 2;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int qt = pass == 0 ? NQ - 1 - pair : pair;  // longer tile first
+    const int q0 = qt * BQ + qb * 32;
+    const int myq = q0 + ln;
+    const int myqc = myq < T ? myq : T - 1;
+    const int headc = head_ok ? head : H - 1;
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * BK;
-    __syncthreads();
-    // ---- stage the key tile: k_nope of each head, shared rotated key, Vᵀ.
-    // Rows past T repeat row T-1 (finite values); they are causally masked.
-    for (int it = tid; it < G * BK * 16; it += C::NT) {
-      const int gg = it / (BK * 16);
-      const int r = (it / 16) % BK;
-      const int ch = it % 16;
-      const int hh = min(hg * G + gg, H - 1);
-      const int key = min(k0 + r, T - 1);
-      const u32x4 v = ld_global_16(p.k_nope + (((size_t)b * H + hh) * T + key) * kNope + ch * 8);
-      *reinterpret_cast<u32x4*>(sK + (gg * BK + r) * kNope + ((ch ^ kswz(r)) * 8)) = v;
-    }
-    for (int it = tid; it < BK * 8; it += C::NT) {
-      const int r = it / 8, ch = it % 8;
-      const int key = min(k0 + r, T - 1);
-      const u32x4 v = ld_global_16(p.kpe_rot + ((size_t)b * T + key) * kRope + ch * 8);
-      *reinterpret_cast<u32x4*>(sKP + r * kRope + ((ch ^ (kswz(r) & 7)) * 8)) = v;
-    }
-    for (int it = tid; it < G * (BK / 8) * 32; it += C::NT) {
-      // 8 keys x 4 dims per item: load rows, transpose in registers.
-      const int gg = it / ((BK / 8) * 32);
-      const int r2 = it % ((BK / 8) * 32);
-      const int kg = r2 / 32, dg = r2 % 32;
-      const int hh = min(hg * G + gg, H - 1);
-      const uint16_t* vb = p.v + ((size_t)b * H + hh) * T * kV + dg * 4;
-      u32x2 w[8];
+    // ---- query fragments (B operand), rotary part rotated in registers
+    bf16x8 qf[12];
+    {
+      const size_t qrow = ((size_t)b * H + headc) * T + myqc;
+      const uint16_t* qn = p.q_nope + qrow * kNope;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int key = min(k0 + kg * 8 + kk, T - 1);
-        w[kk] = ld_global_8(vb + (size_t)key * kV);
-      }
-      uint16_t* dst = sVt + (gg * kV + dg * 4) * VT_STRIDE + kg * 8;
+      for (int kb = 0; kb < 8; ++kb) qf[kb] = as_bf16x8(ld_global_16(qn + kb * 16 + hf * 8));
+      const uint16_t* qp = p.q_pe + qrow * kRope;
+      u32x4 x[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 o;
+      for (int pp = 0; pp < 4; ++pp) x[pp] = ld_global_16(qp + pp * 16 + hf * 8);
+      const float2* csr = p.cs + (size_t)myqc * kPairs;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t a0 = w[2 * e][j >> 1], a1 = w[2 * e + 1][j >> 1];
-          o[e] = (j & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+      for (int pp = 0; pp < 2; ++pp) {
+        bf16x8 ylo, yhi;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 c = csr[pp * 16 + hf * 8 + e];
+          const uint32_t wl = x[pp][e >> 1], wh = x[pp + 2][e >> 1];
+          const float lo = (e & 1) ? bf16hi(wl) : bf16lo(wl);
+          const float hi = (e & 1) ? bf16hi(wh) : bf16lo(wh);
+          ylo[e] = f32_to_bf16(fmaf(lo, c.x, -(hi * c.y)));
+          yhi[e] = f32_to_bf16(fmaf(hi, c.x, lo * c.y));
         }
-        *reinterpret_cast<u32x4*>(dst + j * VT_STRIDE) = o;
+        qf[8 + pp] = ylo;
+        qf[10 + pp] = yhi;
       }
     }
-    __syncthreads();
-    if (!head_ok || k0 > q0 + 31) continue;  // every key of the tile is after this wave's queries
 
-    // ---- Sᵀ = K·Qᵀ for two 32-key blocks
-    f32x16 s[2];
+    float m_run = -INFINITY;  // reference maximum of scaled scores (base 2)
+    float l_run = 0.f;        // this lane's share of the row sum
+    f32x16 acc[4] = {};       // Oᵀ: dims db*32 + (r/4)*8 + hf*4 + r%4, query ln
+
+    auto compute_tile = [&](const uint8_t* buf, int kt) {
+      const int k0 = kt * BK;
+      if (!head_ok || k0 > q0 + 31) return;  // every key after this wave's queries
+      f32x16 s[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      s[j] = f32x16{};
-      const int r = j * 32 + r_key;
-      const int sw = kswz(r);
-      const uint16_t* krow = sK + (g * BK + r) * kNope;
+      for (int j = 0; j < 2; ++j) {
+        s[j] = f32x16{};
+        const uint8_t* kr = buf + KOFF + k_lane + j * 32 * K_ROW;
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((kb * 2 + hf) ^ sw) * 8));
-        s[j] = mfma32x32x16(a, qf[kb], s[j]);
+        for (int kb = 0; kb < 8; ++kb)
+          s[j] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kr + kb * 32), qf[kb], s[j]);
+        const uint8_t* pr = buf + KPOFF + kp_lane + j * 32 * KP_ROW;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          s[j] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(pr + kb * 32), qf[8 + kb], s[j]);
       }
-      const uint16_t* prow = sKP + r * kRope;
+      if (k0 + BK - 1 > q0) {  // tile straddles this wave's diagonal
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(prow + (((kb * 2 + hf) ^ (sw & 7)) * 8));
-        s[j] = mfma32x32x16(a, qf[8 + kb], s[j]);
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + j * 32 + ((r >> 3) * 16) + hf * 8 + ((r >> 2) & 1) * 4 + (r & 3);
+            if (key > myq) s[j][r] = -INFINITY;
+          }
       }
-    }
-    // ---- causal mask where the tile straddles this wave's diagonal
-    if (k0 + BK - 1 > q0) {
+      float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      mx = max_halves(mx) * cl2;
+      const bool need = mx > m_run + TAU;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + j * 32 + ((r >> 2) >> 1) * 16 + hf * 8 + ((r >> 2) & 1) * 4 + (r & 3);
-          if (key > myq) s[j][r] = -INFINITY;
-        }
-    }
-    // ---- online softmax (base 2)
-    float mx = s[0][0];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
-    mx = max_halves(mx);
-    const float m_new = fmaxf(m_run, mx * cl2);
-    const float alpha = fast_exp2(m_run - m_new);
-    bf16x8 pf[4];
-    float ls = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pv = fast_exp2(fmaf(s[c >> 1][(c & 1) * 8 + e], cl2, -m_new));
-        const __bf16 pb = f32_to_bf16(pv);
-        pf[c][e] = pb;
-        ls += (float)pb;
+        for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+        m_run = m_new;
       }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db] *= alpha;
-    // ---- Oᵀ += Vᵀ·Pᵀ
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const uint16_t* vrow = sVt + (g * kV + db * 32 + ln) * VT_STRIDE + hf * 8;
+      bf16x8 pf[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + c * 16);
-        acc[db] = mfma32x32x16(a, pf[c], acc[db]);
-      }
-    }
-  }
-
-  if (!head_ok) return;
-  const float l_tot = sum_halves(l_run);
-  const float inv = 1.0f / l_tot;
-  if (myq < T) {
-    const size_t obase = ((size_t)b * T + myq) * ((size_t)H * kV) + (size_t)head * kV;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = db * 32 + gq * 8 + hf * 4;
-        const float o0 = acc[db][gq * 4 + 0] * inv, o1 = acc[db][gq * 4 + 1] * inv;
-        const float o2 = acc[db][gq * 4 + 2] * inv, o3 = acc[db][gq * 4 + 3] * inv;
-        if (p.out_f32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase + d0) = f32x4{o0, o1, o2, o3};
-        } else {
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + obase + d0) =
-              u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = fast_exp2(fmaf(s[c >> 1][(c & 1) * 8 + e], cl2, -m_run));
+          const float p1 = fast_exp2(fmaf(s[c >> 1][(c & 1) * 8 + e + 1], cl2, -m_run));
+          const uint32_t pk = pack_bf16x2(p0, p1);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                                  __builtin_bit_cast(bf16x2, ones), l_run, false);
+          const bf16x2 pb = __builtin_bit_cast(bf16x2, pk);
+          pf[c][e] = pb[0];
+          pf[c][e + 1] = pb[1];
         }
       }
-    if (p.lse && hf == 0)
-      p.lse[((size_t)b * H + head) * T + myq] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+      // Oᵀ += Vᵀ·Pᵀ
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint8_t* vr = buf + VOFF + v_lane[db];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const s16x4 lo = ds_read_tr(vr + c * 16 * V_ROW);
+          const s16x4 hi = ds_read_tr(vr + c * 16 * V_ROW + 4 * V_ROW);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = mfma32x32x16(a, pf[c], acc[db]);
+        }
+      }
+    };
+
+    const int kend = min(T, qt * BQ + BQ);
+    const int nkt = (kend + BK - 1) / BK;
+    issue_tile(lds_a, 0);
+    wait_vmem();
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt += 2) {
+      if (kt + 1 < nkt) issue_tile(lds_b, kt + 1);
+      compute_tile(lds_a, kt);
+      wait_vmem();
+      __syncthreads();
+      if (kt + 1 >= nkt) break;
+      if (kt + 2 < nkt) issue_tile(lds_a, kt + 2);
+      compute_tile(lds_b, kt + 1);
+      wait_vmem();
+      __syncthreads();
+    }
+
+    // ---- epilogue
+    if (head_ok) {
+      const float l_tot = sum_halves(l_run);
+      const float inv = 1.0f / l_tot;
+      if (myq < T) {
+        const size_t obase = ((size_t)b * T + myq) * ((size_t)H * kV) + (size_t)head * kV;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int d0 = db * 32 + gq * 8 + hf * 4;
+            const float o0 = acc[db][gq * 4 + 0] * inv, o1 = acc[db][gq * 4 + 1] * inv;
+            const float o2 = acc[db][gq * 4 + 2] * inv, o3 = acc[db][gq * 4 + 3] * inv;
+            if (p.out_f32) {
+              *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase + d0) = f32x4{o0, o1, o2, o3};
+            } else {
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + obase + d0) =
+                  u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+            }
+          }
+        if (p.lse && hf == 0)
+          p.lse[((size_t)b * H + head) * T + myq] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+      }
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-  constexpr int G = 2, WPH = 2;
-  using C = Cfg<G, WPH>;
   const int HG = (p.H + G - 1) / G;
-  const int NQ = (p.T + C::BQ - 1) / C::BQ;
-  const long blocks = (long)NQ * p.B * HG;
+  const int NQ = (p.T + BQ - 1) / BQ;
+  const int NP = (NQ + 1) / 2;
+  const long blocks = (long)p.B * HG * NP;
   if (blocks <= 0 || blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<G, WPH>), dim3((unsigned)blocks), dim3(C::NT), 0, stream, p);
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 
