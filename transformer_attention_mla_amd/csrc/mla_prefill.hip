@@ -15,10 +15,12 @@
 //     amount of causal work.  Workgroups of the same (sequence, head pair) are
 //     placed on the same XCD and issued together, so that XCD's L2 serves
 //     their shared key/value stream.
-//   * Per key tile (64 keys) the workgroup stages k_nope of both heads, the
-//     rotated shared rotary key (once for both heads) and V of both heads in
-//     LDS, with asynchronous buffer→LDS copies into a second buffer while the
-//     current tile is multiplied.
+//   * Key tiles are 32 keys.  A tile (k_nope of both heads, the rotated shared
+//     rotary key -- staged once for both heads -- and V of both heads) lives in
+//     one of four LDS stages.  Asynchronous buffer→LDS copies run three tiles
+//     ahead of the tile being multiplied; the workgroup barrier between tiles
+//     waits only for the next tile's copies (explicit, in-order vmcnt counts),
+//     never for the ones still in flight behind it.
 //
 // Per wave and key tile
 //   * Sᵀ = K·Qᵀ with v_mfma_f32_32x32x16_bf16: the key tile is the A operand
@@ -48,26 +50,30 @@ constexpr int WPH = 4;        // waves per head
 constexpr int NW = G * WPH;   // 8 waves
 constexpr int NT = 64 * NW;   // 512 threads
 constexpr int BQ = 32 * WPH;  // 128 queries per head per tile
-constexpr int BK = 64;        // keys per tile
+constexpr int BK = 32;        // keys per tile
+constexpr int NSTAGE = 4;     // LDS stages; copies run NSTAGE-1 tiles ahead
 constexpr float TAU = 8.0f;   // lazy-rescale threshold (log2 units)
 
-// LDS stage layout (bytes)
+// LDS stage layout (bytes): k_nope head 0 | head 1 | rotated key | V head 0 | head 1.
 constexpr int K_ROW = 272;                  // 256 B of k_nope + 16 B pad (17 slots)
-constexpr int K_HEAD = BK * K_ROW;          // 17408
-constexpr int KP_ROW = 144;                 // 128 B of rotated key + 16 B pad (9 slots)
+constexpr int K_HEAD = BK * K_ROW;          // 8704
+constexpr int KPOFF = G * K_HEAD;           // 17408
+constexpr int KP_ROW = 128;                 // rotated key, 16 B chunks XOR-swizzled
+constexpr int VOFF = KPOFF + BK * KP_ROW;   // 21504
 constexpr int V_ROW = 256;                  // natural layout, 64 B blocks XOR-swizzled
-constexpr int V_HEAD = BK * V_ROW;          // 16384
-constexpr int KOFF = 0;
-constexpr int KPOFF = KOFF + G * K_HEAD;    // 34816
-constexpr int VOFF = KPOFF + BK * KP_ROW;   // 44032
-constexpr int STAGE = VOFF + G * V_HEAD;    // 76800
+constexpr int V_HEAD = BK * V_ROW;          // 8192
+constexpr int STAGE = VOFF + G * V_HEAD;    // 37888
 
-// DMA work per stage, in 1 KiB chunks (one wave-instruction of 64 x 16 B each).
-constexpr int DK = (BK * 17) / 64;           // 17 per head
-constexpr int DKP = (BK * 9) / 64;           // 9
-constexpr int DV = (BK * 16) / 64;           // 16 per head
-
-static_assert(BK * 17 % 64 == 0 && BK * 9 % 64 == 0, "slot counts must fill whole wave loads");
+// Copies per tile in 1 KiB chunks (one wave-instruction of 64 x 16 B each):
+// chunks [0, 17) k_nope, [17, 21) rotated key, [21, 37) V.  Every wave issues
+// the same number of copies (the spare ones repeat a chunk another wave also
+// copies, writing identical bytes), so one vmcnt count fits all waves.
+constexpr int NCHUNK = STAGE / 1024;           // 37
+constexpr int CK = KPOFF / 1024;               // 17
+constexpr int CKP = VOFF / 1024;               // 21
+constexpr int DPW = (NCHUNK + NW - 1) / NW;    // 5 copies per wave per tile
+static_assert(STAGE % 1024 == 0 && KPOFF % 1024 == 0 && VOFF % 1024 == 0, "chunk layout");
+static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS budget");
 
 // Tile-local key held in LDS row R of a 32-key block: the key that A-operand
 // lane R fetches.  Accumulator register r of lane (n, h) is row
@@ -79,25 +85,57 @@ __device__ __forceinline__ int akey(int R) {
   return (g4 >> 1) * 16 + h * 8 + (g4 & 1) * 4 + i;
 }
 
-__shared__ __attribute__((aligned(16))) uint8_t lds_a[STAGE];
-__shared__ __attribute__((aligned(16))) uint8_t lds_b[STAGE];
+// XOR swizzle of the 16 B chunks of a 128 B rotated-key row: distinct for any
+// 8 consecutive rows and for same-parity rows among 16 consecutive ones.
+__device__ __forceinline__ int kpswz(int R) { return (R ^ (R >> 3)) & 7; }
+
+__shared__ __attribute__((aligned(16))) uint8_t lds_s0[STAGE];
+__shared__ __attribute__((aligned(16))) uint8_t lds_s1[STAGE];
+__shared__ __attribute__((aligned(16))) uint8_t lds_s2[STAGE];
+__shared__ __attribute__((aligned(16))) uint8_t lds_s3[STAGE];
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// One wave-instruction copying 64 x 16 B from a buffer into LDS at
+// lds_wave_base + 16 * lane.  Written as inline assembly so that the compiler
+// does not treat it as a store that may alias every later LDS read (it would
+// then wait for all outstanding copies before each read); completion is
+// ordered explicitly with vmcnt waits before the barriers instead.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wave_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 16, (int)voff, 0, 0, 0);
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory", "m0");
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// s_waitcnt vmcnt(n) (lgkmcnt and expcnt untouched); n is a compile-time constant.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the implicit full memory fence of __syncthreads:
+// LDS reads of this wave are complete (lgkmcnt(0)); outstanding copies are
+// accounted for explicitly by the caller.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ s16x4 ds_read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
+
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const int tid = threadIdx.x;
@@ -133,78 +171,84 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const int head = hg * G + g;
   const bool head_ok = head < H;
 
-  // ---- asynchronous tile copies.  The stage buffer is a sequence of 1 KiB
-  // chunks (k_nope head 0 | head 1 | rotated key | V head 0 | head 1); wave w
-  // copies chunks w, w+8, ... of each region.  Every lane's byte offset inside
-  // its sequence's tensor is fixed up to the tile start, added per tile.  One
-  // buffer descriptor per tensor and sequence: rows past the end of the tensor
-  // read as zero; rows past T inside it belong to the next head and are masked.
-  constexpr int NCK = G * DK, NCKP = DKP, NCV = G * DV;  // 34, 9, 32 chunks
-  constexpr int IK = (NCK + NW - 1) / NW, IKP = (NCKP + NW - 1) / NW, IV = (NCV + NW - 1) / NW;
-  uint32_t voffK[IK], voffKP[IKP], voffV[IV];
+  // ---- asynchronous tile copies.  Copy i of wave w moves chunk
+  // j = (w + 8 i) (a spare copy repeats chunk j - 8).  Lane offsets inside the
+  // sequence's tensor are fixed; the buffer descriptor's base advances with the
+  // tile.  One descriptor per tensor and sequence: rows past the end of the
+  // tensor read as zero; rows past T inside it belong to the next head and are
+  // masked.
+  uint32_t voff[DPW];
+  int kind[DPW];  // 0 k_nope, 1 rotated key, 2 V (wave-uniform)
 #pragma unroll
-  for (int i = 0; i < IK; ++i) {
-    const int j = wave + NW * i;
-    const int gg = j / DK;
-    const int hh = min(hg * G + gg, H - 1);
-    const int s = (j % DK) * 64 + lane;
-    const int R = s / 17;
-    int c = s % 17;
-    if (c == 16) c = 15;  // pad slot: harmless duplicate
-    voffK[i] = ((uint32_t)hh * (uint32_t)T + (uint32_t)((R >> 5) * 32 + akey(R & 31))) * 256u + c * 16;
+  for (int i = 0; i < DPW; ++i) {
+    int j = wave + NW * i;
+    if (j >= NCHUNK) j -= NW;
+    uint32_t v;
+    if (j < CK) {
+      const int s = j * 64 + lane;  // slot in the k_nope region (17 per row)
+      const int gg = s / (BK * 17);
+      const int s2 = s % (BK * 17);
+      const int R = s2 / 17;
+      int c = s2 % 17;
+      if (c == 16) c = 15;  // pad slot: harmless duplicate
+      const int hh = min(hg * G + gg, H - 1);
+      v = ((uint32_t)hh * (uint32_t)T + (uint32_t)akey(R)) * 256u + c * 16;
+      kind[i] = 0;
+    } else if (j < CKP) {
+      const int s = (j - CK) * 64 + lane;  // slot in the rotated-key region (8 per row)
+      const int R = s / 8;
+      const int c = (s % 8) ^ kpswz(R);
+      v = (uint32_t)(akey(R) * 128 + c * 16);
+      kind[i] = 1;
+    } else {
+      const int s = (j - CKP) * 64 + lane;  // slot in the V region (16 per row)
+      const int gg = s / (BK * 16);
+      const int row = (s % (BK * 16)) / 16;
+      const int c = (s % 16) ^ ((row & 3) << 2);
+      const int hh = min(hg * G + gg, H - 1);
+      v = ((uint32_t)hh * (uint32_t)T + (uint32_t)row) * 256u + c * 16;
+      kind[i] = 2;
+    }
+    voff[i] = v;
   }
-#pragma unroll
-  for (int i = 0; i < IKP; ++i) {
-    const int s = (wave + NW * i) * 64 + lane;
-    const int R = s / 9;
-    int c = s % 9;
-    if (c == 8) c = 7;
-    voffKP[i] = (uint32_t)(((R >> 5) * 32 + akey(R & 31)) * 128 + c * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < IV; ++i) {
-    const int j = wave + NW * i;
-    const int gg = j / DV;
-    const int hh = min(hg * G + gg, H - 1);
-    const int s = (j % DV) * 64 + lane;
-    const int row = s / 16;
-    const int c = (s % 16) ^ ((row & 3) << 2);
-    voffV[i] = ((uint32_t)hh * (uint32_t)T + (uint32_t)row) * 256u + c * 16;
-  }
+  const uint16_t* kseq = p.k_nope + (size_t)b * H * T * kNope;
+  const uint16_t* vseq = p.v + (size_t)b * H * T * kV;
+  const uint16_t* pseq = p.kpe_rot + (size_t)b * T * kRope;
   const uint32_t seq_bytes = (uint32_t)((size_t)H * T * 256);
-  const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.k_nope + (size_t)b * H * T * kNope, seq_bytes);
-  const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.v + (size_t)b * H * T * kV, seq_bytes);
-  const __amdgpu_buffer_rsrc_t rKP = make_rsrc(p.kpe_rot + (size_t)b * T * kRope, (uint32_t)T * 128u);
 
-  auto issue_tile = [&](uint8_t* buf, int kt) {
+  auto issue = [&](uint8_t* buf, int kt) {
     const uint32_t k0 = (uint32_t)(kt * BK);
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kseq + (size_t)k0 * kNope, seq_bytes - k0 * 256u);
+    const __amdgpu_buffer_rsrc_t rP = make_rsrc(pseq + (size_t)k0 * kRope, (uint32_t)(T - (int)k0) * 128u);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vseq + (size_t)k0 * kV, seq_bytes - k0 * 256u);
 #pragma unroll
-    for (int i = 0; i < IK; ++i) {
-      const int j = wave + NW * i;
-      if (j < NCK) dma16(rK, buf + KOFF + j * 1024, voffK[i] + k0 * 256u);
-    }
-#pragma unroll
-    for (int i = 0; i < IKP; ++i) {
-      const int j = wave + NW * i;
-      if (j < NCKP) dma16(rKP, buf + KPOFF + j * 1024, voffKP[i] + k0 * 128u);
-    }
-#pragma unroll
-    for (int i = 0; i < IV; ++i) {
-      const int j = wave + NW * i;
-      if (j < NCV) dma16(rV, buf + VOFF + j * 1024, voffV[i] + k0 * 256u);
+    for (int i = 0; i < DPW; ++i) {
+      int j = wave + NW * i;
+      if (j >= NCHUNK) j -= NW;
+      uint8_t* dst = buf + j * 1024;
+      if (kind[i] == 0)
+        dma16(rK, dst, voff[i]);
+      else if (kind[i] == 1)
+        dma16(rP, dst, voff[i]);
+      else
+        dma16(rV, dst, voff[i]);
     }
   };
 
-  // Zero both stages once, so rows that a copy leaves unwritten hold finite values.
+  // Zero the stages once, so rows that a copy leaves unwritten hold finite values.
   for (int o = tid * 16; o < STAGE; o += NT * 16) {
-    *reinterpret_cast<u32x4*>(lds_a + o) = u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(lds_b + o) = u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(lds_s0 + o) = u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(lds_s1 + o) = u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(lds_s2 + o) = u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(lds_s3 + o) = u32x4{0, 0, 0, 0};
   }
   __syncthreads();
 
   // Per-lane LDS addresses for the products.
-  const int k_lane = g * K_HEAD + ln * K_ROW + hf * 16;         // + j*32*K_ROW + kb*32
-  const int kp_lane = ln * KP_ROW + hf * 16;                     // + j*32*KP_ROW + kb*32
+  const int k_lane = g * K_HEAD + ln * K_ROW + hf * 16;  // + kb*32
+  int kp_lane[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) kp_lane[kb] = KPOFF + ln * KP_ROW + (((kb * 2 + hf) ^ kpswz(ln)) * 16);
   const int q16 = lane >> 4, s16 = lane & 15;
   // ds_read_b64_tr_b16: lane s of a 16-lane group addresses key row
   // (q16/2)*8 + t*4 + s/4 of a 16-key chunk, dims (q16%2)*16 + (s%4)*4 .. +3 of a
@@ -214,7 +258,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   int v_lane[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
-    v_lane[db] = g * V_HEAD + v_row * V_ROW +
+    v_lane[db] = VOFF + g * V_HEAD + v_row * V_ROW +
                  (((db ^ (s16 >> 2)) * 4 + (q16 & 1) * 2 + ((s16 & 3) >> 1)) * 16) + (s16 & 1) * 8;
 
   const float cl2 = p.scale_log2;
@@ -228,6 +272,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     const int myq = q0 + ln;
     const int myqc = myq < T ? myq : T - 1;
     const int headc = head_ok ? head : H - 1;
+    const int kend = min(T, qt * BQ + BQ);
+    const int nkt = (kend + BK - 1) / BK;
 
     // ---- query fragments (B operand), rotary part rotated in registers
     bf16x8 qf[12];
@@ -258,41 +304,42 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
       }
     }
 
+    // ---- first copies of the pass, issued after the query loads so that
+    // waiting for those does not wait for the copies (the previous pass ended
+    // with all waves past their last LDS read and no copy outstanding)
+    issue(lds_s0, 0);
+    if (nkt > 1) issue(lds_s1, 1);
+    if (nkt > 2) issue(lds_s2, 2);
+
     float m_run = -INFINITY;  // reference maximum of scaled scores (base 2)
     float l_run = 0.f;        // this lane's share of the row sum
     f32x16 acc[4] = {};       // Oᵀ: dims db*32 + (r/4)*8 + hf*4 + r%4, query ln
 
-    auto compute_tile = [&](const uint8_t* buf, int kt) {
+    // Scores, softmax and PV of key tile kt held in stage `buf`.
+    auto compute = [&](const uint8_t* buf, int kt) {
       const int k0 = kt * BK;
       if (!head_ok || k0 > q0 + 31) return;  // every key after this wave's queries
-      f32x16 s[2];
+      f32x16 s = {};
+      const uint8_t* kr = buf + k_lane;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        s[j] = f32x16{};
-        const uint8_t* kr = buf + KOFF + k_lane + j * 32 * K_ROW;
+      for (int kb = 0; kb < 8; ++kb)
+        s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kr + kb * 32), qf[kb], s);
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-          s[j] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kr + kb * 32), qf[kb], s[j]);
-        const uint8_t* pr = buf + KPOFF + kp_lane + j * 32 * KP_ROW;
+      for (int kb = 0; kb < 4; ++kb)
+        s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(buf + kp_lane[kb]), qf[8 + kb], s);
+      if (k0 + BK - 1 > q0) {  // the tile on this wave's diagonal
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          s[j] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(pr + kb * 32), qf[8 + kb], s[j]);
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + ((r >> 3) * 16) + hf * 8 + ((r >> 2) & 1) * 4 + (r & 3);
+          if (key > myq) s[r] = -INFINITY;
+        }
       }
-      if (k0 + BK - 1 > q0) {  // tile straddles this wave's diagonal
+      float mx = max3(s[0], s[1], s[2]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + j * 32 + ((r >> 3) * 16) + hf * 8 + ((r >> 2) & 1) * 4 + (r & 3);
-            if (key > myq) s[j][r] = -INFINITY;
-          }
-      }
-      float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      for (int r = 3; r < 15; r += 2) mx = max3(mx, s[r], s[r + 1]);
+      mx = fmaxf(mx, s[15]);
       mx = max_halves(mx) * cl2;
-      const bool need = mx > m_run + TAU;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2(m_run - m_new);
         l_run *= alpha;
@@ -300,27 +347,27 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
         for (int db = 0; db < 4; ++db) acc[db] *= alpha;
         m_run = m_new;
       }
-      bf16x8 pf[4];
+      bf16x8 pf[2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < 2; ++c) {
+        u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = fast_exp2(fmaf(s[c >> 1][(c & 1) * 8 + e], cl2, -m_run));
-          const float p1 = fast_exp2(fmaf(s[c >> 1][(c & 1) * 8 + e + 1], cl2, -m_run));
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(fmaf(s[c * 8 + 2 * e], cl2, -m_run));
+          const float p1 = fast_exp2(fmaf(s[c * 8 + 2 * e + 1], cl2, -m_run));
+          // (a scalar: __builtin_bit_cast of a vector element reads element 0)
           const uint32_t pk = pack_bf16x2(p0, p1);
+          w[e] = pk;
           l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
                                                   __builtin_bit_cast(bf16x2, ones), l_run, false);
-          const bf16x2 pb = __builtin_bit_cast(bf16x2, pk);
-          pf[c][e] = pb[0];
-          pf[c][e + 1] = pb[1];
         }
+        pf[c] = as_bf16x8(w);
       }
-      // Oᵀ += Vᵀ·Pᵀ
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint8_t* vr = buf + VOFF + v_lane[db];
+        const uint8_t* vr = buf + v_lane[db];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < 2; ++c) {
           const s16x4 lo = ds_read_tr(vr + c * 16 * V_ROW);
           const s16x4 hi = ds_read_tr(vr + c * 16 * V_ROW + 4 * V_ROW);
           const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -329,22 +376,37 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
       }
     };
 
-    const int kend = min(T, qt * BQ + BQ);
-    const int nkt = (kend + BK - 1) / BK;
-    issue_tile(lds_a, 0);
-    wait_vmem();
-    __syncthreads();
-    for (int kt = 0; kt < nkt; kt += 2) {
-      if (kt + 1 < nkt) issue_tile(lds_b, kt + 1);
-      compute_tile(lds_a, kt);
-      wait_vmem();
-      __syncthreads();
+    // Wait until this wave's copies of tile kt are done (copies of tiles
+    // kt+1 and kt+2, when issued, may still be in flight), then barrier: after
+    // it every wave's copies of tile kt have landed and every wave has left
+    // the stage that the next copy overwrites.
+    auto wait_tile = [&](int kt) {
+      if (kt + 2 < nkt)
+        wait_vm<2 * DPW>();
+      else if (kt + 1 < nkt)
+        wait_vm<DPW>();
+      else
+        wait_vm<0>();
+      barrier_lds();
+    };
+
+    wait_tile(0);
+    // iteration kt: copy tile kt+3 into the stage tile kt-1 used, multiply tile kt
+    auto step = [&](uint8_t* cur, uint8_t* ahead, int kt) {
+      if (kt + 3 < nkt) issue(ahead, kt + 3);
+      compute(cur, kt);
+      if (kt + 1 < nkt) wait_tile(kt + 1);
+    };
+    for (int kt = 0; kt < nkt; kt += 4) {
+      step(lds_s0, lds_s3, kt);
       if (kt + 1 >= nkt) break;
-      if (kt + 2 < nkt) issue_tile(lds_a, kt + 2);
-      compute_tile(lds_b, kt + 1);
-      wait_vmem();
-      __syncthreads();
+      step(lds_s1, lds_s0, kt + 1);
+      if (kt + 2 >= nkt) break;
+      step(lds_s2, lds_s1, kt + 2);
+      if (kt + 3 >= nkt) break;
+      step(lds_s3, lds_s2, kt + 3);
     }
+    barrier_lds();  // every wave is done with the stages before the next pass refills them
 
     // ---- epilogue
     if (head_ok) {
