@@ -27,6 +27,29 @@ sys.path.insert(0, REPO)
 PEAK_BF16_TFLOPS = 2516.6   # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBPS = 8000.0      # HBM3E
 METRIC = "MLA prefill TFLOP/s (causal) + % bf16 MFMA peak; decode HBM GB/s, 1 GPU"
+CSRC = os.path.join(REPO, "transformer_attention_mla_amd", "csrc")
+
+# HBM bytes per launch at this file's workloads, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE) scaled by what the same counters read for a
+# copy of known size (FETCH_SIZE counts half the bytes read, WRITE_SIZE all the
+# bytes written).  Each figure holds only for the kernel source it was taken on,
+# identified by a hash of its files; after any change the figure is dropped.
+MEASURED_TRAFFIC = {
+    "prefill_kernel": ("5aa48862ec460e1d", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
+                       2038202785, "profiles/prefill_kernel_B4_T4096_H64.txt"),
+    "decode_split_kernel": ("11010db7dc8c5d63", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                            21477496360, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
+}
+
+
+def measured_traffic(kernel):
+    import hashlib
+    digest, files, nbytes, _ = MEASURED_TRAFFIC[kernel]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return nbytes if h.hexdigest()[:16] == digest else None
 
 
 def prefill_flops(B, H, T):
@@ -201,7 +224,8 @@ def main():
             "attention_plus_oproj_tflops": (fa + fo) / (ta + to) / 1e12}
         res["roofline"] = {"bound": "mfma", "achieved": fa / ta / 1e12, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": fa / ta / 1e12 / PEAK_BF16_TFLOPS,
-                           "traffic": None, "kernel": "prefill_kernel (+ rope_prep_kernel)",
+                           "traffic": measured_traffic("prefill_kernel"),
+                           "kernel": "prefill_kernel (+ rope_prep_kernel)",
                            "per_launch": f"{fa:.4e} causal flops"}
         parts.append(f"prefill B={B} T={T} H={H} causal + o_proj [{B * T}x{K_O}]x[{K_O}x{N_O}]")
         cfg.update({"prefill_batch": B, "prefill_seq_len": T})
@@ -217,7 +241,9 @@ def main():
             "oproj_ms": avg["decode_oproj"], "oproj_gbps": bo / tod / 1e9}
         res["roofline_decode"] = {"bound": "hbm", "achieved": bd / td / 1e9, "peak": PEAK_HBM_GBPS,
                                   "unit": "GB/s", "frac": bd / td / 1e9 / PEAK_HBM_GBPS,
-                                  "traffic": None, "kernel": "decode_split_kernel",
+                                  "traffic": (measured_traffic("decode_split_kernel")
+                                              if args.decode_splits == 0 else None),
+                                  "kernel": "decode_split_kernel",
                                   "per_launch": f"{bd} bytes"}
         parts.append(f"decode B={Bd} L={L} H={Hd} q_pos={q_pos} + o_proj [{Bd}x{K_O}]x[{K_O}x{N_O}]")
         cfg.update({"decode_batch": Bd, "decode_kv_len": L})

@@ -319,14 +319,16 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     auto compute = [&](const uint8_t* buf, int kt) {
       const int k0 = kt * BK;
       if (!head_ok || k0 > q0 + 31) return;  // every key after this wave's queries
-      f32x16 s = {};
+      bf16x8 kf[12];
       const uint8_t* kr = buf + k_lane;
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-        s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kr + kb * 32), qf[kb], s);
+      for (int kb = 0; kb < 8; ++kb) kf[kb] = *reinterpret_cast<const bf16x8*>(kr + kb * 32);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(buf + kp_lane[kb]), qf[8 + kb], s);
+      for (int kb = 0; kb < 4; ++kb) kf[8 + kb] = *reinterpret_cast<const bf16x8*>(buf + kp_lane[kb]);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 s = {};
+#pragma unroll
+      for (int kb = 0; kb < 12; ++kb) s = mfma32x32x16(kf[kb], qf[kb], s);
       if (k0 + BK - 1 > q0) {  // the tile on this wave's diagonal
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -363,6 +365,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
         }
         pf[c] = as_bf16x8(w);
       }
+      bf16x8 vf[4][2];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const uint8_t* vr = buf + v_lane[db];
@@ -370,10 +373,14 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
         for (int c = 0; c < 2; ++c) {
           const s16x4 lo = ds_read_tr(vr + c * 16 * V_ROW);
           const s16x4 hi = ds_read_tr(vr + c * 16 * V_ROW + 4 * V_ROW);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[db] = mfma32x32x16(a, pf[c], acc[db]);
+          vf[db][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db] = mfma32x32x16(vf[db][c], pf[c], acc[db]);
     };
 
     // Wait until this wave's copies of tile kt are done (copies of tiles
