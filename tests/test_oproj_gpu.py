@@ -20,8 +20,12 @@ def xw(M, K, N, seed):
     return x, w
 
 
+# The last three shapes take the wide-tile kernel (>= 256 tiles of 256 x 256):
+# ragged last m-group and n-tile, a tile count that is not a multiple of the 8
+# XCDs, N not a multiple of 4 (element stores), and an exact 256-multiple.
 @pytest.mark.parametrize("M,K,N", [(1, 128, 1), (17, 256, 100), (130, 1024, 300), (64, 8192, 7168),
-                                   (200, 512, 7168), (5, 8192, 33), (300, 128, 129)])
+                                   (200, 512, 7168), (5, 8192, 33), (300, 128, 129),
+                                   (4764, 128, 3803), (4100, 256, 4000), (8192, 512, 2048)])
 def test_oproj_parity(M, K, N, gpu_device):
     say(f"o_proj parity M={M} K={K} N={N}")
     x, w = xw(M, K, N, 10 + M)
@@ -60,6 +64,18 @@ def test_oproj_selection_weight_exact(gpu_device):
     y = mla.mla_out_proj(x.to(gpu_device), w.to(gpu_device))
     torch.cuda.synchronize()
     assert torch.equal(y.cpu(), x[:, :N])
+
+
+def test_oproj_wide_selection_weight_exact(gpu_device):
+    """Wide-tile kernel: with W = I every output is one input element times 1,
+    so y must equal x bit for bit (every tile of the grouped order written)."""
+    M, K, N = 4352, 4096, 4096
+    say(f"o_proj wide selection M={M} K={K} N={N}")
+    x = inputs.normal_bf16((M, K), 6, device=gpu_device)
+    w = torch.eye(N, K, dtype=torch.bfloat16, device=gpu_device)
+    y = mla.mla_out_proj(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y, x[:, :N])
 
 
 def test_attention_then_oproj_workload1(gpu_device):

@@ -253,6 +253,7 @@ int mla_out_proj(const mla_bf16* x, const mla_bf16* w_o, void* y, int M, int K, 
   p.N = N;
   p.splits = splits;
   p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
+  p.group_m = 0;  // kernel default
   (void)hipGetLastError();
   if (mla::launch_oproj(p, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_LAUNCH;
   return MLA_OK;

@@ -72,4 +72,43 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ------------------------------------------------------------------------
+// Asynchronous buffer -> LDS copies (gfx950).
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One wave-instruction copying 64 x 16 B from a buffer into LDS at
+// lds_wave_base + 16 * lane.  Written as inline assembly so that the compiler
+// does not treat it as a store that may alias every later LDS read (it would
+// then wait for all outstanding copies before each read); completion is
+// ordered explicitly with vmcnt waits before the barriers instead.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wave_base, uint32_t voff) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt vmcnt(n) (lgkmcnt and expcnt untouched); n is a compile-time constant.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the implicit full memory fence of __syncthreads:
+// LDS reads of this wave are complete (lgkmcnt(0)); outstanding copies are
+// accounted for explicitly by the caller.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
 }  // namespace mla

@@ -87,6 +87,7 @@ struct OprojParams {
   int M, K, N;
   int splits;
   int out_f32;
+  int group_m;        // wide kernel: m-tiles per group of the tile order
 };
 
 int oproj_choose_splits(int M, int K, int N);

@@ -16,6 +16,15 @@
 // current slab is multiplied.  For small M the K range is split over
 // workgroups (float32 partials in the caller's workspace, then a reduction
 // kernel) so the weight stream is spread over every compute unit.
+//
+// Large M (enough 256 x 256 tiles to fill the chip) takes a second kernel:
+// 256 (n) × 256 (m) tiles per workgroup of 8 waves, k staged 64 at a time in
+// two LDS stages filled by asynchronous buffer→LDS copies (details at the
+// kernel).  Tiles are handed to
+// the XCDs (workgroup ids are dealt round-robin over the 8 XCDs) as
+// contiguous runs of a grouped order — a few m-tiles against every n-tile —
+// so the workgroups resident on one XCD share x rows and weight rows through
+// that XCD's L2, and all XCDs sweep the weight in step.
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -161,6 +170,185 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
   }
 }
 
+// ---------------------------------------------------------------- wide tiles --
+// 256 (n) × 256 (m) tiles per workgroup of 8 waves (two per SIMD; wave w
+// computes n rows 128(w%2).. and m rows 64(w/2).. of the tile).  k is staged
+// 64 at a time: 128-byte LDS rows, so every 8 lanes of a copy fetch one whole
+// 128-byte line, in two LDS stages of 64 KiB.  Each slab is multiplied in two
+// 32-k halves so the fragment reads of one half overlap the MFMAs of the
+// other; the copy of slab kt+2 is issued as soon as every wave has read slab
+// kt.  The buffer→LDS copy rate per CU, not the MFMA rate, bounds this kernel
+// (a copy-only run of it takes about 80% of its time).
+constexpr int WBN = 256;  // w rows (n) per tile
+constexpr int WBM = 256;  // x rows (m) per tile
+constexpr int WBK = 64;   // k per slab
+constexpr int WNW = 8;    // waves: 2 along n × 4 along m
+constexpr int WNT = 64 * WNW;
+constexpr int WTN = WBN / 2 / 32;          // 32-row w blocks per wave (4)
+constexpr int WTM = WBM / (WNW / 2) / 32;  // 32-row x blocks per wave (2)
+constexpr int WGROUP_M = 4;                // m-tiles per group of the tile order
+constexpr int WPART = WBN * WBK * 2;       // 32 KiB: one operand's slab
+constexpr int WSTAGE_B = 2 * WPART;        // 64 KiB per stage
+constexpr int WCPW = WSTAGE_B / 1024 / WNW;  // copies (1 KiB = 8 rows) per wave per slab
+static_assert(WBN == WBM, "one copy plan for both operands");
+static_assert(2 * WSTAGE_B <= 160 * 1024, "LDS budget");
+
+// Slot of 16-byte chunk c (of 8) in 128-byte row r: c ^ wswz(r).  Any 8
+// consecutive rows read at one chunk hit 8 distinct slots mod 128 B, any 16
+// (from a multiple of 16) 16 distinct slots mod 256 B; depends on r mod 32 only.
+__device__ __forceinline__ int wswz(int row) { return (row & 7) ^ ((row >> 3) & 3); }
+
+__shared__ __attribute__((aligned(1024))) uint8_t wlds[2 * WSTAGE_B];
+
+__global__ __launch_bounds__(WNT) void oproj_wide_kernel(OprojParams p) {
+  const int M = p.M, N = p.N, K = p.K;
+  const int tiles_n = (N + WBN - 1) / WBN;
+  const int tiles_m = (M + WBM - 1) / WBM;
+  const int ntiles = tiles_m * tiles_n;
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7, seq = b >> 3;
+  const int t = xcd * (ntiles >> 3) + min(xcd, ntiles & 7) + seq;
+  const int gm = p.group_m;
+  const int group = t / (gm * tiles_n);
+  const int first_m = group * gm;
+  const int rows_m = min(gm, tiles_m - first_m);
+  const int within = t - group * gm * tiles_n;
+  const int tm = first_m + within % rows_m;
+  const int tn = within / rows_m;
+  const int n0 = tn * WBN, m0 = tm * WBM;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, hf = lane >> 5;
+  const int wn = wave & 1, wm = wave >> 1;
+
+  // Copy plan: wave w copies 1 KiB chunks j = w + WNW i (8 rows each); chunks
+  // 0..31 are w rows, 32..63 x rows.  Lane l writes bytes 16l.. of its chunk:
+  // row 8(j%32) + l/8, slot l%8, which holds source chunk slot ^ wswz(row).
+  uint32_t voff[WCPW];
+#pragma unroll
+  for (int i = 0; i < WCPW; ++i) {
+    const int j = wave + WNW * i;
+    const int row = (j & 31) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ wswz(row);
+    voff[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)c * 16u;
+  }
+  const uint16_t* wbase = p.w + (size_t)n0 * K;
+  const uint16_t* xbase = p.x + (size_t)m0 * K;
+  const size_t wbytes = (size_t)(N - n0) * K * 2;
+  const size_t xbytes = (size_t)(M - m0) * K * 2;
+  const int nk = K / WBK;
+
+  auto issue = [&](int stage, int kt) {
+    const int k0 = kt * WBK;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + k0, (uint32_t)min(wbytes - (size_t)k0 * 2, (size_t)0x7fffffff));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase + k0, (uint32_t)min(xbytes - (size_t)k0 * 2, (size_t)0x7fffffff));
+    uint8_t* sb = wlds + stage * WSTAGE_B;
+#pragma unroll
+    for (int i = 0; i < WCPW; ++i)  // i < WCPW/2: w rows
+      dma16(i < WCPW / 2 ? rw : rx, sb + (wave + WNW * i) * 1024, voff[i]);
+  };
+
+  // Fragment of k16 step kk (0..3) for row ln of a 32-row block: chunk 2kk + hf.
+  const int swz = wswz(ln);
+  int foff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) foff[kk] = ln * 128 + ((2 * kk + hf) ^ swz) * 16;
+
+  struct Frags {
+    bf16x8 a[WTN][2], bx[WTM][2];
+  };
+  auto load_frags = [&](Frags& f, int stage, int half) {
+    const uint8_t* sw = wlds + stage * WSTAGE_B + wn * (WTN * 32) * 128;
+    const uint8_t* sx = wlds + stage * WSTAGE_B + WPART + wm * (WTM * 32) * 128;
+    const int o0 = half ? foff[2] : foff[0];
+    const int o1 = half ? foff[3] : foff[1];
+#pragma unroll
+    for (int i = 0; i < WTN; ++i) {
+      f.a[i][0] = *reinterpret_cast<const bf16x8*>(sw + i * 32 * 128 + o0);
+      f.a[i][1] = *reinterpret_cast<const bf16x8*>(sw + i * 32 * 128 + o1);
+    }
+#pragma unroll
+    for (int jm = 0; jm < WTM; ++jm) {
+      f.bx[jm][0] = *reinterpret_cast<const bf16x8*>(sx + jm * 32 * 128 + o0);
+      f.bx[jm][1] = *reinterpret_cast<const bf16x8*>(sx + jm * 32 * 128 + o1);
+    }
+  };
+  f32x16 acc[WTN][WTM] = {};
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < WTN; ++i)
+#pragma unroll
+        for (int jm = 0; jm < WTM; ++jm) acc[i][jm] = mfma32x32x16(f.a[i][kk], f.bx[jm][kk], acc[i][jm]);
+  };
+
+  issue(0, 0);
+  issue(1, 1);  // nk >= 2 (K % 128 == 0)
+  wait_vm<WCPW>();
+  barrier_lds();
+  Frags f0, f1;
+  load_frags(f0, 0, 0);
+  // Slab kt (stage kt & 1), first half's fragments in f0:
+  //   read the second half (f1), multiply the first;
+  //   wait for slab kt+1 (its copies are the only ones in flight), barrier:
+  //   slab kt+1 visible, and every wave has read all of slab kt;
+  //   refill slab kt's stage with slab kt+2; read slab kt+1's first half
+  //   (f0); multiply slab kt's second half.
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    load_frags(f1, st, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    if (kt + 1 < nk) {
+      wait_vm<0>();  // slab kt+1's copies are the only ones in flight
+      barrier_lds();
+      if (kt + 2 < nk) issue(st, kt + 2);
+      load_frags(f0, st ^ 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+  }
+
+#pragma unroll
+  for (int jm = 0; jm < WTM; ++jm) {
+    const int m = m0 + wm * (WTM * 32) + jm * 32 + ln;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < WTN; ++i)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int n = n0 + wn * (WTN * 32) + i * 32 + gq * 8 + hf * 4;
+        const float v0 = acc[i][jm][gq * 4 + 0], v1 = acc[i][jm][gq * 4 + 1];
+        const float v2 = acc[i][jm][gq * 4 + 2], v3 = acc[i][jm][gq * 4 + 3];
+        if (p.out_f32) {
+          float* dst = static_cast<float*>(p.y) + (size_t)m * N + n;
+          if (n + 3 < N && (N & 3) == 0) {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
+          } else {
+            if (n < N) dst[0] = v0;
+            if (n + 1 < N) dst[1] = v1;
+            if (n + 2 < N) dst[2] = v2;
+            if (n + 3 < N) dst[3] = v3;
+          }
+        } else {
+          __bf16* dst = static_cast<__bf16*>(p.y) + (size_t)m * N + n;
+          if (n + 3 < N && (N & 3) == 0) {
+            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          } else {
+            if (n < N) dst[0] = f32_to_bf16(v0);
+            if (n + 1 < N) dst[1] = f32_to_bf16(v1);
+            if (n + 2 < N) dst[2] = f32_to_bf16(v2);
+            if (n + 3 < N) dst[3] = f32_to_bf16(v3);
+          }
+        }
+      }
+  }
+}
+
 // y = sum over splits of the float32 partials, in split order.
 __global__ __launch_bounds__(256) void oproj_reduce_kernel(OprojParams p) {
   const size_t total = (size_t)p.M * p.N;
@@ -177,7 +365,15 @@ __global__ __launch_bounds__(256) void oproj_reduce_kernel(OprojParams p) {
 
 }  // namespace
 
+// The wide kernel needs enough 256 x 256 tiles to fill the chip, and 32-bit
+// buffer offsets for 256 rows of x or w.
+static bool oproj_use_wide(int M, int K, int N) {
+  const long wide_tiles = (long)((M + WBM - 1) / WBM) * ((N + WBN - 1) / WBN);
+  return wide_tiles >= 256 && (long long)K * 2 * WBM < 0x7fffffffLL;
+}
+
 int oproj_choose_splits(int M, int K, int N) {
+  if (oproj_use_wide(M, K, N)) return 1;
   const long tiles = (long)((M + OBM - 1) / OBM) * ((N + OBN - 1) / OBN);
   const int slabs = K / OBK;
   if (tiles >= 256 || slabs <= 1) return 1;
@@ -192,7 +388,15 @@ int oproj_choose_splits(int M, int K, int N) {
   return best;
 }
 
-hipError_t launch_oproj(const OprojParams& p, hipStream_t stream) {
+hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
+  OprojParams p = p_in;
+  if (p.splits == 1 && oproj_use_wide(p.M, p.K, p.N)) {
+    const long wide_tiles = (long)((p.M + WBM - 1) / WBM) * ((p.N + WBN - 1) / WBN);
+    if (wide_tiles > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if (p.group_m <= 0) p.group_m = WGROUP_M;
+    hipLaunchKernelGGL(oproj_wide_kernel, dim3((unsigned)wide_tiles), dim3(WNT), 0, stream, p);
+    return hipGetLastError();
+  }
   const long tiles = (long)((p.M + OBM - 1) / OBM) * ((p.N + OBN - 1) / OBN);
   if (tiles <= 0 || tiles > 0x7fffffffL || p.splits < 1 || p.splits > 65535)
     return hipErrorInvalidConfiguration;
