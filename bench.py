@@ -35,10 +35,10 @@ CSRC = os.path.join(REPO, "transformer_attention_mla_amd", "csrc")
 # bytes written).  Each figure holds only for the kernel source it was taken on,
 # identified by a hash of its files; after any change the figure is dropped.
 MEASURED_TRAFFIC = {
-    "prefill_kernel": ("3af7763fa4173228", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
-                       2066326474, "profiles/prefill_kernel_B4_T4096_H64.txt"),
-    "decode_split_kernel": ("d1c921952a613d47", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                            21477492862, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
+    "prefill_kernel": ("5ee551a3f4b0f187", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
+                       2072159276, "profiles/prefill_kernel_B4_T4096_H64.txt"),
+    "decode_split_kernel": ("20586ef06657d5ae", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                            21477496766, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
 }
 
 
@@ -70,35 +70,41 @@ def oproj_bytes(M, K, N):
 
 def cpu_baseline(d, B, H, T, R, scale, budget_s):
     """Time the oracle on a bounded sample of the prefill workload: every row
-    of sequence 0 for the first n heads, n chosen from a one-head
-    calibration so the sample takes about budget_s seconds."""
+    of the first n (sequence, head) units in sequence-major order, n chosen
+    from a one-unit calibration so the sample takes about budget_s seconds."""
     import numpy as np
     import oracle
     from transformer_attention_mla_amd import inputs
 
     threads = oracle.default_threads()
+    cache = {}
 
-    def head_inputs(n):
-        sl = lambda t: inputs.bits(t[0:1, 0:n])
-        return (sl(d["q_nope"]), sl(d["q_pe"]), sl(d["k_nope"]), inputs.bits(d["k_pe"][0:1]),
-                sl(d["v"]))
+    def seq_inputs(nb):
+        if nb not in cache:
+            sl = lambda t: inputs.bits(t[0:nb])
+            cache.clear()
+            cache[nb] = (sl(d["q_nope"]), sl(d["q_pe"]), sl(d["k_nope"]), sl(d["k_pe"]), sl(d["v"]))
+        return cache[nb]
 
     def run(n):
-        qn, qp, kn, kp, v = head_inputs(n)
-        rows = np.arange(T, dtype=np.int32)
-        sel = np.stack([np.zeros(n * T, np.int32), np.repeat(np.arange(n, dtype=np.int32), T),
-                        np.tile(rows, n)], 1)
+        nb = (n + H - 1) // H
+        qn, qp, kn, kp, v = seq_inputs(nb)
+        units = np.arange(n, dtype=np.int32)
+        sel = np.stack([np.repeat(units // H, T), np.repeat(units % H, T),
+                        np.tile(np.arange(T, dtype=np.int32), n)], 1).astype(np.int32)
         t0 = time.perf_counter()
         oracle.prefill_rows(qn, qp, kn, kp, v, R, scale, sel, nthreads=threads)
         return time.perf_counter() - t0
 
     t1 = run(1)
-    n = max(1, min(H, int(budget_s / max(t1, 1e-3))))
+    n = max(1, min(B * H, int(budget_s / max(t1, 1e-3))))
     tn = t1 if n == 1 else run(n)
     flops = prefill_flops(1, n, T)
+    last_b, last_h = (n - 1) // H, (n - 1) % H
     return {"value": flops / tn / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"prefill rows of sequence 0, heads 0..{n - 1} (all {T} rows each) of the "
-                      f"B={B} T={T} workload; {flops / 1e9:.1f} GFLOP in {tn:.2f} s, fp64",
+            "sample": f"every row of the first {n} (sequence, head) units (through sequence {last_b}, "
+                      f"head {last_h}) of the B={B} T={T} H={H} workload; {flops / 1e9:.1f} GFLOP in "
+                      f"{tn:.2f} s, fp64",
             "seconds": round(tn, 3)}
 
 

@@ -37,7 +37,7 @@ def oracle_full(d):
 
 
 SHAPES = [(1, 1, 1), (1, 3, 17), (2, 3, 63), (1, 2, 64), (1, 3, 65), (1, 2, 129), (3, 1, 100),
-          (1, 5, 200), (1, 64, 64), (2, 4, 1000)]
+          (1, 5, 200), (1, 64, 64), (2, 4, 1000), (1, 2, 96), (1, 3, 300)]
 
 
 @pytest.mark.parametrize("B,H,T", SHAPES)

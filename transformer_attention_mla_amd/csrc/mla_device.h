@@ -96,19 +96,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
+// The waitcnt and barrier builtins touch no memory as far as the compiler is
+// concerned, so it may move loads and stores across them; the empty asm
+// statements with a memory clobber pin every memory access of the wave to its
+// side of the wait (compiler ordering only: no instruction is emitted).
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
 // s_waitcnt vmcnt(n) (lgkmcnt and expcnt untouched); n is a compile-time constant.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  compiler_fence();
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  compiler_fence();
 }
 
 // Workgroup barrier without the implicit full memory fence of __syncthreads:
 // LDS reads of this wave are complete (lgkmcnt(0)); outstanding copies are
 // accounted for explicitly by the caller.
 __device__ __forceinline__ void barrier_lds() {
+  compiler_fence();
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
+  compiler_fence();
 }
 
 }  // namespace mla

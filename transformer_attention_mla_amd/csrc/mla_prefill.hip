@@ -20,7 +20,11 @@
 //     one of four LDS stages.  Asynchronous buffer→LDS copies run three tiles
 //     ahead of the tile being multiplied; the workgroup barrier between tiles
 //     waits only for the next tile's copies (explicit, in-order vmcnt counts),
-//     never for the ones still in flight behind it.
+//     never for the ones still in flight behind it.  A wave issuing copies
+//     stalls until the copy engine takes them, so the copies are issued by
+//     the four waves that finish each step first, at the end of the step,
+//     where they would otherwise idle at the barrier.  Past the last tile the
+//     copies are empty (zero-length descriptors), keeping the counts uniform.
 //
 // Per wave and key tile
 //   * Sᵀ = K·Qᵀ with v_mfma_f32_32x32x16_bf16: the key tile is the A operand
@@ -65,13 +69,16 @@ constexpr int V_HEAD = BK * V_ROW;          // 8192
 constexpr int STAGE = VOFF + G * V_HEAD;    // 37888
 
 // Copies per tile in 1 KiB chunks (one wave-instruction of 64 x 16 B each):
-// chunks [0, 17) k_nope, [17, 21) rotated key, [21, 37) V.  Every wave issues
-// the same number of copies (the spare ones repeat a chunk another wave also
-// copies, writing identical bytes), so one vmcnt count fits all waves.
+// chunks [0, 17) k_nope, [17, 21) rotated key, [21, 37) V.  Only the first
+// NCW waves copy (the SIMD gives them its matrix core first, so they reach
+// the end of a step early and issue the copies while the other waves still
+// compute); each issues the same number (the spare ones repeat a chunk another
+// wave also copies, writing identical bytes), so one vmcnt count fits all.
 constexpr int NCHUNK = STAGE / 1024;           // 37
 constexpr int CK = KPOFF / 1024;               // 17
 constexpr int CKP = VOFF / 1024;               // 21
-constexpr int DPW = (NCHUNK + NW - 1) / NW;    // 5 copies per wave per tile
+constexpr int NCW = 4;                         // waves that copy
+constexpr int DPW = (NCHUNK + NCW - 1) / NCW;  // 10 copies per copying wave per tile
 static_assert(STAGE % 1024 == 0 && KPOFF % 1024 == 0 && VOFF % 1024 == 0, "chunk layout");
 static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS budget");
 
@@ -135,8 +142,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const int head = hg * G + g;
   const bool head_ok = head < H;
 
-  // ---- asynchronous tile copies.  Copy i of wave w moves chunk
-  // j = (w + 8 i) (a spare copy repeats chunk j - 8).  Lane offsets inside the
+  // ---- asynchronous tile copies.  Copy i of copying wave w moves chunk
+  // j = (w + NCW i) (a spare copy repeats chunk j - NCW).  Lane offsets inside the
   // sequence's tensor are fixed; the buffer descriptor's base advances with the
   // tile.  One descriptor per tensor and sequence: rows past the end of the
   // tensor read as zero; rows past T inside it belong to the next head and are
@@ -145,8 +152,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   int kind[DPW];  // 0 k_nope, 1 rotated key, 2 V (wave-uniform)
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
-    int j = wave + NW * i;
-    if (j >= NCHUNK) j -= NW;
+    int j = (wave % NCW) + NCW * i;
+    if (j >= NCHUNK) j -= NCW;
     uint32_t v;
     if (j < CK) {
       const int s = j * 64 + lane;  // slot in the k_nope region (17 per row)
@@ -180,23 +187,39 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const uint16_t* pseq = p.kpe_rot + (size_t)b * T * kRope;
   const uint32_t seq_bytes = (uint32_t)((size_t)H * T * 256);
 
-  auto issue = [&](uint8_t* buf, int kt) {
-    const uint32_t k0 = (uint32_t)(kt * BK);
-    const __amdgpu_buffer_rsrc_t rK = make_rsrc(kseq + (size_t)k0 * kNope, seq_bytes - k0 * 256u);
-    const __amdgpu_buffer_rsrc_t rP = make_rsrc(pseq + (size_t)k0 * kRope, (uint32_t)(T - (int)k0) * 128u);
-    const __amdgpu_buffer_rsrc_t rV = make_rsrc(vseq + (size_t)k0 * kV, seq_bytes - k0 * 256u);
+  // Copies of one tile: descriptors whose base advances with the tile, and the
+  // stage they fill.  Past the last tile the descriptors are empty (nothing is
+  // read; the copies write zeros into a stage no later tile of the pass uses),
+  // so every step issues the same number of copies.
+  struct Copies {
+    __amdgpu_buffer_rsrc_t rK, rP, rV;
+    uint8_t* buf;
+  };
+  auto plan = [&](uint8_t* buf, int kt, int nkt) {
+    const bool live = kt < nkt;
+    const uint32_t k0 = live ? (uint32_t)(kt * BK) : 0u;
+    Copies c;
+    c.rK = make_rsrc(kseq + (size_t)k0 * kNope, live ? seq_bytes - k0 * 256u : 0u);
+    c.rP = make_rsrc(pseq + (size_t)k0 * kRope, live ? (uint32_t)(T - (int)k0) * 128u : 0u);
+    c.rV = make_rsrc(vseq + (size_t)k0 * kV, live ? seq_bytes - k0 * 256u : 0u);
+    c.buf = buf;
+    return c;
+  };
+  auto copy_one = [&](const Copies& c, int i) {
+    int j = (wave % NCW) + NCW * i;
+    if (j >= NCHUNK) j -= NCW;
+    uint8_t* dst = c.buf + j * 1024;
+    if (kind[i] == 0)
+      dma16(c.rK, dst, voff[i]);
+    else if (kind[i] == 1)
+      dma16(c.rP, dst, voff[i]);
+    else
+      dma16(c.rV, dst, voff[i]);
+  };
+  auto copy_all = [&](const Copies& c) {
+    if (wave >= NCW) return;
 #pragma unroll
-    for (int i = 0; i < DPW; ++i) {
-      int j = wave + NW * i;
-      if (j >= NCHUNK) j -= NW;
-      uint8_t* dst = buf + j * 1024;
-      if (kind[i] == 0)
-        dma16(rK, dst, voff[i]);
-      else if (kind[i] == 1)
-        dma16(rP, dst, voff[i]);
-      else
-        dma16(rV, dst, voff[i]);
-    }
+    for (int i = 0; i < DPW; ++i) copy_one(c, i);
   };
 
   // Zero the stages once, so rows that a copy leaves unwritten hold finite values.
@@ -271,9 +294,9 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     // ---- first copies of the pass, issued after the query loads so that
     // waiting for those does not wait for the copies (the previous pass ended
     // with all waves past their last LDS read and no copy outstanding)
-    issue(lds_s0, 0);
-    if (nkt > 1) issue(lds_s1, 1);
-    if (nkt > 2) issue(lds_s2, 2);
+    copy_all(plan(lds_s0, 0, nkt));
+    copy_all(plan(lds_s1, 1, nkt));
+    copy_all(plan(lds_s2, 2, nkt));
 
     float m_run = -INFINITY;  // reference maximum of scaled scores (base 2)
     float l_run = 0.f;        // this lane's share of the row sum
@@ -282,7 +305,6 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     // Scores, softmax and PV of key tile kt held in stage `buf`.
     auto compute = [&](const uint8_t* buf, int kt) {
       const int k0 = kt * BK;
-      if (!head_ok || k0 > q0 + 31) return;  // every key after this wave's queries
       bf16x8 kf[12];
       const uint8_t* kr = buf + k_lane;
 #pragma unroll
@@ -352,20 +374,18 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     // it every wave's copies of tile kt have landed and every wave has left
     // the stage that the next copy overwrites.
     auto wait_tile = [&](int kt) {
-      if (kt + 2 < nkt)
-        wait_vm<2 * DPW>();
-      else if (kt + 1 < nkt)
-        wait_vm<DPW>();
-      else
-        wait_vm<0>();
+      (void)kt;
+      wait_vm<2 * DPW>();  // tiles kt+1 and kt+2 (possibly empty) may still be in flight
       barrier_lds();
     };
 
     wait_tile(0);
-    // iteration kt: copy tile kt+3 into the stage tile kt-1 used, multiply tile kt
+    // Iteration kt: multiply tile kt, then copy tile kt+3 into the stage tile
+    // kt-1 used (every wave left it before the barrier that opened this
+    // iteration) just before waiting at the barrier for tile kt+1.
     auto step = [&](uint8_t* cur, uint8_t* ahead, int kt) {
-      if (kt + 3 < nkt) issue(ahead, kt + 3);
-      compute(cur, kt);
+      if (head_ok && kt * BK <= q0 + 31) compute(cur, kt);
+      copy_all(plan(ahead, kt + 3, nkt));
       if (kt + 1 < nkt) wait_tile(kt + 1);
     };
     for (int kt = 0; kt < nkt; kt += 4) {
@@ -377,6 +397,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
       if (kt + 3 >= nkt) break;
       step(lds_s3, lds_s2, kt + 3);
     }
+    wait_vm<0>();   // the empty copies past the last tile are done too
     barrier_lds();  // every wave is done with the stages before the next pass refills them
 
     // ---- epilogue
