@@ -9,22 +9,27 @@
 // Transformer blocks": causal mask M [T queries, T keys], positions 0..T-1.
 //
 // Work decomposition
-//   * A workgroup (8 waves) owns 2 heads × 128 queries of one sequence; each
-//     wave owns 32 queries of one head.  It processes a pair of query tiles,
-//     i and NQ-1-i, one after the other, so every workgroup does the same
-//     amount of causal work.  Workgroups of the same (sequence, head pair) are
-//     placed on the same XCD and issued together, so that XCD's L2 serves
-//     their shared key/value stream.
-//   * Key tiles are 32 keys.  A tile (k_nope of both heads, the rotated shared
-//     rotary key -- staged once for both heads -- and V of both heads) lives in
-//     one of four LDS stages.  Asynchronous buffer→LDS copies run three tiles
-//     ahead of the tile being multiplied; the workgroup barrier between tiles
-//     waits only for the next tile's copies (explicit, in-order vmcnt counts),
-//     never for the ones still in flight behind it.  A wave issuing copies
-//     stalls until the copy engine takes them, so the copies are issued by
-//     the four waves that finish each step first, at the end of the step,
-//     where they would otherwise idle at the barrier.  Past the last tile the
-//     copies are empty (zero-length descriptors), keeping the counts uniform.
+//   * A workgroup (8 waves) owns one head × 256 queries of one sequence; each
+//     wave owns 32 queries.  It processes a pair of query tiles, i and NQ-1-i,
+//     one after the other, so every workgroup does the same amount of causal
+//     work.  Workgroups of the same (sequence, head) are placed on the same
+//     XCD and issued together, so that XCD's L2 serves their key/value stream.
+//     (The head count per workgroup, G, is a constant: two heads per
+//     workgroup share one staged copy of the rotated key tile, but one head
+//     with twice the queries copies 43% fewer key/value bytes per query-head,
+//     which measured faster.  The rotated key is computed once per position
+//     for all heads either way.)
+//   * Key tiles are 32 keys.  A tile (k_nope, the rotated shared rotary key and
+//     V) lives in one of four LDS stages.  Asynchronous buffer→LDS copies run
+//     three tiles ahead of the tile being multiplied; the workgroup barrier
+//     between tiles waits only for the next tile's copies (explicit, in-order
+//     vmcnt counts), never for the ones still in flight behind it.  A wave
+//     issuing copies stalls until the copy engine takes them, so the copies
+//     are issued by the two waves that finish each step first (the SIMD gives
+//     the older of its two waves the matrix core first), at the end of the
+//     step, where they would otherwise idle at the barrier.  Past the last
+//     tile the copies are empty (zero-length descriptors), keeping the counts
+//     uniform.
 //
 // Per wave and key tile
 //   * Sᵀ = K·Qᵀ with v_mfma_f32_32x32x16_bf16: the key tile is the A operand
@@ -49,11 +54,11 @@
 namespace mla {
 namespace {
 
-constexpr int G = 2;          // heads per workgroup
-constexpr int WPH = 4;        // waves per head
+constexpr int G = 1;          // heads per workgroup
+constexpr int WPH = 8;        // waves per head
 constexpr int NW = G * WPH;   // 8 waves
 constexpr int NT = 64 * NW;   // 512 threads
-constexpr int BQ = 32 * WPH;  // 128 queries per head per tile
+constexpr int BQ = 32 * WPH;  // 256 queries per tile
 constexpr int BK = 32;        // keys per tile
 constexpr int NSTAGE = 4;     // LDS stages; copies run NSTAGE-1 tiles ahead
 constexpr float TAU = 8.0f;   // lazy-rescale threshold (log2 units)
@@ -61,26 +66,29 @@ constexpr float TAU = 8.0f;   // lazy-rescale threshold (log2 units)
 // LDS stage layout (bytes): k_nope head 0 | head 1 | rotated key | V head 0 | head 1.
 constexpr int K_ROW = 272;                  // 256 B of k_nope + 16 B pad (17 slots)
 constexpr int K_HEAD = BK * K_ROW;          // 8704
-constexpr int KPOFF = G * K_HEAD;           // 17408
+constexpr int KPOFF = (G * K_HEAD + 1023) / 1024 * 1024;  // k_nope region in whole 1 KiB chunks
 constexpr int KP_ROW = 128;                 // rotated key, 16 B chunks XOR-swizzled
-constexpr int VOFF = KPOFF + BK * KP_ROW;   // 21504
+constexpr int VOFF = KPOFF + BK * KP_ROW;   // 13312
 constexpr int V_ROW = 256;                  // natural layout, 64 B blocks XOR-swizzled
 constexpr int V_HEAD = BK * V_ROW;          // 8192
-constexpr int STAGE = VOFF + G * V_HEAD;    // 37888
+constexpr int STAGE = VOFF + G * V_HEAD;    // 21504
 
 // Copies per tile in 1 KiB chunks (one wave-instruction of 64 x 16 B each):
-// chunks [0, 17) k_nope, [17, 21) rotated key, [21, 37) V.  Only the first
+// chunks [0, CK) k_nope (padded to whole chunks), [CK, CKP) rotated key,
+// [CKP, NCHUNK) V.  Only the first
 // NCW waves copy (the SIMD gives them its matrix core first, so they reach
 // the end of a step early and issue the copies while the other waves still
 // compute); each issues the same number (the spare ones repeat a chunk another
 // wave also copies, writing identical bytes), so one vmcnt count fits all.
-constexpr int NCHUNK = STAGE / 1024;           // 37
-constexpr int CK = KPOFF / 1024;               // 17
-constexpr int CKP = VOFF / 1024;               // 21
-constexpr int NCW = 4;                         // waves that copy
-constexpr int DPW = (NCHUNK + NCW - 1) / NCW;  // 10 copies per copying wave per tile
+constexpr int NCHUNK = STAGE / 1024;           // 21
+constexpr int CK = KPOFF / 1024;               // 9
+constexpr int CKP = VOFF / 1024;               // 13
+constexpr int NCW = 2;                         // waves that copy
+constexpr int DPW = (NCHUNK + NCW - 1) / NCW;  // 11 copies per copying wave per tile
 static_assert(STAGE % 1024 == 0 && KPOFF % 1024 == 0 && VOFF % 1024 == 0, "chunk layout");
 static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS budget");
+static_assert((NSTAGE - 2) * DPW < 64, "vmcnt range");
+static_assert(NCHUNK - NCW >= CKP, "spare copies repeat V chunks");
 
 // Tile-local key held in LDS row R of a 32-key block: the key that A-operand
 // lane R fetches.  Accumulator register r of lane (n, h) is row
@@ -96,10 +104,7 @@ __device__ __forceinline__ int akey(int R) {
 // 8 consecutive rows and for same-parity rows among 16 consecutive ones.
 __device__ __forceinline__ int kpswz(int R) { return (R ^ (R >> 3)) & 7; }
 
-__shared__ __attribute__((aligned(16))) uint8_t lds_s0[STAGE];
-__shared__ __attribute__((aligned(16))) uint8_t lds_s1[STAGE];
-__shared__ __attribute__((aligned(16))) uint8_t lds_s2[STAGE];
-__shared__ __attribute__((aligned(16))) uint8_t lds_s3[STAGE];
+__shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ s16x4 ds_read_tr(const uint8_t* p) {
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const int HG = (H + G - 1) / G;
   const int NQ = (T + BQ - 1) / BQ;
   const int NP = (NQ + 1) / 2;  // query-tile pairs
-  const int U = p.B * HG;       // (sequence, head pair) units
+  const int U = p.B * HG;       // (sequence, head group) units
 
   // ---- XCD-aware placement: workgroup P runs on XCD P % 8; give each XCD whole
   // units, and issue a unit's pairs back to back.
@@ -159,10 +164,14 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
       const int s = j * 64 + lane;  // slot in the k_nope region (17 per row)
       const int gg = s / (BK * 17);
       const int s2 = s % (BK * 17);
-      const int R = s2 / 17;
+      int R = s2 / 17;
       int c = s2 % 17;
       if (c == 16) c = 15;  // pad slot: harmless duplicate
-      const int hh = min(hg * G + gg, H - 1);
+      if (gg >= G) {        // slot in the padding after the last head: duplicate too
+        R = BK - 1;
+        c = 15;
+      }
+      const int hh = min(hg * G + min(gg, G - 1), H - 1);
       v = ((uint32_t)hh * (uint32_t)T + (uint32_t)akey(R)) * 256u + c * 16;
       kind[i] = 0;
     } else if (j < CKP) {
@@ -223,12 +232,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   };
 
   // Zero the stages once, so rows that a copy leaves unwritten hold finite values.
-  for (int o = tid * 16; o < STAGE; o += NT * 16) {
-    *reinterpret_cast<u32x4*>(lds_s0 + o) = u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(lds_s1 + o) = u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(lds_s2 + o) = u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(lds_s3 + o) = u32x4{0, 0, 0, 0};
-  }
+  for (int o = tid * 16; o < NSTAGE * STAGE; o += NT * 16)
+    *reinterpret_cast<u32x4*>(lds + o) = u32x4{0, 0, 0, 0};
   __syncthreads();
 
   // Per-lane LDS addresses for the products.
@@ -294,9 +299,9 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     // ---- first copies of the pass, issued after the query loads so that
     // waiting for those does not wait for the copies (the previous pass ended
     // with all waves past their last LDS read and no copy outstanding)
-    copy_all(plan(lds_s0, 0, nkt));
-    copy_all(plan(lds_s1, 1, nkt));
-    copy_all(plan(lds_s2, 2, nkt));
+    auto stage = [&](int kt) { return lds + (kt % NSTAGE) * STAGE; };
+#pragma unroll
+    for (int st = 0; st < NSTAGE - 1; ++st) copy_all(plan(stage(st), st, nkt));
 
     float m_run = -INFINITY;  // reference maximum of scaled scores (base 2)
     float l_run = 0.f;        // this lane's share of the row sum
@@ -375,7 +380,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     // the stage that the next copy overwrites.
     auto wait_tile = [&](int kt) {
       (void)kt;
-      wait_vm<2 * DPW>();  // tiles kt+1 and kt+2 (possibly empty) may still be in flight
+      wait_vm<(NSTAGE - 2) * DPW>();  // later tiles' (possibly empty) copies may still be in flight
       barrier_lds();
     };
 
@@ -385,18 +390,10 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     // iteration) just before waiting at the barrier for tile kt+1.
     auto step = [&](uint8_t* cur, uint8_t* ahead, int kt) {
       if (head_ok && kt * BK <= q0 + 31) compute(cur, kt);
-      copy_all(plan(ahead, kt + 3, nkt));
+      copy_all(plan(ahead, kt + NSTAGE - 1, nkt));
       if (kt + 1 < nkt) wait_tile(kt + 1);
     };
-    for (int kt = 0; kt < nkt; kt += 4) {
-      step(lds_s0, lds_s3, kt);
-      if (kt + 1 >= nkt) break;
-      step(lds_s1, lds_s0, kt + 1);
-      if (kt + 2 >= nkt) break;
-      step(lds_s2, lds_s1, kt + 2);
-      if (kt + 3 >= nkt) break;
-      step(lds_s3, lds_s2, kt + 3);
-    }
+    for (int kt = 0; kt < nkt; ++kt) step(stage(kt), stage(kt + NSTAGE - 1), kt);
     wait_vm<0>();   // the empty copies past the last tile are done too
     barrier_lds();  // every wave is done with the stages before the next pass refills them
 
