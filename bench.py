@@ -35,10 +35,10 @@ CSRC = os.path.join(REPO, "transformer_attention_mla_amd", "csrc")
 # bytes written).  Each figure holds only for the kernel source it was taken on,
 # identified by a hash of its files; after any change the figure is dropped.
 MEASURED_TRAFFIC = {
-    "prefill_kernel": ("2fa313cb69676b27", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
-                       2030544382, "profiles/prefill_kernel_B4_T4096_H64.txt"),
-    "decode_split_kernel": ("20586ef06657d5ae", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                            21477503913, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
+    "prefill_kernel": ("4fb77bda87d97088", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
+                       2059366265, "profiles/prefill_kernel_B4_T4096_H64.txt"),
+    "decode_split_kernel": ("f78eb5a86ff042d4", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                            21477492520, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
 }
 
 
@@ -108,6 +108,55 @@ def cpu_baseline(d, B, H, T, R, scale, budget_s):
             "seconds": round(tn, 3)}
 
 
+def other_configs(mla, inputs, w_o, scale, dev, calls=10):
+    """Prefill attention and o_proj at the other prefill workloads (T = 64,
+    1024 with plain rotary angles; T = 16384 with the YaRN table), each call
+    timed with HIP events after 3 untimed ones; median per call.  Reported
+    beside the main line, not part of it."""
+    import torch
+
+    out = {}
+    for w in (1, 2, 4):
+        wl = inputs.WORKLOADS[w]
+        B, H, T = wl["B"], wl["H"], wl["T"]
+        print(f"other config: workload {w} (B={B} T={T})", file=sys.stderr, flush=True)
+        d = inputs.prefill_inputs(B, H, T, workload=w, device=dev)
+        o = torch.empty((B, T, H * 128), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(mla.mla_prefill_workspace_bytes(B, H, T), dtype=torch.uint8, device=dev)
+        M, K_O, N_O = B * T, H * 128, w_o.shape[0]
+        y = torch.empty((M, N_O), dtype=torch.bfloat16, device=dev)
+        ws_o = torch.empty(max(16, mla.mla_out_proj_workspace_bytes(M, K_O, N_O)), dtype=torch.uint8,
+                           device=dev)
+        fa = lambda: mla.mla_attend_prefill(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"],
+                                            d["R"], scale, out=o, workspace=ws)
+        fo = lambda: mla.mla_out_proj(o.view(M, K_O), w_o, y=y, workspace=ws_o)
+
+        def med(fn):
+            for _ in range(3):
+                fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(calls)]
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            t = sorted(a.elapsed_time(b) for a, b in ev)
+            return t[len(t) // 2]
+
+        ta, to = med(fa), med(fo)
+        fl_a, fl_o = prefill_flops(B, H, T), oproj_flops(M, K_O, N_O)
+        out[f"prefill_B{B}_T{T}_H{H}"] = {
+            "attention_ms": ta, "attention_tflops": fl_a / ta / 1e9,
+            "attention_frac_peak": fl_a / ta / 1e9 / PEAK_BF16_TFLOPS,
+            "oproj_ms": to, "oproj_tflops": fl_o / to / 1e9,
+            "oproj_gbps": oproj_bytes(M, K_O, N_O) / to / 1e6,
+            "rope": wl["rope"]}
+        del d, o, ws, y, ws_o
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +166,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--decode-splits", type=int, default=0)
     ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the extra prefill figures at T=64, 1024 and 16384")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, run a plain streaming kernel over 1 GiB (read 1 GiB, "
                          "write 1 GiB) three times, to scale hardware byte counters")
@@ -259,6 +310,9 @@ def main():
             res["roofline"] = res.pop("roofline_decode")
     cfg["workload"] = "; ".join(parts)
     res["config"] = cfg
+
+    if do_p and not args.no_other_configs:
+        res["other_configs"] = other_configs(mla, inputs, w_o, scale, dev)
 
     if do_p and not args.no_cpu_baseline:
         print("cpu baseline", file=sys.stderr, flush=True)

@@ -177,6 +177,27 @@ def sampled_rows(T, n_rand, rng):
     return np.array(sorted(rows), np.int32)
 
 
+def test_prefill_paired_tiles_every_row(gpu_device):
+    """B=4, H=64, T=640: enough work that every workgroup takes a pair of
+    query tiles (the schedule used at the large workloads), with a ragged
+    last query tile; every row of four heads against the oracle."""
+    B, H, T = 4, 64, 640
+    say(f"prefill paired tiles B={B} H={H} T={T}")
+    d = inputs.prefill_inputs(B, H, T, workload=0, device=gpu_device)
+    out32, lse = mla.mla_attend_prefill(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"],
+                                        d["R"], SCALE, out_f32=True, want_lse=True)
+    torch.cuda.synchronize()
+    R = d["R"].cpu().numpy()
+    rows = np.arange(T, dtype=np.int32)
+    for b, h in [(0, 0), (1, 17), (2, 42), (3, 63)]:
+        sl = lambda t: bits(t[b:b + 1, h:h + 1]) if t.shape[1] == H else bits(t[b:b + 1])
+        sel = np.stack([np.zeros_like(rows), np.zeros_like(rows), rows], 1)
+        o, l = oracle.prefill_rows(sl(d["q_nope"]), sl(d["q_pe"]), sl(d["k_nope"]), sl(d["k_pe"]),
+                                   sl(d["v"]), R, SCALE, sel)
+        check_close(to_host64(out32[b, :, h * 128:(h + 1) * 128]), o, TOL, f"b={b} h={h} all rows")
+        check_close(to_host64(lse[b, h]), l, TOL, f"b={b} h={h} lse")
+
+
 @pytest.mark.parametrize("workload", [3, 4])
 def test_prefill_large_workloads_sampled(workload, gpu_device):
     """Workloads 3 (B=4, T=4096) and 4 (B=1, T=16384, YaRN angles) in the

@@ -15,6 +15,7 @@ constexpr int kRope = 64;
 constexpr int kPairs = 32;
 constexpr int kQK = kNope + kRope;  // 192
 constexpr int kV = 128;
+constexpr int kComputeUnits = 256;  // MI355X (gfx950): 8 XCDs x 32 CUs
 
 constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -49,6 +50,7 @@ struct PrefillParams {
   int B, H, T;
   float scale_log2;    // softmax_scale * log2(e)
   int out_f32;
+  int paired;          // set by launch_prefill: 1 = a workgroup takes query tiles i and NQ-1-i
 };
 
 hipError_t launch_rope_prep(const PrefillParams& p, hipStream_t stream);

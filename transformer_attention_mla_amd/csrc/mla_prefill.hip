@@ -12,7 +12,9 @@
 //   * A workgroup (8 waves) owns one head × 256 queries of one sequence; each
 //     wave owns 32 queries.  It processes a pair of query tiles, i and NQ-1-i,
 //     one after the other, so every workgroup does the same amount of causal
-//     work.  Workgroups of the same (sequence, head) are placed on the same
+//     work -- unless that leaves fewer than two workgroups per compute unit
+//     (short sequences), when each workgroup takes one query tile, the
+//     longest first.  Workgroups of the same (sequence, head) are placed on the same
 //     XCD and issued together, so that XCD's L2 serves their key/value stream.
 //     (The head count per workgroup, G, is a constant: two heads per
 //     workgroup share one staged copy of the rotated key tile, but one head
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const int H = p.H, T = p.T;
   const int HG = (H + G - 1) / G;
   const int NQ = (T + BQ - 1) / BQ;
-  const int NP = (NQ + 1) / 2;  // query-tile pairs
+  const int NP = p.paired ? (NQ + 1) / 2 : NQ;  // query-tile pairs (or single tiles)
   const int U = p.B * HG;       // (sequence, head group) units
 
   // ---- XCD-aware placement: workgroup P runs on XCD P % 8; give each XCD whole
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const uint32_t ones = 0x3f803f80u;  // bf16 pair (1, 1)
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-  const int npass = (pair == NQ - 1 - pair) ? 1 : 2;
+  const int npass = (!p.paired || pair == NQ - 1 - pair) ? 1 : 2;
   for (int pass = 0; pass < npass; ++pass) {
     const int qt = pass == 0 ? NQ - 1 - pair : pair;  // longer tile first
     const int q0 = qt * BQ + qb * 32;
@@ -429,10 +431,14 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   const int HG = (p.H + G - 1) / G;
   const int NQ = (p.T + BQ - 1) / BQ;
-  const int NP = (NQ + 1) / 2;
-  const long blocks = (long)p.B * HG * NP;
+  PrefillParams q = p;
+  // Pairs balance causal work; single tiles double the workgroups, which
+  // matters when pairs would leave compute units idle.
+  const long paired_blocks = (long)p.B * HG * ((NQ + 1) / 2);
+  q.paired = paired_blocks >= 2 * kComputeUnits ? 1 : 0;
+  const long blocks = (long)p.B * HG * (q.paired ? (NQ + 1) / 2 : NQ);
   if (blocks <= 0 || blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, q);
   return hipGetLastError();
 }
 
