@@ -62,6 +62,11 @@ def _load():
     lib.oracle_decode.restype = I
     lib.oracle_decode_rows.argtypes = [P, P, P, P, P, I, I, D, I, I, I, I, P, P, P, I]
     lib.oracle_decode_rows.restype = I
+    lib.oracle_decode_shared_kpe.argtypes = [P, P, P, P, P, P, I, I, D, I, I, I, P, P, I]
+    lib.oracle_decode_shared_kpe.restype = I
+    lib.oracle_decode_shared_kpe_rows.argtypes = [P, P, P, P, P, P, I, I, D, I, I, I, I, P, P, P,
+                                                  I]
+    lib.oracle_decode_shared_kpe_rows.restype = I
     lib.oracle_out_proj.argtypes = [P, P, I, I, I, P, I]
     lib.oracle_out_proj.restype = I
     lib.oracle_out_proj_rows.argtypes = [P, P, I, I, I, I, P, P, I]
@@ -208,6 +213,56 @@ def decode_rows(q_nope, q_pe, k_cache, v_cache, R, q_pos, scale, sel, nthreads=N
                                 _p(out), _p(lse), nthreads or default_threads())
     if rc:
         raise ValueError(f"oracle_decode_rows failed ({rc})")
+    return out, lse
+
+
+def _check_shared_kpe_shapes(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache):
+    B, H, L, dn = k_nope_cache.shape
+    if dn != 128 or q_nope.shape != (B, H, 128) or q_pe.shape != (B, H, 64):
+        raise ValueError("k_nope_cache must be [B,H,L,128], q_nope [B,H,128], q_pe [B,H,64]")
+    if kpe_cache.shape != (B, L, 64) or v_cache.shape != (B, H, L, 128):
+        raise ValueError("kpe_cache must be [B,L,64] and v_cache [B,H,L,128]")
+    return B, H, L
+
+
+def decode_shared_kpe(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, q_pos, scale,
+                      nthreads=None):
+    """Decode against the shared-rotary cache layout: k_nope_cache [B,H,L,128],
+    kpe_cache [B,L,64] (rotated keys, one per position for every head), v_cache
+    [B,H,L,128].  Returns out [B,H*128] and lse [B,H]."""
+    lib = _load()
+    q_nope, q_pe, k_nope_cache, kpe_cache, v_cache = map(
+        _u16, (q_nope, q_pe, k_nope_cache, kpe_cache, v_cache))
+    R = _f32(R)
+    B, H, L = _check_shared_kpe_shapes(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache)
+    out = np.empty((B, H * 128), dtype=np.float64)
+    lse = np.empty((B, H), dtype=np.float64)
+    rc = lib.oracle_decode_shared_kpe(_p(q_nope), _p(q_pe), _p(k_nope_cache), _p(kpe_cache),
+                                      _p(v_cache), _p(R), R.shape[0], int(q_pos), float(scale),
+                                      B, H, L, _p(out), _p(lse), nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_decode_shared_kpe failed ({rc})")
+    return out, lse
+
+
+def decode_shared_kpe_rows(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, q_pos, scale, sel,
+                           nthreads=None):
+    """As decode_shared_kpe for selected (b, h) pairs ``sel`` [n,2]: out [n,128], lse [n]."""
+    lib = _load()
+    q_nope, q_pe, k_nope_cache, kpe_cache, v_cache = map(
+        _u16, (q_nope, q_pe, k_nope_cache, kpe_cache, v_cache))
+    R = _f32(R)
+    B, H, L = _check_shared_kpe_shapes(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache)
+    sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 2)
+    n = sel.shape[0]
+    out = np.empty((n, 128), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = lib.oracle_decode_shared_kpe_rows(_p(q_nope), _p(q_pe), _p(k_nope_cache), _p(kpe_cache),
+                                           _p(v_cache), _p(R), R.shape[0], int(q_pos),
+                                           float(scale), B, H, L, n, _p(sel), _p(out), _p(lse),
+                                           nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_decode_shared_kpe_rows failed ({rc})")
     return out, lse
 
 

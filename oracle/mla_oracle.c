@@ -341,6 +341,11 @@ typedef struct {
   const int *sel; /* NULL or n_sel (b, h) pairs */
   double *out;    /* full: [B][H*128]; rows: [n_sel][128] */
   double *lse;    /* full: [B][H]; rows: [n_sel] */
+  /* NULL: k_cache rows are [nope | rope] (192).  Otherwise the shared-rotary
+   * layout: k_cache rows are the 128 nope dims of each head and kpe_cache
+   * [B][L][64] holds the one rotated rope key per position, shared by every
+   * head ([MIX] the rotated key part is one tensor for all heads). */
+  const uint16_t *kpe_cache;
 } decode_ctx;
 
 static void decode_unit(void *vctx, long unit, double *scratch) {
@@ -359,13 +364,25 @@ static void decode_unit(void *vctx, long unit, double *scratch) {
   for (int d = 0; d < OR_ROPE; d++) qpe[d] = widen(c->q_pe[bh * OR_ROPE + d]);
   oracle_rotate_row(qpe, c->R + (size_t)c->q_pos * OR_PAIRS, qr);
   for (int d = 0; d < OR_ROPE; d++) qr[d] = oracle_bf16_round(qr[d]);
-  const long krow = OR_NOPE + OR_ROPE;
-  const uint16_t *kc = c->k_cache + bh * c->L * krow;
-  /* Widen the cached rotary parts of this head (already bf16 values). */
   double *kr = scratch + c->L;
-  for (long j = 0; j < c->L; j++)
-    for (int d = 0; d < OR_ROPE; d++) kr[j * OR_ROPE + d] = widen(kc[j * krow + OR_NOPE + d]);
-  rows_t kn = {kc, krow};
+  rows_t kn;
+  if (c->kpe_cache) {
+    /* Nope rows of this head; the rotated rope key of position j is row j of
+     * the sequence's shared table (already bf16 values). */
+    kn.base = c->k_cache + bh * c->L * OR_NOPE;
+    kn.stride = OR_NOPE;
+    const uint16_t *kp = c->kpe_cache + (long)b * c->L * OR_ROPE;
+    for (long j = 0; j < c->L; j++)
+      for (int d = 0; d < OR_ROPE; d++) kr[j * OR_ROPE + d] = widen(kp[j * OR_ROPE + d]);
+  } else {
+    const long krow = OR_NOPE + OR_ROPE;
+    const uint16_t *kc = c->k_cache + bh * c->L * krow;
+    /* Widen the cached rotary parts of this head (already bf16 values). */
+    for (long j = 0; j < c->L; j++)
+      for (int d = 0; d < OR_ROPE; d++) kr[j * OR_ROPE + d] = widen(kc[j * krow + OR_NOPE + d]);
+    kn.base = kc;
+    kn.stride = krow;
+  }
   rows_t vv = {c->v_cache + bh * c->L * OR_VDIM, OR_VDIM};
   attend_row(qn, qr, kn, kr, OR_ROPE, vv, c->L, c->scale, scratch, o, &l);
   if (c->sel) {
@@ -385,7 +402,7 @@ int oracle_decode(const uint16_t *q_nope, const uint16_t *q_pe, const uint16_t *
                   const uint16_t *v_cache, const float *R, int r_rows, int q_pos, double scale,
                   int B, int H, int L, double *out, double *lse, int nthreads) {
   if (B <= 0 || H <= 0 || L <= 0 || q_pos < 0 || q_pos >= r_rows) return 1;
-  decode_ctx c = {q_nope, q_pe, k_cache, v_cache, R, q_pos, scale, B, H, L, NULL, out, lse};
+  decode_ctx c = {q_nope, q_pe, k_cache, v_cache, R, q_pos, scale, B, H, L, NULL, out, lse, NULL};
   return run_units(decode_unit, &c, (long)B * H, (size_t)L * (1 + OR_ROPE), nthreads);
 }
 
@@ -397,7 +414,37 @@ int oracle_decode_rows(const uint16_t *q_nope, const uint16_t *q_pe, const uint1
   if (B <= 0 || H <= 0 || L <= 0 || q_pos < 0 || q_pos >= r_rows || n_sel < 0) return 1;
   for (int i = 0; i < n_sel; i++)
     if (sel[2 * i] < 0 || sel[2 * i] >= B || sel[2 * i + 1] < 0 || sel[2 * i + 1] >= H) return 1;
-  decode_ctx c = {q_nope, q_pe, k_cache, v_cache, R, q_pos, scale, B, H, L, sel, out, lse};
+  decode_ctx c = {q_nope, q_pe, k_cache, v_cache, R, q_pos, scale, B, H, L, sel, out, lse, NULL};
+  return run_units(decode_unit, &c, (long)n_sel, (size_t)L * (1 + OR_ROPE), nthreads);
+}
+
+/* Decode against the shared-rotary cache layout: k_nope_cache [B][H][L][128],
+ * kpe_cache [B][L][64] (rotated, one per position for all heads), v_cache
+ * [B][H][L][128].  Same scores and softmax as oracle_decode: the score of key
+ * j is the nope dot product plus the rope dot product with row j of the
+ * shared table. */
+int oracle_decode_shared_kpe(const uint16_t *q_nope, const uint16_t *q_pe,
+                             const uint16_t *k_nope_cache, const uint16_t *kpe_cache,
+                             const uint16_t *v_cache, const float *R, int r_rows, int q_pos,
+                             double scale, int B, int H, int L, double *out, double *lse,
+                             int nthreads) {
+  if (B <= 0 || H <= 0 || L <= 0 || q_pos < 0 || q_pos >= r_rows || !kpe_cache) return 1;
+  decode_ctx c = {q_nope, q_pe, k_nope_cache, v_cache, R, q_pos, scale, B, H, L, NULL, out, lse,
+                  kpe_cache};
+  return run_units(decode_unit, &c, (long)B * H, (size_t)L * (1 + OR_ROPE), nthreads);
+}
+
+int oracle_decode_shared_kpe_rows(const uint16_t *q_nope, const uint16_t *q_pe,
+                                  const uint16_t *k_nope_cache, const uint16_t *kpe_cache,
+                                  const uint16_t *v_cache, const float *R, int r_rows, int q_pos,
+                                  double scale, int B, int H, int L, int n_sel, const int *sel,
+                                  double *out, double *lse, int nthreads) {
+  if (B <= 0 || H <= 0 || L <= 0 || q_pos < 0 || q_pos >= r_rows || n_sel < 0 || !kpe_cache)
+    return 1;
+  for (int i = 0; i < n_sel; i++)
+    if (sel[2 * i] < 0 || sel[2 * i] >= B || sel[2 * i + 1] < 0 || sel[2 * i + 1] >= H) return 1;
+  decode_ctx c = {q_nope, q_pe, k_nope_cache, v_cache, R, q_pos, scale, B, H, L, sel, out, lse,
+                  kpe_cache};
   return run_units(decode_unit, &c, (long)n_sel, (size_t)L * (1 + OR_ROPE), nthreads);
 }
 

@@ -342,6 +342,53 @@ def test_decode_zero_query_mean_and_count():
     assert np.array_equal(np.rint(np.exp(lse)), np.full((B, H), L))
 
 
+def shared_kpe_case(B, H, L, seed):
+    qn = rand_bits((B, H, 128), seed)
+    qp = rand_bits((B, H, 64), seed + 1)
+    kn = rand_bits((B, H, L, 128), seed + 2)
+    kp = rand_bits((B, L, 64), seed + 3)
+    vc = rand_bits((B, H, L, 128), seed + 4)
+    return qn, qp, kn, kp, vc
+
+
+def test_decode_shared_kpe_equals_joined_cache():
+    """The shared-rotary layout is the joined layout with the one rope key per
+    position copied into every head's rows: same outputs, bit for bit."""
+    B, H, L, qpos = 3, 4, 45, 60
+    qn, qp, kn, kp, vc = shared_kpe_case(B, H, L, 1500)
+    R = inputs.rope_angles(qpos + 1)
+    joined = np.concatenate([kn, np.broadcast_to(kp[:, None], (B, H, L, 64))], axis=-1)
+    want, wl = oracle.decode(qn, qp, np.ascontiguousarray(joined), vc, R, qpos, SCALE)
+    got, gl = oracle.decode_shared_kpe(qn, qp, kn, kp, vc, R, qpos, SCALE)
+    assert np.array_equal(got, want) and np.array_equal(gl, wl)
+    sel = np.array([[2, 3], [0, 1], [1, 0]], np.int32)
+    ro, rl = oracle.decode_shared_kpe_rows(qn, qp, kn, kp, vc, R, qpos, SCALE, sel)
+    for i, (b, h) in enumerate(sel):
+        assert np.array_equal(ro[i], got[b, h * 128:(h + 1) * 128]) and rl[i] == gl[b, h]
+
+
+def test_decode_shared_kpe_single_key_zero_query_and_sharing():
+    B, H = 2, 3
+    qn, qp, kn, kp, vc = shared_kpe_case(B, H, 1, 1600)
+    R = inputs.rope_angles(4)
+    out, _ = oracle.decode_shared_kpe(qn, qp, kn, kp, vc, R, 3, SCALE)
+    assert np.array_equal(out, widen(vc).reshape(B, H * 128))  # one key: its value row
+    L = 33
+    qn, qp, kn, kp, vc = shared_kpe_case(B, H, L, 1700)
+    z = np.zeros((B, H, 128), np.uint16), np.zeros((B, H, 64), np.uint16)
+    out, lse = oracle.decode_shared_kpe(z[0], z[1], kn, kp, vc, R, 3, SCALE)
+    assert np.max(np.abs(out - widen(vc).mean(axis=2).reshape(B, H * 128))) < 1e-13
+    assert np.array_equal(np.rint(np.exp(lse)), np.full((B, H), L))
+    # The rope table of sequence 1 feeds every head of sequence 1 and nothing else.
+    base, _ = oracle.decode_shared_kpe(qn, qp, kn, kp, vc, R, 3, SCALE)
+    kp2 = kp.copy()
+    kp2[1] = rand_bits((L, 64), 1799)
+    pert, _ = oracle.decode_shared_kpe(qn, qp, kn, kp2, vc, R, 3, SCALE)
+    assert np.array_equal(pert[0], base[0])
+    assert all(not np.array_equal(pert[1, h * 128:(h + 1) * 128], base[1, h * 128:(h + 1) * 128])
+               for h in range(H))
+
+
 def test_decode_rows_equal_full():
     B, H, L = 2, 3, 30
     qn = rand_bits((B, H, 128), 1400)
