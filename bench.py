@@ -157,6 +157,46 @@ def other_configs(mla, inputs, w_o, scale, dev, calls=10):
     return out
 
 
+def decode_shared_kpe_bytes(B, H, L):
+    return B * H * L * (128 + 128) * 2 + B * L * 64 * 2 + B * H * ((128 + 64) * 2 + 128 * 2)
+
+
+def decode_shared_kpe_figures(mla, inputs, scale, dev, calls=10):
+    """Decode at B=64, H=64, L=8192 with the shared-rotary cache layout (nope
+    keys per head, one rotated rope key per position for all heads): median
+    call time and HBM rate on its algorithmic bytes (every cached byte once,
+    q in, output out).  Reported beside the main line, not part of it."""
+    import torch
+
+    wd = inputs.WORKLOADS[5]
+    B, H, L, q_pos = wd["B"], wd["H"], wd["L"], wd["q_pos"]
+    print("decode, shared-rotary cache layout", file=sys.stderr, flush=True)
+    d = inputs.decode_shared_kpe_inputs(B, H, L, q_pos, workload=5, device=dev)
+    out = torch.empty((B, H * 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(16, mla.mla_decode_workspace_bytes(B, H, L, 0)), dtype=torch.uint8,
+                     device=dev)
+    f = lambda: mla.mla_attend_decode_shared_kpe(d["q_nope"], d["q_pe"], d["k_nope_cache"],
+                                                 d["kpe_cache"], d["v_cache"], d["R"], q_pos, scale,
+                                                 out=out, workspace=ws)
+    for _ in range(3):
+        f()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for a, b in ev:
+        a.record()
+        f()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)[calls // 2]
+    nb = decode_shared_kpe_bytes(B, H, L)
+    del d
+    torch.cuda.empty_cache()
+    return {"workload": f"decode B={B} L={L} H={H} q_pos={q_pos}, k_nope [B,H,L,128] + shared "
+                        f"rotated k_pe [B,L,64] + V [B,H,L,128]",
+            "attention_ms": t, "hbm_gbps": nb / t / 1e6, "frac_hbm": nb / t / 1e6 / PEAK_HBM_GBPS,
+            "per_launch": f"{nb} bytes"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,7 +207,8 @@ def main():
     ap.add_argument("--decode-splits", type=int, default=0)
     ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all")
     ap.add_argument("--no-other-configs", action="store_true",
-                    help="skip the extra prefill figures at T=64, 1024 and 16384")
+                    help="skip the extra figures: prefill at T=64, 1024 and 16384, and decode "
+                         "with the shared-rotary cache layout")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, run a plain streaming kernel over 1 GiB (read 1 GiB, "
                          "write 1 GiB) three times, to scale hardware byte counters")
@@ -313,6 +354,8 @@ def main():
 
     if do_p and not args.no_other_configs:
         res["other_configs"] = other_configs(mla, inputs, w_o, scale, dev)
+    if do_d and not args.no_other_configs:
+        res["decode_shared_kpe"] = decode_shared_kpe_figures(mla, inputs, scale, dev)
 
     if do_p and not args.no_cpu_baseline:
         print("cpu baseline", file=sys.stderr, flush=True)

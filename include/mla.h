@@ -141,6 +141,27 @@ int mla_attend_decode(const mla_bf16 *q_nope, const mla_bf16 *q_pe, const mla_bf
                       size_t workspace_bytes, void *out, float *lse, uint32_t flags,
                       void *stream);
 
+/* Decode against a cache that keeps the rotated rope key once per position
+ * for all heads (page "Kimi K2 · Mix and project": the key's rotated part is
+ * one shared tensor for every head; the cache stores keys after the rotary
+ * step).  Same computation as mla_attend_decode with the joined key row
+ * [k_nope_cache[b,h,j] | kpe_cache[b,j]]; each head reads 256 + 256 bytes of its own
+ * per key instead of 384 + 256; the shared rope rows (128 bytes per key) serve
+ * every head of the sequence.
+ *
+ *   k_nope_cache [B, H, L, 128]  bf16   non-rotated key parts
+ *   kpe_cache    [B, L, 64]      bf16   rotated rope keys, one per position
+ *   (all other arguments, the workspace size -- mla_decode_workspace_bytes --
+ *   and the error behaviour as for mla_attend_decode; kpe_cache NULL is
+ *   MLA_ERR_NULL, misaligned MLA_ERR_ALIGN, overlapping an output MLA_ERR_ALIAS)
+ */
+int mla_attend_decode_shared_kpe(const mla_bf16 *q_nope, const mla_bf16 *q_pe,
+                                 const mla_bf16 *k_nope_cache, const mla_bf16 *kpe_cache,
+                                 const mla_bf16 *v_cache, const float *R, int r_rows, int q_pos,
+                                 float softmax_scale, int B, int H, int L, int num_splits,
+                                 void *workspace, size_t workspace_bytes, void *out, float *lse,
+                                 uint32_t flags, void *stream);
+
 /* --------------------------------------------------------------- o_proj --
  * y = x · w_oᵀ, the 8,192 → 7,168 output projection without bias (page "Kimi
  * K2 · Mix and project", parameter table and excerpt "mla-output").

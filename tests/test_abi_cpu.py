@@ -82,6 +82,17 @@ def decode(**kw):
                                        a["lse"], a["flags"], None)
 
 
+def decode_shared(**kw):
+    a = dict(q_nope=A[0], q_pe=A[1], kn=A[2], kp=A[8], vc=A[3], R=A[4], r_rows=10, q_pos=9,
+             scale=0.07, B=1, H=2, L=100, splits=1, ws=None, ws_bytes=0, out=A[5], lse=None,
+             flags=0)
+    a.update(kw)
+    return mla.lib().mla_attend_decode_shared_kpe(
+        a["q_nope"], a["q_pe"], a["kn"], a["kp"], a["vc"], a["R"], a["r_rows"], a["q_pos"],
+        a["scale"], a["B"], a["H"], a["L"], a["splits"], a["ws"], a["ws_bytes"], a["out"],
+        a["lse"], a["flags"], None)
+
+
 def oproj(**kw):
     a = dict(x=A[0], w=A[1], y=A[2], M=16384, K=8192, N=7168, ws=None, ws_bytes=0, flags=0)
     a.update(kw)
@@ -117,6 +128,18 @@ def test_prefill_rejects(kw, code):
 ])
 def test_decode_rejects(kw, code):
     assert decode(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kp=None), NULL), (dict(kn=None), NULL),
+    (dict(flags=4), FLAGS), (dict(L=0), DIM), (dict(q_pos=10), DIM), (dict(scale=0.0), SCALE),
+    (dict(splits=4), WORKSPACE),
+    (dict(kp=ctypes.c_void_p(9 * 16 * GB + 8)), ALIGN),
+    (dict(out=ctypes.c_void_p(9 * 16 * GB + 256)), ALIAS),     # out inside kpe_cache
+    (dict(out=ctypes.c_void_p(3 * 16 * GB + 51200 - 16)), ALIAS),  # end of the 128-wide key cache
+])
+def test_decode_shared_kpe_rejects(kw, code):
+    assert decode_shared(**kw) == code
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -118,3 +118,63 @@ def test_decode_workload5_sampled(gpu_device):
         check_close(to_host64(out32[b, h * 128:(h + 1) * 128]), o[0], TOL, f"b={b} h={h}")
         check_close(np.array([lse[b, h].item()]), l[0], TOL, f"b={b} h={h} lse")
         check_bf16_close(out16[b, h * 128:(h + 1) * 128], o[0], f"b={b} h={h} bf16")
+
+
+# ---- shared-rotary cache layout (nope keys per head, one rope key per position)
+
+def run_shared(d, dev, **kw):
+    g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in d.items()}
+    out, lse = mla.mla_attend_decode_shared_kpe(g["q_nope"], g["q_pe"], g["k_nope_cache"],
+                                                g["kpe_cache"], g["v_cache"], g["R"], g["q_pos"],
+                                                SCALE, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("B,H,L", [(1, 1, 1), (2, 3, 17), (3, 2, 1000), (2, 64, 300)])
+@pytest.mark.parametrize("splits", [0, 1, 3, 64])
+def test_decode_shared_kpe_parity(B, H, L, splits, gpu_device):
+    say(f"decode shared-kpe parity B={B} H={H} L={L} splits={splits}")
+    d = inputs.decode_shared_kpe_inputs(B, H, L, q_pos=L + 3)
+    want, want_lse = oracle.decode_shared_kpe(bits(d["q_nope"]), bits(d["q_pe"]),
+                                              bits(d["k_nope_cache"]), bits(d["kpe_cache"]),
+                                              bits(d["v_cache"]), d["R"].numpy(), d["q_pos"], SCALE)
+    o32, lse = run_shared(d, gpu_device, num_splits=splits, out_f32=True, want_lse=True)
+    o16, _ = run_shared(d, gpu_device, num_splits=splits)
+    check_close(to_host64(o32), want, TOL, "float32 output vs oracle")
+    check_close(to_host64(lse), want_lse, TOL, "lse vs oracle")
+    check_bf16_is_rne_of_f32(o16, o32)
+    check_bf16_close(o16, want, "bf16 output vs oracle")
+
+
+def test_decode_shared_kpe_equals_joined(gpu_device):
+    """The same cache in both layouts gives bit-identical outputs: the
+    kernels read the same bf16 key pieces and add them in the same order."""
+    B, H, L = 3, 8, 700
+    say(f"decode shared-kpe vs joined B={B} H={H} L={L}")
+    d = inputs.decode_shared_kpe_inputs(B, H, L, q_pos=L)
+    joined = torch.cat([d["k_nope_cache"], d["kpe_cache"][:, None].expand(B, H, L, 64)], -1)
+    dj = dict(q_nope=d["q_nope"], q_pe=d["q_pe"], k_cache=joined.contiguous(),
+              v_cache=d["v_cache"], R=d["R"], q_pos=d["q_pos"])
+    for splits in (1, 5):
+        a, la = run_shared(d, gpu_device, num_splits=splits, out_f32=True, want_lse=True)
+        b, lb = run(dj, gpu_device, num_splits=splits, out_f32=True, want_lse=True)
+        assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_decode_shared_kpe_full_size_sampled(gpu_device):
+    """B=64, H=64, L=8192 (the benchmark's decode shape) in the shared layout;
+    the oracle computes sampled (b, h) outputs exactly."""
+    w = inputs.WORKLOADS[5]
+    B, H, L, q_pos = w["B"], w["H"], w["L"], w["q_pos"]
+    say(f"decode shared-kpe sampled B={B} H={H} L={L}")
+    d = inputs.decode_shared_kpe_inputs(B, H, L, q_pos, workload=5, device=gpu_device)
+    o32, lse = run_shared(d, gpu_device, out_f32=True, want_lse=True)
+    sel = np.array([[0, 0], [63, 63], [17, 5], [40, 33], [5, 62]], np.int32)
+    sb = lambda t, b: bits(t[b:b + 1])
+    for b, h in sel:
+        want, wl = oracle.decode_shared_kpe_rows(
+            sb(d["q_nope"], b), sb(d["q_pe"], b), sb(d["k_nope_cache"], b), sb(d["kpe_cache"], b),
+            sb(d["v_cache"], b), d["R"].cpu().numpy(), q_pos, SCALE, np.array([[0, h]], np.int32))
+        check_close(to_host64(o32[b, h * 128:(h + 1) * 128]), want[0], TOL, f"b={b} h={h}")
+        check_close(to_host64(lse[b, h:h + 1]), wl, TOL, f"b={b} h={h} lse")

@@ -16,7 +16,8 @@ import os
 __all__ = [
     "MLA_OUT_F32", "MlaError", "lib", "mla_abi_version", "mla_status_string",
     "mla_prefill_workspace_bytes", "mla_attend_prefill", "mla_decode_splits",
-    "mla_decode_workspace_bytes", "mla_attend_decode", "mla_out_proj_workspace_bytes",
+    "mla_decode_workspace_bytes", "mla_attend_decode", "mla_attend_decode_shared_kpe",
+    "mla_out_proj_workspace_bytes",
     "mla_out_proj", "NOPE", "ROPE", "VDIM", "PAIRS",
 ]
 
@@ -60,6 +61,9 @@ def lib():
     L.mla_decode_workspace_bytes.restype = Z
     L.mla_attend_decode.argtypes = [P, P, P, P, P, I, I, F, I, I, I, I, P, Z, P, P, U, P]
     L.mla_attend_decode.restype = I
+    L.mla_attend_decode_shared_kpe.argtypes = [P, P, P, P, P, P, I, I, F, I, I, I, I, P, Z, P, P,
+                                               U, P]
+    L.mla_attend_decode_shared_kpe.restype = I
     L.mla_out_proj_workspace_bytes.argtypes = [I, I, I]
     L.mla_out_proj_workspace_bytes.restype = Z
     L.mla_out_proj.argtypes = [P, P, P, I, I, I, P, Z, U, P]
@@ -212,6 +216,46 @@ def mla_attend_decode(q_nope, q_pe, k_cache, v_cache, R, q_pos, softmax_scale, *
                                  MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
     if rc:
         raise MlaError(rc, "mla_attend_decode")
+    return out, lse
+
+
+def mla_attend_decode_shared_kpe(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, q_pos,
+                                 softmax_scale, *, num_splits=0, out=None, lse=None,
+                                 want_lse=False, out_f32=False, workspace=None, stream=None):
+    """Decode against the shared-rotary cache layout.  Shapes: q_nope [B,H,128],
+    q_pe [B,H,64] (unrotated; rotated at q_pos), k_nope_cache [B,H,L,128],
+    kpe_cache [B,L,64] (rotated keys, one per position for every head),
+    v_cache [B,H,L,128], R [r_rows,32].  Returns (out [B,H*128], lse [B,H] or None)."""
+    torch = _torch()
+    if k_nope_cache.dim() != 4:
+        raise ValueError("k_nope_cache must be [B, H, L, 128]")
+    B, H, L, _ = k_nope_cache.shape
+    dev = k_nope_cache.device
+    bf = torch.bfloat16
+    _check(q_nope, "q_nope", bf, (B, H, NOPE), dev)
+    _check(q_pe, "q_pe", bf, (B, H, ROPE), dev)
+    _check(k_nope_cache, "k_nope_cache", bf, (B, H, L, NOPE), dev)
+    _check(kpe_cache, "kpe_cache", bf, (B, L, ROPE), dev)
+    _check(v_cache, "v_cache", bf, (B, H, L, VDIM), dev)
+    if R.dim() != 2:
+        raise ValueError("R must be [r_rows, 32]")
+    _check(R, "R", torch.float32, (R.shape[0], PAIRS), dev)
+    odt = torch.float32 if out_f32 else bf
+    if out is None:
+        out = torch.empty((B, H * VDIM), dtype=odt, device=dev)
+    _check(out, "out", odt, (B, H * VDIM), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H), dev)
+    need = mla_decode_workspace_bytes(B, H, L, num_splits)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
+    rc = lib().mla_attend_decode_shared_kpe(
+        _ptr(q_nope), _ptr(q_pe), _ptr(k_nope_cache), _ptr(kpe_cache), _ptr(v_cache), _ptr(R),
+        R.shape[0], int(q_pos), float(softmax_scale), B, H, L, int(num_splits), _ptr(workspace),
+        ws_bytes, _ptr(out), _ptr(lse), MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_attend_decode_shared_kpe")
     return out, lse
 
 

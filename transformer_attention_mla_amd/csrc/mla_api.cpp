@@ -171,12 +171,18 @@ size_t mla_decode_workspace_bytes(int B, int H, int L, int num_splits) {
   return decode_ws_bytes(B, H, s);
 }
 
-int mla_attend_decode(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16* k_cache,
-                      const mla_bf16* v_cache, const float* R, int r_rows, int q_pos,
-                      float softmax_scale, int B, int H, int L, int num_splits, void* workspace,
-                      size_t workspace_bytes, void* out, float* lse, uint32_t flags,
-                      void* stream) {
-  if (!q_nope || !q_pe || !k_cache || !v_cache || !R || !out) return MLA_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points: kpe_cache null selects the joined key layout.
+int decode_common(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16* k_cache,
+                  const mla_bf16* kpe_cache, bool shared_kpe, const mla_bf16* v_cache,
+                  const float* R, int r_rows, int q_pos, float softmax_scale, int B, int H, int L,
+                  int num_splits, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                  uint32_t flags, void* stream) {
+  if (!q_nope || !q_pe || !k_cache || !v_cache || !R || !out || (shared_kpe && !kpe_cache))
+    return MLA_ERR_NULL;
   if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
   if (!dims_ok(B, H, L, kQK) || r_rows <= 0 || r_rows > kMaxDim || q_pos < 0 || q_pos >= r_rows ||
       num_splits < 0)
@@ -186,16 +192,19 @@ int mla_attend_decode(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf
   const size_t need = decode_ws_bytes(B, H, splits);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
   if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(R) || !aligned16(out) || !aligned16(lse) || !aligned16(workspace))
+      !aligned16(R) || !aligned16(out) || !aligned16(lse) || !aligned16(workspace) ||
+      !aligned16(kpe_cache))
     return MLA_ERR_ALIGN;
   const size_t bh = (size_t)B * H;
   const size_t out_elt = (flags & MLA_OUT_F32) ? 4 : 2;
+  const size_t krow = shared_kpe ? kNope : kQK;
   const Range in[] = {{q_nope, bh * kNope * 2}, {q_pe, bh * kRope * 2},
-                      {k_cache, bh * L * kQK * 2}, {v_cache, bh * L * kV * 2},
-                      {R, (size_t)r_rows * mla::kPairs * 4}};
+                      {k_cache, bh * L * krow * 2}, {v_cache, bh * L * kV * 2},
+                      {R, (size_t)r_rows * mla::kPairs * 4},
+                      {shared_kpe ? kpe_cache : nullptr, shared_kpe ? (size_t)B * L * kRope * 2 : 0}};
   const Range outs[] = {{out, bh * kV * out_elt}, {lse, lse ? bh * 4 : 0},
                         {need ? workspace : nullptr, need}};
-  if (any_alias(in, 5, outs, 3)) return MLA_ERR_ALIAS;
+  if (any_alias(in, 6, outs, 3)) return MLA_ERR_ALIAS;
   const int dev = check_device();
   if (dev != MLA_OK) return dev;
 
@@ -203,6 +212,7 @@ int mla_attend_decode(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf
   p.q_nope = q_nope;
   p.q_pe = q_pe;
   p.k_cache = k_cache;
+  p.kpe_cache = shared_kpe ? kpe_cache : nullptr;
   p.v_cache = v_cache;
   p.R = R;
   p.q_pos = q_pos;
@@ -218,6 +228,31 @@ int mla_attend_decode(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf
   (void)hipGetLastError();
   if (mla::launch_decode(p, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_LAUNCH;
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_attend_decode(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16* k_cache,
+                      const mla_bf16* v_cache, const float* R, int r_rows, int q_pos,
+                      float softmax_scale, int B, int H, int L, int num_splits, void* workspace,
+                      size_t workspace_bytes, void* out, float* lse, uint32_t flags,
+                      void* stream) {
+  return decode_common(q_nope, q_pe, k_cache, nullptr, false, v_cache, R, r_rows, q_pos,
+                       softmax_scale, B, H, L, num_splits, workspace, workspace_bytes, out, lse,
+                       flags, stream);
+}
+
+int mla_attend_decode_shared_kpe(const mla_bf16* q_nope, const mla_bf16* q_pe,
+                                 const mla_bf16* k_nope_cache, const mla_bf16* kpe_cache,
+                                 const mla_bf16* v_cache, const float* R, int r_rows, int q_pos,
+                                 float softmax_scale, int B, int H, int L, int num_splits,
+                                 void* workspace, size_t workspace_bytes, void* out, float* lse,
+                                 uint32_t flags, void* stream) {
+  return decode_common(q_nope, q_pe, k_nope_cache, kpe_cache, true, v_cache, R, r_rows, q_pos,
+                       softmax_scale, B, H, L, num_splits, workspace, workspace_bytes, out, lse,
+                       flags, stream);
 }
 
 // ------------------------------------------------------------------- o_proj

@@ -8,6 +8,11 @@
 // its own position (page "Kimi K2 · Transformer blocks": positions continue
 // from the cached length).
 //
+// Two cache layouts: joined key rows [nope 128 | rotated rope 64] per head,
+// or nope rows per head plus one rotated rope key per position shared by all
+// heads (page "Kimi K2 · Mix and project": the key's rotated part is one tensor
+// for every head), which reads 1/3 fewer key bytes per head.
+//
 // Design:
 //   * Workgroup = one (b, h, split) of 4 waves; a split is a contiguous key
 //     range [L·s/S, L·(s+1)/S).  Inside a wave, 8 lanes share one key: each
@@ -50,6 +55,7 @@ __device__ __forceinline__ float group8_sum(float x) {
   return x;
 }
 
+template <bool SHARED_KPE>
 __global__ __launch_bounds__(64 * DWAVES) void decode_split_kernel(DecodeParams p) {
   __shared__ float s_m[NGROUPS], s_l[NGROUPS];
   __shared__ float s_o[NGROUPS][kV];
@@ -98,8 +104,10 @@ __global__ __launch_bounds__(64 * DWAVES) void decode_split_kernel(DecodeParams 
   }
 
   const float cl2 = p.scale_log2;
-  const uint16_t* kbase = p.k_cache + (size_t)bh * L * kQK;
+  constexpr int KROW = SHARED_KPE ? kNope : kQK;  // elements per cached key row
+  const uint16_t* kbase = p.k_cache + (size_t)bh * L * KROW;
   const uint16_t* vbase = p.v_cache + (size_t)bh * L * kV;
+  const uint16_t* pbase = SHARED_KPE ? p.kpe_cache + (size_t)(bh / p.H) * L * kRope : nullptr;
 
   float m_run = -INFINITY, l_run = 0.f;
   float o[16];
@@ -111,11 +119,14 @@ __global__ __launch_bounds__(64 * DWAVES) void decode_split_kernel(DecodeParams 
 #pragma unroll
     for (int u = 0; u < KPG; ++u) {
       const int key = min(base + u * 8 + kq, ke - 1);
-      const uint16_t* krow = kbase + (size_t)key * kQK;
+      const uint16_t* krow = kbase + (size_t)key * KROW;
       const uint16_t* vrow = vbase + (size_t)key * kV;
       kr[u][0] = ld_global_16(krow + j * 8);
       kr[u][1] = ld_global_16(krow + 64 + j * 8);
-      kr[u][2] = ld_global_16(krow + 128 + j * 8);
+      if constexpr (SHARED_KPE)
+        kr[u][2] = ld_global_16(pbase + (size_t)key * kRope + j * 8);
+      else
+        kr[u][2] = ld_global_16(krow + 128 + j * 8);
       vr[u][0] = ld_global_16(vrow + j * 8);
       vr[u][1] = ld_global_16(vrow + 64 + j * 8);
     }
@@ -254,7 +265,10 @@ int decode_choose_splits(int B, int H, int L, int requested) {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const long blocks = (long)p.B * p.H * p.splits;
   if (blocks <= 0 || blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)blocks), dim3(64 * DWAVES), 0, stream, p);
+  if (p.kpe_cache)
+    hipLaunchKernelGGL(decode_split_kernel<true>, dim3((unsigned)blocks), dim3(64 * DWAVES), 0, stream, p);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<false>, dim3((unsigned)blocks), dim3(64 * DWAVES), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((long)p.B * p.H)), dim3(kV), 0, stream, p);

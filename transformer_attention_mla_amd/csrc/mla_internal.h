@@ -60,7 +60,8 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 struct DecodeParams {
   const uint16_t* q_nope;
   const uint16_t* q_pe;
-  const uint16_t* k_cache;
+  const uint16_t* k_cache;    // [B][H][L][192] joined keys, or [B][H][L][128] nope keys
+  const uint16_t* kpe_cache;  // null (joined layout) or [B][L][64] rotated keys shared by heads
   const uint16_t* v_cache;
   const float* R;
   int q_pos;

@@ -23,6 +23,7 @@ ROT_DIM = 64          # qk_rope_head_dim
 PAIRS = ROT_DIM // 2
 
 SEED_Q_NOPE, SEED_Q_PE, SEED_K_NOPE, SEED_K_PE, SEED_V, SEED_WO, SEED_KC, SEED_VC = range(8)
+SEED_KNC, SEED_KPC = 8, 9  # shared-rotary cache layout: nope keys, rope keys
 
 # The five workloads: (kind, B, T or L) with 64 heads.
 WORKLOADS = {
@@ -132,6 +133,23 @@ def decode_inputs(B: int, H: int, L: int, q_pos: int, workload: int = 0, device=
     v_cache = g((B, H, L, 128), SEED_VC)
     R = torch.from_numpy(rope_angles(q_pos + 1)).to(device)
     return dict(q_nope=q_nope, q_pe=q_pe, k_cache=k_cache, v_cache=v_cache, R=R, q_pos=q_pos)
+
+
+def decode_shared_kpe_inputs(B: int, H: int, L: int, q_pos: int, workload: int = 0, device="cpu"):
+    """The shared-rotary cache layout: q_nope, q_pe (bf16), k_nope_cache
+    [B,H,L,128], kpe_cache [B,L,64] (one rotated rope key per position for all
+    heads), v_cache [B,H,L,128] (bf16) and R with q_pos + 1 rows."""
+    import torch
+
+    g = lambda shape, k: normal_bf16(shape, seed_of(workload, k), device=device)
+    q_nope = g((B, H, 128), SEED_Q_NOPE)
+    q_pe = g((B, H, 64), SEED_Q_PE)
+    k_nope_cache = g((B, H, L, 128), SEED_KNC)
+    kpe_cache = g((B, L, 64), SEED_KPC)
+    v_cache = g((B, H, L, 128), SEED_VC)
+    R = torch.from_numpy(rope_angles(q_pos + 1)).to(device)
+    return dict(q_nope=q_nope, q_pe=q_pe, k_nope_cache=k_nope_cache, kpe_cache=kpe_cache,
+                v_cache=v_cache, R=R, q_pos=q_pos)
 
 
 def out_proj_weight(N: int = D_MODEL, K: int = 64 * 128, workload: int = 0, device="cpu"):
