@@ -35,10 +35,12 @@ CSRC = os.path.join(REPO, "transformer_attention_mla_amd", "csrc")
 # bytes written).  Each figure holds only for the kernel source it was taken on,
 # identified by a hash of its files; after any change the figure is dropped.
 MEASURED_TRAFFIC = {
-    "prefill_kernel": ("4fb77bda87d97088", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
-                       2059366265, "profiles/prefill_kernel_B4_T4096_H64.txt"),
-    "decode_split_kernel": ("f78eb5a86ff042d4", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                            21477492520, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
+    "prefill_kernel": ("2e9416efe79d9384", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
+                       2052310607, "profiles/prefill_kernel_B4_T4096_H64.txt"),
+    "decode_split_kernel": ("6fefb55b4e676b39", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                            21477497491, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
+    "decode_split_kernel_shared_kpe": ("6fefb55b4e676b39", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                                       17370668864, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
 }
 
 
@@ -194,7 +196,8 @@ def decode_shared_kpe_figures(mla, inputs, scale, dev, calls=10):
     return {"workload": f"decode B={B} L={L} H={H} q_pos={q_pos}, k_nope [B,H,L,128] + shared "
                         f"rotated k_pe [B,L,64] + V [B,H,L,128]",
             "attention_ms": t, "hbm_gbps": nb / t / 1e6, "frac_hbm": nb / t / 1e6 / PEAK_HBM_GBPS,
-            "per_launch": f"{nb} bytes"}
+            "per_launch": f"{nb} bytes",
+            "traffic": measured_traffic("decode_split_kernel_shared_kpe")}
 
 
 def main():

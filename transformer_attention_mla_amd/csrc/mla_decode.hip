@@ -61,9 +61,24 @@ __global__ __launch_bounds__(64 * DWAVES) void decode_split_kernel(DecodeParams 
   __shared__ float s_o[NGROUPS][kV];
 
   const int S = p.splits;
-  const int bid = blockIdx.x;
-  const int split = bid % S;
-  const int bh = bid / S;
+  int bh, split;
+  {
+    const int bid = blockIdx.x;
+    if (SHARED_KPE && p.B % 8 == 0) {
+      // Workgroup ids are dealt round-robin to the 8 XCDs: give every (head,
+      // split) of a sequence to one XCD, issued back to back, so that XCD's L2
+      // serves the sequence's shared rope rows to all its heads.
+      const int x = bid % 8, o = bid / 8;
+      const int per_seq = p.H * S;
+      const int b = x + 8 * (o / per_seq);
+      const int r = o % per_seq;
+      bh = b * p.H + r / S;
+      split = r % S;
+    } else {
+      split = bid % S;
+      bh = bid / S;
+    }
+  }
   const int L = p.L;
   const int ks = (int)((long long)L * split / S);
   const int ke = (int)((long long)L * (split + 1) / S);
