@@ -67,6 +67,8 @@ def _load():
     lib.oracle_decode_shared_kpe_rows.argtypes = [P, P, P, P, P, P, I, I, D, I, I, I, I, P, P, P,
                                                   I]
     lib.oracle_decode_shared_kpe_rows.restype = I
+    lib.oracle_decode_latent.argtypes = [P, P, P, P, P, P, I, I, D, I, I, I, I, P, I, P, P, I]
+    lib.oracle_decode_latent.restype = I
     lib.oracle_out_proj.argtypes = [P, P, I, I, I, P, I]
     lib.oracle_out_proj.restype = I
     lib.oracle_out_proj_rows.argtypes = [P, P, I, I, I, I, P, P, I]
@@ -263,6 +265,46 @@ def decode_shared_kpe_rows(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, q_
                                            nthreads or default_threads())
     if rc:
         raise ValueError(f"oracle_decode_shared_kpe_rows failed ({rc})")
+    return out, lse
+
+
+def _check_latent_shapes(q_nope, q_pe, ckv, kpe, w_kv_b):
+    B, L, r = ckv.shape
+    if r != 512 or q_nope.ndim != 3 or q_nope.shape[0] != B or q_nope.shape[2] != 128:
+        raise ValueError("ckv must be [B,L,512] and q_nope [B,H,128]")
+    H = q_nope.shape[1]
+    if q_pe.shape != (B, H, 64) or kpe.shape != (B, L, 64) or w_kv_b.shape != (H * 256, 512):
+        raise ValueError("q_pe must be [B,H,64], kpe [B,L,64], w_kv_b [H*256,512]")
+    return B, H, L
+
+
+def decode_latent(q_nope, q_pe, ckv, kpe, w_kv_b, R, q_pos, scale, sel=None, round_kv=True,
+                  nthreads=None):
+    """Decode against a latent cache: ckv [B,L,512] (the cached latent), kpe
+    [B,L,64] (rotated rope keys, one per position for every head), w_kv_b
+    [H*256,512] (the up-projection, rows h*256.. nope key, h*256+128.. value).
+    Every (b, h): out [B,H*128], lse [B,H]; with ``sel`` [n,2] (b, h) pairs:
+    out [n,128], lse [n].  ``round_kv=False`` keeps the up-projected keys and
+    values unrounded."""
+    lib = _load()
+    q_nope, q_pe, ckv, kpe, w_kv_b = map(_u16, (q_nope, q_pe, ckv, kpe, w_kv_b))
+    R = _f32(R)
+    B, H, L = _check_latent_shapes(q_nope, q_pe, ckv, kpe, w_kv_b)
+    if sel is None:
+        n, psel = 0, None
+        out = np.empty((B, H * 128), dtype=np.float64)
+        lse = np.empty((B, H), dtype=np.float64)
+    else:
+        sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 2)
+        n, psel = sel.shape[0], _p(sel)
+        out = np.empty((n, 128), dtype=np.float64)
+        lse = np.empty((n,), dtype=np.float64)
+    rc = lib.oracle_decode_latent(_p(q_nope), _p(q_pe), _p(ckv), _p(kpe), _p(w_kv_b), _p(R),
+                                  R.shape[0], int(q_pos), float(scale), B, H, L, n, psel,
+                                  1 if round_kv else 0, _p(out), _p(lse),
+                                  nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_decode_latent failed ({rc})")
     return out, lse
 
 

@@ -24,6 +24,8 @@
  *   R1  rotated q_pe / k_pe are stored in the bf16 query/key tensors ([MIX],
  *       "mla-prefill": query_states / key_states are built from them).
  *   R2  the flattened attention output enters o_proj as bf16 ([MIX], "mla-output").
+ *   R3  (latent decode only) the nope keys and values up-projected from the
+ *       cached latent fill the bf16 key and value tensors.
  * Every other intermediate (scores, softmax weights, sums) stays in fp64.
  * Rounding is round-to-nearest-even, done directly from double.
  *
@@ -446,6 +448,119 @@ int oracle_decode_shared_kpe_rows(const uint16_t *q_nope, const uint16_t *q_pe,
   decode_ctx c = {q_nope, q_pe, k_nope_cache, v_cache, R, q_pos, scale, B, H, L, sel, out, lse,
                   kpe_cache};
   return run_units(decode_unit, &c, (long)n_sel, (size_t)L * (1 + OR_ROPE), nthreads);
+}
+
+/* ------------------------------------------------------ latent decode ---- */
+
+/* Decode against a latent cache.  [CONFIG] fixes kv_lora_rank = 512 and the
+ * dense-block parameter total (pinned in the tests) fixes the up-projection as
+ * one 512 -> 64*(128+128) linear map, kv_b_proj, stored [out][in] like every
+ * linear layer of the model.  Reading of its output order (its code is not on
+ * the pages): per head, 128 nope-key features then 128 value features, heads
+ * in order, so head h's key rows are h*256 .. h*256+127 and its value rows
+ * h*256+128 .. h*256+255.  The cache keeps, per position, the 512-wide latent
+ * c and the rotated shared rope key (as in the shared-rotary layout).
+ *
+ * The plain definition: k_nope_j = W_uk,h c_j and v_j = W_uv,h c_j, each
+ * rounded to bf16 (rounding point R3: they fill the bf16 key and value tensors
+ * the attention reads), then the same scores, softmax and value mix as every
+ * other decode here.  round_kv = 0 skips R3 (used by a test that checks the
+ * algebra against an independent evaluation). */
+typedef struct {
+  const uint16_t *q_nope, *q_pe, *ckv, *kpe, *w_kv_b;
+  const float *R;
+  int q_pos;
+  double scale;
+  int B, H, L;
+  const int *sel;
+  double *out, *lse;
+  int round_kv;
+} latent_ctx;
+
+#define OR_LATENT 512
+
+/* Values of the up-projected row, rounded to bf16 (R3) unless round_kv is 0. */
+static void up_project(const uint16_t *w_rows, const uint16_t *c, int n_out, int round_kv,
+                       double *dst) {
+  for (int r = 0; r < n_out; r++) {
+    const uint16_t *w = w_rows + (size_t)r * OR_LATENT;
+    double acc = 0.0;
+    for (int k = 0; k < OR_LATENT; k++) acc += widen(w[k]) * widen(c[k]);
+    dst[r] = round_kv ? oracle_bf16_round(acc) : acc;
+  }
+}
+
+static void latent_unit(void *vctx, long unit, double *scratch) {
+  latent_ctx *c = (latent_ctx *)vctx;
+  int b, h;
+  if (c->sel) {
+    b = c->sel[2 * unit];
+    h = c->sel[2 * unit + 1];
+  } else {
+    h = (int)(unit % c->H);
+    b = (int)(unit / c->H);
+  }
+  const long bh = (long)b * c->H + h;
+  const long L = c->L;
+  double qn[OR_NOPE], qpe[OR_ROPE], qr[OR_ROPE], o[OR_VDIM];
+  for (int d = 0; d < OR_NOPE; d++) qn[d] = widen(c->q_nope[bh * OR_NOPE + d]);
+  for (int d = 0; d < OR_ROPE; d++) qpe[d] = widen(c->q_pe[bh * OR_ROPE + d]);
+  oracle_rotate_row(qpe, c->R + (size_t)c->q_pos * OR_PAIRS, qr);
+  for (int d = 0; d < OR_ROPE; d++) qr[d] = oracle_bf16_round(qr[d]);
+  /* scratch: scores [L] | k_nope [L][128] | v [L][128] | rope keys [L][64] */
+  double *s = scratch, *kn = s + L, *vv = kn + L * OR_NOPE, *kr = vv + L * OR_VDIM;
+  const uint16_t *wk = c->w_kv_b + (size_t)h * (OR_NOPE + OR_VDIM) * OR_LATENT;
+  const uint16_t *wv = wk + (size_t)OR_NOPE * OR_LATENT;
+  for (long j = 0; j < L; j++) {
+    const uint16_t *cj = c->ckv + ((long)b * L + j) * OR_LATENT;
+    up_project(wk, cj, OR_NOPE, c->round_kv, kn + j * OR_NOPE);
+    up_project(wv, cj, OR_VDIM, c->round_kv, vv + j * OR_VDIM);
+    for (int d = 0; d < OR_ROPE; d++) kr[j * OR_ROPE + d] = widen(c->kpe[((long)b * L + j) * OR_ROPE + d]);
+  }
+  /* The definition of attend_row, on double key and value rows. */
+  double m = -INFINITY;
+  for (long j = 0; j < L; j++) {
+    double dot_n = 0.0, dot_r = 0.0;
+    for (int d = 0; d < OR_NOPE; d++) dot_n += qn[d] * kn[j * OR_NOPE + d];
+    for (int d = 0; d < OR_ROPE; d++) dot_r += qr[d] * kr[j * OR_ROPE + d];
+    s[j] = c->scale * (dot_n + dot_r);
+    if (s[j] > m) m = s[j];
+  }
+  double denom = 0.0;
+  for (long j = 0; j < L; j++) denom += exp(s[j] - m);
+  for (int d = 0; d < OR_VDIM; d++) o[d] = 0.0;
+  for (long j = 0; j < L; j++) {
+    const double pj = exp(s[j] - m) / denom;
+    for (int d = 0; d < OR_VDIM; d++) o[d] += pj * vv[j * OR_VDIM + d];
+  }
+  const double l = m + log(denom);
+  if (c->sel) {
+    for (int d = 0; d < OR_VDIM; d++) c->out[unit * OR_VDIM + d] = o[d];
+    if (c->lse) c->lse[unit] = l;
+  } else {
+    double *dst = c->out + (size_t)b * c->H * OR_VDIM + (size_t)h * OR_VDIM;
+    for (int d = 0; d < OR_VDIM; d++) dst[d] = o[d];
+    if (c->lse) c->lse[bh] = l;
+  }
+}
+
+/* q_nope [B][H][128], q_pe [B][H][64] (unrotated), ckv [B][L][512], kpe
+ * [B][L][64] (rotated), w_kv_b [H*256][512]; out [B][H*128] double, lse [B][H]
+ * or NULL.  sel NULL: every (b, h); else n_sel (b, h) pairs and out
+ * [n_sel][128], lse [n_sel]. */
+int oracle_decode_latent(const uint16_t *q_nope, const uint16_t *q_pe, const uint16_t *ckv,
+                         const uint16_t *kpe, const uint16_t *w_kv_b, const float *R, int r_rows,
+                         int q_pos, double scale, int B, int H, int L, int n_sel, const int *sel,
+                         int round_kv, double *out, double *lse, int nthreads) {
+  if (B <= 0 || H <= 0 || L <= 0 || q_pos < 0 || q_pos >= r_rows) return 1;
+  if (sel) {
+    if (n_sel < 0) return 1;
+    for (int i = 0; i < n_sel; i++)
+      if (sel[2 * i] < 0 || sel[2 * i] >= B || sel[2 * i + 1] < 0 || sel[2 * i + 1] >= H) return 1;
+  }
+  latent_ctx c = {q_nope, q_pe, ckv, kpe, w_kv_b, R, q_pos, scale, B, H, L, sel, out, lse, round_kv};
+  const long units = sel ? (long)n_sel : (long)B * H;
+  return run_units(latent_unit, &c, units, (size_t)L * (1 + OR_NOPE + OR_VDIM + OR_ROPE), nthreads);
 }
 
 /* ------------------------------------------------------------- o_proj ---- */

@@ -389,6 +389,83 @@ def test_decode_shared_kpe_single_key_zero_query_and_sharing():
                for h in range(H))
 
 
+def latent_case(B, H, L, seed):
+    qn = rand_bits((B, H, 128), seed)
+    qp = rand_bits((B, H, 64), seed + 1)
+    ckv = rand_bits((B, L, 512), seed + 2)
+    kpe = rand_bits((B, L, 64), seed + 3)
+    w = rand_bits((H * 256, 512), seed + 4, std=0.02)
+    return qn, qp, ckv, kpe, w
+
+
+def test_decode_latent_selection_weights_equal_shared_kpe():
+    """With a kv_b_proj whose rows are one-hot (a different permutation of the
+    latent per head), every up-projected key and value is a latent element
+    exactly, so the latent decode must equal the shared-rotary decode on the
+    explicitly gathered caches, bit for bit: pins the head and row slicing."""
+    B, H, L, qpos = 2, 3, 37, 50
+    qn, qp, ckv, kpe, _ = latent_case(B, H, L, 2100)
+    rng = np.random.default_rng(2105)
+    perm = np.stack([rng.permutation(512) for _ in range(H)])
+    w = np.zeros((H * 256, 512), np.uint16)
+    for h in range(H):
+        w[h * 256 + np.arange(256), perm[h, :256]] = 0x3F80  # bf16 1.0
+    kn = np.stack([ckv[:, :, perm[h, :128]] for h in range(H)], axis=1)
+    vc = np.stack([ckv[:, :, perm[h, 128:256]] for h in range(H)], axis=1)
+    R = inputs.rope_angles(qpos + 1)
+    want, wl = oracle.decode_shared_kpe(qn, qp, np.ascontiguousarray(kn), kpe,
+                                        np.ascontiguousarray(vc), R, qpos, SCALE)
+    got, gl = oracle.decode_latent(qn, qp, ckv, kpe, w, R, qpos, SCALE)
+    assert np.array_equal(got, want) and np.array_equal(gl, wl)
+
+
+def test_decode_latent_absorbed_form():
+    """Without rounding the up-projected keys and values, the latent decode is
+    (W_uk q)·c scores over the latent, the softmax-weighted latent mean, then
+    W_uv: an independent evaluation (numpy, the query rotation as complex
+    multiplication) of the same function in the absorbed order."""
+    B, H, L, qpos = 2, 3, 29, 40
+    qn, qp, ckv, kpe, w = latent_case(B, H, L, 2200)
+    R = inputs.rope_angles(qpos + 1)
+    got, gl = oracle.decode_latent(qn, qp, ckv, kpe, w, R, qpos, SCALE, round_kv=False)
+    W = widen(w).reshape(H, 256, 512)
+    Wk, Wv = W[:, :128], W[:, 128:]
+    C, Kp = widen(ckv), widen(kpe)
+    qr = rne_bf16(complex_rotate(widen(qp), R[qpos].astype(np.float64)))
+    q_lat = np.einsum("bhd,hdc->bhc", widen(qn), Wk)
+    s = SCALE * (np.einsum("bhc,blc->bhl", q_lat, C) + np.einsum("bhr,blr->bhl", qr, Kp))
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    o_lat = np.einsum("bhl,blc->bhc", e / e.sum(axis=-1, keepdims=True), C)
+    want = np.einsum("hec,bhc->bhe", Wv, o_lat).reshape(B, H * 128)
+    lse = (m[..., 0] + np.log(e.sum(axis=-1)))
+    assert np.max(np.abs(got - want)) < 1e-12
+    assert np.max(np.abs(gl - lse)) < 1e-12
+    # with rounding (R3) the result moves, but only by the bf16 rounding of k and v
+    r, _ = oracle.decode_latent(qn, qp, ckv, kpe, w, R, qpos, SCALE)
+    assert 0 < np.max(np.abs(r - got)) < 5e-3
+
+
+def test_decode_latent_equals_joined_decode_and_rows():
+    """Up-project in numpy, round to bf16 (independent RNE), build the joined
+    [nope | rope] cache per head: the joined-cache decode gives the same
+    outputs; selected rows equal the full result."""
+    B, H, L, qpos = 2, 2, 23, 30
+    qn, qp, ckv, kpe, w = latent_case(B, H, L, 2300)
+    R = inputs.rope_angles(qpos + 1)
+    W = widen(w).reshape(H, 256, 512)
+    up = np.einsum("hoc,blc->bhlo", W, widen(ckv))
+    kn, vc = to_bits(rne_bf16(up[..., :128])), to_bits(rne_bf16(up[..., 128:]))
+    joined = np.concatenate([kn, np.broadcast_to(kpe[:, None], (B, H, L, 64))], axis=-1)
+    want, wl = oracle.decode(qn, qp, np.ascontiguousarray(joined), vc, R, qpos, SCALE)
+    got, gl = oracle.decode_latent(qn, qp, ckv, kpe, w, R, qpos, SCALE)
+    assert np.max(np.abs(got - want)) < 1e-14 and np.max(np.abs(gl - wl)) < 1e-13
+    sel = np.array([[1, 1], [0, 0], [1, 0]], np.int32)
+    ro, rl = oracle.decode_latent(qn, qp, ckv, kpe, w, R, qpos, SCALE, sel=sel)
+    for i, (b, h) in enumerate(sel):
+        assert np.array_equal(ro[i], got[b, h * 128:(h + 1) * 128]) and rl[i] == gl[b, h]
+
+
 def test_decode_rows_equal_full():
     B, H, L = 2, 3, 30
     qn = rand_bits((B, H, 128), 1400)

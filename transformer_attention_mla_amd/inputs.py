@@ -24,6 +24,7 @@ PAIRS = ROT_DIM // 2
 
 SEED_Q_NOPE, SEED_Q_PE, SEED_K_NOPE, SEED_K_PE, SEED_V, SEED_WO, SEED_KC, SEED_VC = range(8)
 SEED_KNC, SEED_KPC = 8, 9  # shared-rotary cache layout: nope keys, rope keys
+SEED_CKV, SEED_WKVB = 10, 11  # latent cache, up-projection weight
 
 # The five workloads: (kind, B, T or L) with 64 heads.
 WORKLOADS = {
@@ -150,6 +151,23 @@ def decode_shared_kpe_inputs(B: int, H: int, L: int, q_pos: int, workload: int =
     R = torch.from_numpy(rope_angles(q_pos + 1)).to(device)
     return dict(q_nope=q_nope, q_pe=q_pe, k_nope_cache=k_nope_cache, kpe_cache=kpe_cache,
                 v_cache=v_cache, R=R, q_pos=q_pos)
+
+
+def decode_latent_inputs(B: int, H: int, L: int, q_pos: int, workload: int = 0, device="cpu"):
+    """The latent cache layout: q_nope [B,H,128], q_pe [B,H,64], ckv [B,L,512]
+    (the cached latent after its normalisation, unit scale: N(0,1)), kpe
+    [B,L,64] (rotated rope keys, N(0,1)), w_kv_b [H*256,512] N(0, 0.02) (the
+    configuration's initializer range), all bf16, and R with q_pos + 1 rows."""
+    import torch
+
+    g = lambda shape, k, std=1.0: normal_bf16(shape, seed_of(workload, k), std=std, device=device)
+    q_nope = g((B, H, 128), SEED_Q_NOPE)
+    q_pe = g((B, H, 64), SEED_Q_PE)
+    ckv = g((B, L, 512), SEED_CKV)
+    kpe = g((B, L, 64), SEED_KPC)
+    w_kv_b = g((H * 256, 512), SEED_WKVB, 0.02)
+    R = torch.from_numpy(rope_angles(q_pos + 1)).to(device)
+    return dict(q_nope=q_nope, q_pe=q_pe, ckv=ckv, kpe=kpe, w_kv_b=w_kv_b, R=R, q_pos=q_pos)
 
 
 def out_proj_weight(N: int = D_MODEL, K: int = 64 * 128, workload: int = 0, device="cpu"):
