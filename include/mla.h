@@ -162,6 +162,43 @@ int mla_attend_decode_shared_kpe(const mla_bf16 *q_nope, const mla_bf16 *q_pe,
                                  void *workspace, size_t workspace_bytes, void *out, float *lse,
                                  uint32_t flags, void *stream);
 
+/* Decode against a latent cache.  Page "Block input" (config.json):
+ * kv_lora_rank 512, and the dense-block parameter total fixes kv_b_proj as one
+ * 512 -> H·(128+128) linear map; page "Kimi K2 · Mix and project": keys join a
+ * per-head nope part with the rotated rope part shared by all heads.  The cache
+ * keeps per position the 512-wide latent c (after its normalisation) and the
+ * rotated rope key; head h's nope key is W[h·256 .. h·256+127]·c and its value
+ * W[h·256+128 .. h·256+255]·c (W = kv_b_proj as the linear layer stores it,
+ * [out, in]).  The result equals the shared-rotary decode on those up-projected
+ * keys and values; the library computes it without forming them (query
+ * absorbed into the latent, W_uv applied after the value mix), reading 1,152
+ * bytes per position for all heads.
+ *
+ *   q_nope    [B, H, 128]     bf16   non-rotated query part
+ *   q_pe      [B, H, 64]      bf16   rotary query part, rotated at q_pos
+ *   ckv_cache [B, L, 512]     bf16   cached latent
+ *   kpe_cache [B, L, 64]      bf16   rotated rope keys, one per position
+ *   w_kv_b    [H*256, 512]    bf16   kv_b_proj weight
+ *   R, r_rows, q_pos, softmax_scale, out [B, H*128], lse [B, H], flags, stream
+ *                                    as for mla_attend_decode
+ *   num_splits                       position-range splits per sequence; 0 =
+ *                                    library's choice, else 1..L (clamped to L)
+ *   workspace  >= mla_decode_latent_workspace_bytes(B, H, L, num_splits) bytes,
+ *              always required (absorbed queries and latent outputs live there)
+ *
+ * Limits: 1 <= H <= 64 (all heads of a sequence share one workgroup),
+ * 1 <= L < 2^21, 1 <= B <= 2^20; otherwise MLA_ERR_DIM.  Other errors as for
+ * mla_attend_decode.
+ */
+size_t mla_decode_latent_workspace_bytes(int B, int H, int L, int num_splits);
+
+int mla_attend_decode_latent(const mla_bf16 *q_nope, const mla_bf16 *q_pe,
+                             const mla_bf16 *ckv_cache, const mla_bf16 *kpe_cache,
+                             const mla_bf16 *w_kv_b, const float *R, int r_rows, int q_pos,
+                             float softmax_scale, int B, int H, int L, int num_splits,
+                             void *workspace, size_t workspace_bytes, void *out, float *lse,
+                             uint32_t flags, void *stream);
+
 /* --------------------------------------------------------------- o_proj --
  * y = x · w_oᵀ, the 8,192 → 7,168 output projection without bias (page "Kimi
  * K2 · Mix and project", parameter table and excerpt "mla-output").

@@ -52,6 +52,12 @@ def test_workspace_sizes():
     assert mla.mla_decode_workspace_bytes(2, 3, 100, 4) == 2 * 3 * 4 * 136 * 4
     s = mla.mla_decode_splits(1, 64, 8192, 0)
     assert s > 1 and mla.mla_decode_workspace_bytes(1, 64, 8192, 0) == 64 * s * 136 * 4
+    # latent decode: bf16 absorbed queries + float32 latent outputs (+ split partials)
+    assert mla.mla_decode_latent_workspace_bytes(1, 64, 100, 1) == 64 * 512 * 2 + 64 * 512 * 4
+    assert mla.mla_decode_latent_workspace_bytes(64, 64, 8192, 0) == (
+        64 * 64 * 512 * 6 + 64 * 64 * 4 * 520 * 4)  # 4 splits: one workgroup per compute unit
+    assert mla.mla_decode_latent_workspace_bytes(1, 65, 100, 1) == 0      # > 64 heads
+    assert mla.mla_decode_latent_workspace_bytes(1, 64, 1 << 21, 1) == 0  # L too long
     assert mla.mla_out_proj_workspace_bytes(16384, 8192, 7168) == 0
     assert mla.mla_out_proj_workspace_bytes(64, 8192, 7168) > 0
     assert mla.mla_out_proj_workspace_bytes(64, 100, 7168) == 0  # K not a multiple of 128
@@ -91,6 +97,17 @@ def decode_shared(**kw):
         a["q_nope"], a["q_pe"], a["kn"], a["kp"], a["vc"], a["R"], a["r_rows"], a["q_pos"],
         a["scale"], a["B"], a["H"], a["L"], a["splits"], a["ws"], a["ws_bytes"], a["out"],
         a["lse"], a["flags"], None)
+
+
+def latent(**kw):
+    a = dict(q_nope=A[0], q_pe=A[1], ckv=A[2], kpe=A[3], w=A[4], R=A[5], r_rows=10, q_pos=9,
+             scale=0.07, B=1, H=2, L=100, splits=1, ws=A[6], ws_bytes=1 << 20, out=A[7], lse=None,
+             flags=0)
+    a.update(kw)
+    return mla.lib().mla_attend_decode_latent(
+        a["q_nope"], a["q_pe"], a["ckv"], a["kpe"], a["w"], a["R"], a["r_rows"], a["q_pos"],
+        a["scale"], a["B"], a["H"], a["L"], a["splits"], a["ws"], a["ws_bytes"], a["out"], a["lse"],
+        a["flags"], None)
 
 
 def oproj(**kw):
@@ -140,6 +157,23 @@ def test_decode_rejects(kw, code):
 ])
 def test_decode_shared_kpe_rejects(kw, code):
     assert decode_shared(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_nope=None), NULL), (dict(ckv=None), NULL), (dict(kpe=None), NULL), (dict(w=None), NULL),
+    (dict(R=None), NULL), (dict(out=None), NULL),
+    (dict(flags=2), FLAGS),
+    (dict(L=0), DIM), (dict(H=65), DIM), (dict(L=1 << 21), DIM), (dict(q_pos=10), DIM),
+    (dict(splits=-1), DIM),
+    (dict(scale=0.0), SCALE),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=1000), WORKSPACE),
+    (dict(w=ctypes.c_void_p(5 * 16 * GB + 8)), ALIGN),
+    (dict(out=ctypes.c_void_p(5 * 16 * GB + 256)), ALIAS),   # out inside w_kv_b
+    (dict(ws=A[2]), ALIAS),                                  # workspace over the latent cache
+    (dict(lse=ctypes.c_void_p(7 * 16 * GB + 4096)), ALIAS),  # lse inside the workspace
+])
+def test_decode_latent_rejects(kw, code):
+    assert latent(**kw) == code
 
 
 @pytest.mark.parametrize("kw,code", [

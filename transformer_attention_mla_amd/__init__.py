@@ -17,6 +17,7 @@ __all__ = [
     "MLA_OUT_F32", "MlaError", "lib", "mla_abi_version", "mla_status_string",
     "mla_prefill_workspace_bytes", "mla_attend_prefill", "mla_decode_splits",
     "mla_decode_workspace_bytes", "mla_attend_decode", "mla_attend_decode_shared_kpe",
+    "mla_decode_latent_workspace_bytes", "mla_attend_decode_latent",
     "mla_out_proj_workspace_bytes",
     "mla_out_proj", "NOPE", "ROPE", "VDIM", "PAIRS",
 ]
@@ -25,6 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 
 MLA_OUT_F32 = 0x1
 NOPE, ROPE, VDIM, PAIRS = 128, 64, 128, 32
+LATENT = 512  # kv_lora_rank
 
 _lib = None
 
@@ -64,6 +66,10 @@ def lib():
     L.mla_attend_decode_shared_kpe.argtypes = [P, P, P, P, P, P, I, I, F, I, I, I, I, P, Z, P, P,
                                                U, P]
     L.mla_attend_decode_shared_kpe.restype = I
+    L.mla_decode_latent_workspace_bytes.argtypes = [I, I, I, I]
+    L.mla_decode_latent_workspace_bytes.restype = Z
+    L.mla_attend_decode_latent.argtypes = [P, P, P, P, P, P, I, I, F, I, I, I, I, P, Z, P, P, U, P]
+    L.mla_attend_decode_latent.restype = I
     L.mla_out_proj_workspace_bytes.argtypes = [I, I, I]
     L.mla_out_proj_workspace_bytes.restype = Z
     L.mla_out_proj.argtypes = [P, P, P, I, I, I, P, Z, U, P]
@@ -90,6 +96,10 @@ def mla_decode_splits(B: int, H: int, L: int, num_splits: int = 0) -> int:
 
 def mla_decode_workspace_bytes(B: int, H: int, L: int, num_splits: int = 0) -> int:
     return lib().mla_decode_workspace_bytes(B, H, L, num_splits)
+
+
+def mla_decode_latent_workspace_bytes(B: int, H: int, L: int, num_splits: int = 0) -> int:
+    return lib().mla_decode_latent_workspace_bytes(B, H, L, num_splits)
 
 
 def mla_out_proj_workspace_bytes(M: int, K: int, N: int) -> int:
@@ -256,6 +266,48 @@ def mla_attend_decode_shared_kpe(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache,
         ws_bytes, _ptr(out), _ptr(lse), MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
     if rc:
         raise MlaError(rc, "mla_attend_decode_shared_kpe")
+    return out, lse
+
+
+def mla_attend_decode_latent(q_nope, q_pe, ckv_cache, kpe_cache, w_kv_b, R, q_pos, softmax_scale,
+                             *, num_splits=0, out=None, lse=None, want_lse=False, out_f32=False,
+                             workspace=None, stream=None):
+    """Decode against a latent cache.  Shapes: q_nope [B,H,128], q_pe [B,H,64]
+    (unrotated; rotated at q_pos), ckv_cache [B,L,512], kpe_cache [B,L,64]
+    (rotated keys, one per position for every head), w_kv_b [H*256,512] (the
+    up-projection, per head 128 key rows then 128 value rows), R [r_rows,32].
+    Returns (out [B,H*128], lse [B,H] or None)."""
+    torch = _torch()
+    if ckv_cache.dim() != 3 or q_nope.dim() != 3:
+        raise ValueError("ckv_cache must be [B, L, 512] and q_nope [B, H, 128]")
+    B, L, _ = ckv_cache.shape
+    H = q_nope.shape[1]
+    dev = ckv_cache.device
+    bf = torch.bfloat16
+    _check(q_nope, "q_nope", bf, (B, H, NOPE), dev)
+    _check(q_pe, "q_pe", bf, (B, H, ROPE), dev)
+    _check(ckv_cache, "ckv_cache", bf, (B, L, LATENT), dev)
+    _check(kpe_cache, "kpe_cache", bf, (B, L, ROPE), dev)
+    _check(w_kv_b, "w_kv_b", bf, (H * (NOPE + VDIM), LATENT), dev)
+    if R.dim() != 2:
+        raise ValueError("R must be [r_rows, 32]")
+    _check(R, "R", torch.float32, (R.shape[0], PAIRS), dev)
+    odt = torch.float32 if out_f32 else bf
+    if out is None:
+        out = torch.empty((B, H * VDIM), dtype=odt, device=dev)
+    _check(out, "out", odt, (B, H * VDIM), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H), dev)
+    workspace, ws_bytes = _workspace(workspace, mla_decode_latent_workspace_bytes(B, H, L, num_splits),
+                                     dev)
+    rc = lib().mla_attend_decode_latent(
+        _ptr(q_nope), _ptr(q_pe), _ptr(ckv_cache), _ptr(kpe_cache), _ptr(w_kv_b), _ptr(R),
+        R.shape[0], int(q_pos), float(softmax_scale), B, H, L, int(num_splits), _ptr(workspace),
+        ws_bytes, _ptr(out), _ptr(lse), MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_attend_decode_latent")
     return out, lse
 
 

@@ -255,6 +255,85 @@ int mla_attend_decode_shared_kpe(const mla_bf16* q_nope, const mla_bf16* q_pe,
                        flags, stream);
 }
 
+// ------------------------------------------------------------ latent decode
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kLatentMaxL = (1 << 21) - 1;  // L·1024 bytes must fit a buffer record count
+constexpr int kLatentMaxB = 1 << 20;        // ceil(B/16) grid rows
+
+bool latent_dims_ok(int B, int H, int L) {
+  return dims_ok(B, H, L, mla::kLatent + kRope) && H <= 64 && L <= kLatentMaxL && B <= kLatentMaxB;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_decode_latent_workspace_bytes(int B, int H, int L, int num_splits) {
+  if (!latent_dims_ok(B, H, L) || num_splits < 0) return 0;
+  return mla::latent_workspace_layout(B, H, mla::latent_choose_splits(B, L, num_splits)).total;
+}
+
+int mla_attend_decode_latent(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16* ckv_cache,
+                             const mla_bf16* kpe_cache, const mla_bf16* w_kv_b, const float* R,
+                             int r_rows, int q_pos, float softmax_scale, int B, int H, int L,
+                             int num_splits, void* workspace, size_t workspace_bytes, void* out,
+                             float* lse, uint32_t flags, void* stream) {
+  if (!q_nope || !q_pe || !ckv_cache || !kpe_cache || !w_kv_b || !R || !out) return MLA_ERR_NULL;
+  if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
+  if (!latent_dims_ok(B, H, L) || r_rows <= 0 || r_rows > kMaxDim || q_pos < 0 || q_pos >= r_rows ||
+      num_splits < 0)
+    return MLA_ERR_DIM;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_SCALE;
+  const int splits = mla::latent_choose_splits(B, L, num_splits);
+  const mla::LatentWorkspace ws = mla::latent_workspace_layout(B, H, splits);
+  if (!workspace || workspace_bytes < ws.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(ckv_cache) || !aligned16(kpe_cache) ||
+      !aligned16(w_kv_b) || !aligned16(R) || !aligned16(out) || !aligned16(lse) ||
+      !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  const size_t bh = (size_t)B * H;
+  const size_t out_elt = (flags & MLA_OUT_F32) ? 4 : 2;
+  const Range in[] = {{q_nope, bh * kNope * 2},
+                      {q_pe, bh * kRope * 2},
+                      {ckv_cache, (size_t)B * L * mla::kLatent * 2},
+                      {kpe_cache, (size_t)B * L * kRope * 2},
+                      {w_kv_b, (size_t)H * 256 * mla::kLatent * 2},
+                      {R, (size_t)r_rows * mla::kPairs * 4}};
+  const Range outs[] = {{out, bh * kV * out_elt}, {lse, lse ? bh * 4 : 0}, {workspace, ws.total}};
+  if (any_alias(in, 6, outs, 3)) return MLA_ERR_ALIAS;
+  const int dev = check_device();
+  if (dev != MLA_OK) return dev;
+
+  char* w = static_cast<char*>(workspace);
+  mla::LatentParams p;
+  p.q_nope = q_nope;
+  p.q_pe = q_pe;
+  p.ckv = ckv_cache;
+  p.kpe = kpe_cache;
+  p.w_kv_b = w_kv_b;
+  p.R = R;
+  p.q_pos = q_pos;
+  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  p.B = B;
+  p.H = H;
+  p.L = L;
+  p.splits = splits;
+  p.q_lat = reinterpret_cast<uint16_t*>(w + ws.q_off);
+  p.o_lat = reinterpret_cast<float*>(w + ws.o_off);
+  p.part = splits > 1 ? reinterpret_cast<float*>(w + ws.part_off) : nullptr;
+  p.lse = lse;
+  p.out = out;
+  p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
+  (void)hipGetLastError();
+  if (mla::launch_decode_latent(p, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
 // ------------------------------------------------------------------- o_proj
 
 size_t mla_out_proj_workspace_bytes(int M, int K, int N) {

@@ -81,6 +81,36 @@ constexpr int kDecodePart = 136;
 int decode_choose_splits(int B, int H, int L, int requested);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
+// ---------------------------------------------------------- latent decode --
+constexpr int kLatent = 512;      // kv_lora_rank
+constexpr int kLatentPart = 520;  // split partial: max, sum, 6 pad, 512 outputs
+
+struct LatentParams {
+  const uint16_t* q_nope;  // [B][H][128]
+  const uint16_t* q_pe;    // [B][H][64], unrotated
+  const uint16_t* ckv;     // [B][L][512] cached latent
+  const uint16_t* kpe;     // [B][L][64] rotated rope keys shared by heads
+  const uint16_t* w_kv_b;  // [H*256][512]: per head 128 key rows, 128 value rows
+  const float* R;
+  int q_pos;
+  float scale_log2;
+  int B, H, L;
+  int splits;
+  uint16_t* q_lat;  // workspace [B][H][512] bf16: q_nope·W_uk
+  float* o_lat;     // workspace [B][H][512]: normalised latent output
+  float* part;      // workspace [B][H][splits][kLatentPart] when splits > 1
+  float* lse;
+  void* out;        // [B][H*128]
+  int out_f32;
+};
+
+struct LatentWorkspace {
+  size_t q_off, o_off, part_off, total;
+};
+LatentWorkspace latent_workspace_layout(int B, int H, int splits);
+int latent_choose_splits(int B, int L, int requested);
+hipError_t launch_decode_latent(const LatentParams& p, hipStream_t stream);
+
 // ----------------------------------------------------------------- o_proj --
 struct OprojParams {
   const uint16_t* x;  // [M][K]
