@@ -41,6 +41,8 @@ MEASURED_TRAFFIC = {
                             21477497491, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
     "decode_split_kernel_shared_kpe": ("6fefb55b4e676b39", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
                                        17370668864, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
+    "latent_decode_kernel": ("0", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
+                             0, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
 }
 
 
@@ -198,6 +200,55 @@ def decode_shared_kpe_figures(mla, inputs, scale, dev, calls=10):
             "attention_ms": t, "hbm_gbps": nb / t / 1e6, "frac_hbm": nb / t / 1e6 / PEAK_HBM_GBPS,
             "per_launch": f"{nb} bytes",
             "traffic": measured_traffic("decode_split_kernel_shared_kpe")}
+
+
+def decode_latent_bytes(B, H, L):
+    """Every cached byte once (latent 512 + rotated rope key 64 per position),
+    kv_b_proj once, queries in, outputs out."""
+    return B * L * (512 + 64) * 2 + H * 256 * 512 * 2 + B * H * ((128 + 64) * 2 + 128 * 2)
+
+
+def decode_latent_flops(B, H, L):
+    """Scores over 576 dims and the mix over 512 per (head, position), plus the
+    query absorption (128 x 512) and the value expansion (512 x 128) per head."""
+    return 2.0 * B * H * (L * (576 + 512) + 2 * 128 * 512)
+
+
+def decode_latent_figures(mla, inputs, scale, dev, calls=20):
+    """Decode at B=64, H=64, L=8192 against the latent cache (512-wide latent
+    and the rotated rope key per position, kv_b_proj [64*256, 512]): median
+    call time of the whole entry point (absorb, attend, merge, expand) and its
+    rates on the algorithmic bytes and flops.  Reported beside the main line."""
+    import torch
+
+    wd = inputs.WORKLOADS[5]
+    B, H, L, q_pos = wd["B"], wd["H"], wd["L"], wd["q_pos"]
+    print("decode, latent cache", file=sys.stderr, flush=True)
+    d = inputs.decode_latent_inputs(B, H, L, q_pos, workload=5, device=dev)
+    out = torch.empty((B, H * 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mla.mla_decode_latent_workspace_bytes(B, H, L, 0), dtype=torch.uint8,
+                     device=dev)
+    f = lambda: mla.mla_attend_decode_latent(d["q_nope"], d["q_pe"], d["ckv"], d["kpe"],
+                                             d["w_kv_b"], d["R"], q_pos, scale, out=out,
+                                             workspace=ws)
+    for _ in range(3):
+        f()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for a, b in ev:
+        a.record()
+        f()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)[calls // 2]
+    nb, nf = decode_latent_bytes(B, H, L), decode_latent_flops(B, H, L)
+    del d
+    torch.cuda.empty_cache()
+    return {"workload": f"decode B={B} L={L} H={H} q_pos={q_pos}, latent cache [B,L,512] + "
+                        f"rotated k_pe [B,L,64], kv_b_proj [{H * 256},512]",
+            "call_ms": t, "hbm_gbps": nb / t / 1e6, "frac_hbm": nb / t / 1e6 / PEAK_HBM_GBPS,
+            "tflops": nf / t / 1e9, "per_call": f"{nb} bytes, {nf:.4e} flops",
+            "traffic": measured_traffic("latent_decode_kernel")}
 
 
 def main():
@@ -359,6 +410,7 @@ def main():
         res["other_configs"] = other_configs(mla, inputs, w_o, scale, dev)
     if do_d and not args.no_other_configs:
         res["decode_shared_kpe"] = decode_shared_kpe_figures(mla, inputs, scale, dev)
+        res["decode_latent"] = decode_latent_figures(mla, inputs, scale, dev)
 
     if do_p and not args.no_cpu_baseline:
         print("cpu baseline", file=sys.stderr, flush=True)

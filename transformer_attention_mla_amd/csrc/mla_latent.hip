@@ -24,8 +24,9 @@
 //                         the 512 latent dims with 16x16x32 bf16 MFMA; cache
 //                         tiles of 32 positions staged in LDS by buffer->LDS
 //                         copies three tiles ahead
-//   latent_merge_kernel   log-sum-exp merge of the split partials (splits > 1)
-//   latent_out_kernel     out[b,h] = W_uv,h · o_lat[b,h]            (MFMA 16x16x32)
+//   latent_out_kernel     log-sum-exp merge of the split partials into bf16
+//                         latent rows in LDS, then out[b,h] = W_uv,h · o_lat[b,h]
+//                         (MFMA 16x16x32)
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -47,12 +48,14 @@ static_assert(L_STAGE % 1024 == 0 && L_CHUNKS % LW == 0, "copy layout");
 static_assert(LNST * L_STAGE <= 160 * 1024, "LDS budget");
 static_assert((LNST - 2) * L_CPW < 64, "vmcnt range");
 
-// 16-byte chunk swizzle of latent row r (chunk x stored at x ^ lsw(r)).  The
-// score reads take one chunk from 16 consecutive rows: lsw is a bijection on
-// r mod 16 (and on r mod 8 for 8 rows).  The transposed value reads take two
-// neighbouring chunks from 4 consecutive rows 4g..4g+3: lsw(4g+i) = 2i + (g&1)
-// + 8(g>>1) keeps the four chunk pairs apart.
-__device__ __forceinline__ int lsw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+// 16-byte chunk swizzle of latent row r (chunk x stored at x ^ lsw(r)); rows
+// are 1 KiB, so a chunk's bank group is its physical index mod 16 (64 banks),
+// or mod 8 within a 128-byte half.  Score reads take one chunk from 16
+// consecutive rows: lsw is a bijection on r mod 16, and on r mod 8 over any 8
+// aligned rows.  Transposed value reads: the 32 lanes of a half-wave take two
+// neighbouring chunks (one pair) from each of 8 aligned rows, and the pair
+// indices lsw(r) >> 1 are distinct mod 8 over those rows.
+__device__ __forceinline__ int lsw(int r) { return (r & 7) | (((r ^ (r >> 3)) & 1) << 3); }
 // Rope-key rows (8 chunks): distinct for any 8 consecutive rows and for
 // same-parity rows among 16 consecutive ones.
 __device__ __forceinline__ int psw(int r) { return (r ^ (r >> 3)) & 7; }
@@ -83,35 +86,59 @@ __device__ __forceinline__ bf16x8 pack8(const float* y) {
 }
 
 // ------------------------------------------------------------------ absorb --
-// q_lat[b][h][c] = bf16(Σ_d q_nope[b][h][d] · W[h·256 + d][c]).  One wave per
-// 16 sequences × 16 latent columns of one head; K = 128 in 4 MFMA steps.  The
-// weight's reduction index d is its row, so each lane gathers 8 rows of its
-// column (32 contiguous bytes per row across the 16 lanes of a group).
+// q_lat[b][h][c] = bf16(Σ_d q_nope[b][h][d] · W[h·256 + d][c]).  One workgroup
+// per (head h, 64 latent columns), 4 waves of 16 columns, looping over the
+// sequences 16 at a time; K = 128 in 4 MFMA steps.  The weight's reduction
+// index d is its row, so the 128 x 64 weight block is staged in LDS with
+// 16-byte loads and its B fragments (8 consecutive rows of one column) come
+// from ds_read_b64_tr_b16.  LDS row d (128 B) keeps chunk x at x ^ qsw(d): the
+// 32 lanes of a half-wave read two chunks from each of rows 8g..8g+3 and
+// 8g+8..8g+11 (+4 for the second read), which qsw spreads over 16 bank groups.
+__device__ __forceinline__ int qsw(int d) { return ((((d >> 1) & 1) | (((d >> 3) & 1) << 1)) << 1); }
+
 __global__ __launch_bounds__(256) void latent_q_kernel(LatentParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.x, b0 = blockIdx.y * 16, c0 = (blockIdx.z * 4 + wave) * 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t wt[kNope * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, cb = blockIdx.y * 64;
   const int q = lane >> 4, i = lane & 15;
   const int H = p.H;
-  const int brow = b0 + i;
-  const uint16_t* w = p.w_kv_b + (size_t)h * 256 * kLatent + c0 + i;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // Stage W[h·256 + d][cb .. cb+63], d < 128: 1024 chunks of 16 B, 4 per thread.
+  const uint16_t* wsrc = p.w_kv_b + (size_t)h * 256 * kLatent + cb;
 #pragma unroll
-  for (int ks = 0; ks < kNope / 32; ++ks) {
-    u32x4 a = {0u, 0u, 0u, 0u};
-    if (brow < p.B) a = ld_global_16(p.q_nope + ((size_t)brow * H + h) * kNope + ks * 32 + q * 8);
-    u32x4 bw;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = ks * 32 + q * 8 + 2 * j;
-      bw[j] = (uint32_t)w[(size_t)d * kLatent] | ((uint32_t)w[(size_t)(d + 1) * kLatent] << 16);
-    }
-    acc = mfma16x16x32(as_bf16x8(a), as_bf16x8(bw), acc);
+  for (int it = 0; it < 4; ++it) {
+    const int item = tid + it * 256;
+    const int d = item >> 3, x = item & 7;
+    const u32x4 v = ld_global_16(wsrc + (size_t)d * kLatent + x * 8);
+    *reinterpret_cast<u32x4*>(wt + d * 128 + ((x ^ qsw(d)) * 16)) = v;
   }
+  __syncthreads();
+  // B fragments of this wave's 16 columns for the 4 k-steps: lane s of group q
+  // addresses row ks*32 + 8q + s/4 (+4), columns 16*wave + (s%4)*4 .. +3.
+  bf16x8 bf[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int b = b0 + q * 4 + r;
-    if (b < p.B)
-      reinterpret_cast<__bf16*>(p.q_lat)[((size_t)b * H + h) * kLatent + c0 + i] = f32_to_bf16(acc[r]);
+  for (int ks = 0; ks < 4; ++ks) {
+    const int d = ks * 32 + q * 8 + (i >> 2);
+    const int colb = wave * 32 + (i & 3) * 8;  // byte offset of the column group in the row
+    const s16x4 lo = ds_read_tr(wt + d * 128 + ((((colb >> 4) ^ qsw(d)) * 16)) + (colb & 15));
+    const s16x4 hi = ds_read_tr(wt + (d + 4) * 128 + ((((colb >> 4) ^ qsw(d + 4)) * 16)) + (colb & 15));
+    bf[ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  const int c = cb + wave * 16 + i;
+  for (int b0 = 0; b0 < p.B; b0 += 16) {
+    const int brow = b0 + i;
+    const uint16_t* qn = p.q_nope + ((size_t)(brow < p.B ? brow : 0) * H + h) * kNope + q * 8;
+    u32x4 a[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[ks] = brow < p.B ? ld_global_16(qn + ks * 32) : (u32x4){0u, 0u, 0u, 0u};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(as_bf16x8(a[ks]), bf[ks], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int b = b0 + q * 4 + r;
+      if (b < p.B)
+        reinterpret_cast<__bf16*>(p.q_lat)[((size_t)b * H + h) * kLatent + c] = f32_to_bf16(acc[r]);
+    }
   }
 }
 
@@ -199,11 +226,26 @@ void latent_decode_kernel(LatentParams p) {
   // i then receives dim db*16 + i of those four positions.  The position order
   // (4q..4q+3, 16+4q..16+4q+3) is the order in which the Sᵀ accumulators hold
   // them, so the weights are the B operand without any exchange.
+  // The swizzle only permutes the low 4 bits of a chunk index, so a read's
+  // address splits into a lane part (kept in a register) and a constant part
+  // (the instruction's offset): score reads of chunk 4m + j use k_lane[j] +
+  // 256m; value reads of dim block 8m + j use v_lane[j] + 256m.
   const int srow_sw = lsw(i16);  // rows i16 and 16 + i16 share the swizzle
+  int k_lane[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) k_lane[j] = i16 * L_CROW + (((j * 4 + q) ^ srow_sw) * 16);
+  int p_lane[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      p_lane[kb][c] = L_POFF + (kb * 16 + i16) * L_PROW + (((c * 4 + q) ^ psw(kb * 16 + i16)) * 16);
   const int vrow = q * 4 + (i16 >> 2);
   const int vrow_sw = lsw(vrow);
-  const int vhalf = (i16 & 1) * 8;
-  const int vsub = (i16 & 3) >> 1;
+  int v_lane[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    v_lane[j] = vrow * L_CROW + (((2 * j + ((i16 & 3) >> 1)) ^ vrow_sw) * 16) + (i16 & 1) * 8;
 
   const float cl2 = p.scale_log2;
   const uint32_t ones = 0x3f803f80u;
@@ -219,26 +261,50 @@ void latent_decode_kernel(LatentParams p) {
   for (int t = 0; t < ntiles; ++t) {
     wait_vm<(LNST - 2) * L_CPW>();
     barrier_lds();
-    copy_tile(t + LNST - 1);
     const uint8_t* st = llds + (t % LNST) * L_STAGE;
 
-    // Sᵀ for the two 16-position halves of the tile.
-    f32x4 s[2];
+    // Sᵀ for the two 16-position halves of the tile.  With one wave per SIMD
+    // nothing hides an LDS read's latency, so reads run ahead of the products:
+    // the first half's 18 key fragments are requested up front, the second
+    // half's one by one behind the first half's products.
+    auto kread = [&](int kb, int c) {
+      return c < 16 ? ds_read_16(st + k_lane[c & 3] + kb * 16 * L_CROW + (c >> 2) * 256)
+                    : ds_read_16(st + p_lane[kb][c - 16]);
+    };
+    u32x4 k0f[18], k1f[18];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint8_t* rowp = st + (kb * 16 + i16) * L_CROW;
-      const uint8_t* prow = st + L_POFF + (kb * 16 + i16) * L_PROW;
-      const int pr_sw = psw(kb * 16 + i16);
-      u32x4 kf[18];
+    for (int c = 0; c < 18; ++c) k0f[c] = kread(0, c);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int c = 0; c < 16; ++c) kf[c] = ds_read_16(rowp + (((c * 4 + q) ^ srow_sw) * 16));
-#pragma unroll
-      for (int c = 0; c < 2; ++c) kf[16 + c] = ds_read_16(prow + (((c * 4 + q) ^ pr_sw) * 16));
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 18; ++c) a = mfma16x16x32(as_bf16x8(kf[c]), qf[c], a);
-      s[kb] = a;
+    for (int c = 0; c < 18; ++c) {
+      s[0] = mfma16x16x32(as_bf16x8(k0f[c]), qf[c], s[0]);
+      k1f[c] = kread(1, c);
     }
+    // Pin the order product, read, product, read, ...: each second-half
+    // fragment takes the registers of a first-half one already consumed.
+#pragma unroll
+    for (int c = 0; c < 18; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < 18; ++c) s[1] = mfma16x16x32(as_bf16x8(k1f[c]), qf[c], s[1]);
+
+    // Value fragments, 8 dim blocks per group; the first group is requested
+    // before the softmax so its reads overlap that work.
+    bf16x8 vf[8];
+    auto vload = [&](int g) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int off = v_lane[u] + g * 256;
+        const s16x4 lo = ds_read_tr(st + off);
+        const s16x4 hi = ds_read_tr(st + off + 16 * L_CROW);
+        vf[u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    vload(0);
 
     // Online softmax (base 2) over this tile: lane holds positions
     // kb*16 + 4q + r of head hh; the other 24 are in lanes q' != q.
@@ -276,21 +342,19 @@ void latent_decode_kernel(LatentParams p) {
                                               __builtin_bit_cast(bf16x2, ones), l_run, false);
     }
     const bf16x8 pf = as_bf16x8(pk);
+    // The next copies go out here, not at the top of the step: a wave stalls
+    // until the copy engine accepts each copy, and with one wave per SIMD a
+    // stall before the score products idles the matrix core (16% slower).
+    copy_tile(t + LNST - 1);
 
-    // Oᵀ += Cᵀ·Pᵀ over the 512 latent dims, 16 at a time.
+    // Oᵀ += Cᵀ·Pᵀ over the 512 latent dims, 16 at a time; each group's reads
+    // are issued right behind the previous group's products.
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      bf16x8 vf[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int db = g * 8 + u;
-        const int off = vrow * L_CROW + (((2 * db + vsub) ^ vrow_sw) * 16) + vhalf;
-        const s16x4 lo = ds_read_tr(st + off);
-        const s16x4 hi = ds_read_tr(st + off + 16 * L_CROW);
-        vf[u] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc[g * 8 + u] = mfma16x16x32(vf[u], pf, acc[g * 8 + u]);
+      if (g + 1 < 4) vload(g + 1);
     }
   }
   wait_vm<0>();
@@ -315,50 +379,78 @@ void latent_decode_kernel(LatentParams p) {
   }
 }
 
-// Combine the split partials of one (b, h): 128 threads x 4 dims.
-__global__ __launch_bounds__(128) void latent_merge_kernel(LatentParams p) {
-  const int bh = blockIdx.x;
-  const int d = threadIdx.x * 4;
-  const int S = p.splits;
-  const float* part = p.part + (size_t)bh * S * kLatentPart;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, part[s * kLatentPart]);
-  float lt = 0.f;
-  f32x4 od = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const float ms = part[s * kLatentPart];
-    const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
-    lt = fmaf(part[s * kLatentPart + 1], w, lt);
-    od += *reinterpret_cast<const f32x4*>(part + s * kLatentPart + 8 + d) * w;
-  }
-  *reinterpret_cast<f32x4*>(p.o_lat + (size_t)bh * kLatent + d) = od * (1.f / lt);
-  if (p.lse && d == 0) p.lse[bh] = (M + log2f(lt)) * 0.69314718055994530942f;
-}
-
-// ------------------------------------------------------------------ expand --
-// out[b][h·128 + e] = Σ_c W[h·256 + 128 + e][c] · o_lat[b][h][c].  One wave per
-// 16 sequences × 16 value dims of one head; K = 512 in 16 MFMA steps; o_lat is
-// rounded to bf16 as it is loaded (RNE), the weight rows are K-contiguous.
-__global__ __launch_bounds__(256) void latent_out_kernel(LatentParams p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.x, b0 = blockIdx.y * 16, e0 = (blockIdx.z * 4 + wave) * 16;
+// ----------------------------------------------------------- merge+expand --
+// One workgroup per (head h, 16 sequences), 8 waves.  First the 16 latent
+// output rows are formed in LDS as bf16 (RNE): with splits, by the
+// log-sum-exp merge of the partials (max, sum, unnormalised output), else
+// from the normalised rows the decode kernel stored.  Then wave w computes
+// out[b][h·128 + 16w .. +15] = Σ_c W[h·256 + 128 + e][c] · o[b][c] over the
+// 512 latent dims in 16 MFMA steps; the weight rows are K-contiguous and all
+// 16 of a lane's fragments are requested before the first product.  LDS row r
+// keeps chunk x (8 dims) at x ^ r.
+__global__ __launch_bounds__(512) void latent_out_kernel(LatentParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t tile[16 * L_CROW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, b0 = blockIdx.y * 16;
+  const int H = p.H, S = p.splits;
   const int q = lane >> 4, i = lane & 15;
-  const int H = p.H;
-  const int brow = b0 + i;
-  const float* o = p.o_lat + ((size_t)(brow < p.B ? brow : 0) * H + h) * kLatent + q * 8;
+  const int e0 = wave * 16;
+
+  // Weight fragments first: their latency overlaps the merge below.
   const uint16_t* w = p.w_kv_b + ((size_t)h * 256 + kNope + e0 + i) * kLatent + q * 8;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int ks = 0; ks < kLatent / 32; ++ks) {
-    float y[8];
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(o + ks * 32);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(o + ks * 32 + 4);
+  u32x4 wf[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      y[e] = brow < p.B ? lo[e] : 0.f;
-      y[4 + e] = brow < p.B ? hi[e] : 0.f;
+  for (int ks = 0; ks < 16; ++ks) wf[ks] = ld_global_16(w + ks * 32);
+
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int item = tid + it * 512;  // 16 rows x 64 chunks of 8 dims
+    const int r = item >> 6, ch = item & 63;
+    const int b = b0 + r;
+    float y[8];
+    if (b >= p.B) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = 0.f;
+    } else if (S == 1) {
+      const float* o = p.o_lat + ((size_t)b * H + h) * kLatent + ch * 8;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(o);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(o + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[e] = lo[e];
+        y[4 + e] = hi[e];
+      }
+    } else {
+      const float* part = p.part + ((size_t)b * H + h) * S * kLatentPart;
+      float M = -INFINITY;
+      for (int sp = 0; sp < S; ++sp) M = fmaxf(M, part[sp * kLatentPart]);
+      float lt = 0.f;
+      f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+      for (int sp = 0; sp < S; ++sp) {
+        const float* ps = part + sp * kLatentPart;
+        const float ms = ps[0];
+        const float wt = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+        lt = fmaf(ps[1], wt, lt);
+        lo += *reinterpret_cast<const f32x4*>(ps + 8 + ch * 8) * wt;
+        hi += *reinterpret_cast<const f32x4*>(ps + 12 + ch * 8) * wt;
+      }
+      const float inv = 1.f / lt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[e] = lo[e] * inv;
+        y[4 + e] = hi[e] * inv;
+      }
+      if (p.lse && ch == 0) p.lse[(size_t)b * H + h] = (M + log2f(lt)) * 0.69314718055994530942f;
     }
-    acc = mfma16x16x32(pack8(y), as_bf16x8(ld_global_16(w + ks * 32)), acc);
+    *reinterpret_cast<u32x4*>(tile + r * L_CROW + ((ch ^ r) * 16)) = as_u32x4(pack8(y));
+  }
+  __syncthreads();
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(tile + i * L_CROW + (((ks * 4 + q) ^ i) * 16));
+    acc = mfma16x16x32(as_bf16x8(a), as_bf16x8(wf[ks]), acc);
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -399,12 +491,9 @@ hipError_t launch_decode_latent(const LatentParams& p, hipStream_t stream) {
   const long dblocks = (long)p.B * p.splits;
   if (dblocks <= 0 || dblocks > 0x7fffffffL || bblocks > 65535 || p.H > LW * LHW)
     return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(latent_q_kernel, dim3(p.H, (unsigned)bblocks, kLatent / 64), dim3(256), 0,
-                     stream, p);
+  hipLaunchKernelGGL(latent_q_kernel, dim3(p.H, kLatent / 64), dim3(256), 0, stream, p);
   hipLaunchKernelGGL(latent_decode_kernel, dim3((unsigned)dblocks), dim3(64 * LW), 0, stream, p);
-  if (p.splits > 1)
-    hipLaunchKernelGGL(latent_merge_kernel, dim3((unsigned)((long)p.B * p.H)), dim3(128), 0, stream, p);
-  hipLaunchKernelGGL(latent_out_kernel, dim3(p.H, (unsigned)bblocks, kV / 64), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(latent_out_kernel, dim3(p.H, (unsigned)bblocks), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
