@@ -69,6 +69,9 @@ def _load():
     lib.oracle_decode_shared_kpe_rows.restype = I
     lib.oracle_decode_latent.argtypes = [P, P, P, P, P, P, I, I, D, I, I, I, I, P, I, P, P, I]
     lib.oracle_decode_latent.restype = I
+    lib.oracle_e4m3_to_double_array.argtypes = [P, P, ctypes.c_size_t]
+    lib.oracle_dequant_fp8.argtypes = [P, P, I, I, P]
+    lib.oracle_dequant_fp8.restype = I
     lib.oracle_out_proj.argtypes = [P, P, I, I, I, P, I]
     lib.oracle_out_proj.restype = I
     lib.oracle_out_proj_rows.argtypes = [P, P, I, I, I, I, P, P, I]
@@ -306,6 +309,40 @@ def decode_latent(q_nope, q_pe, ckv, kpe, w_kv_b, R, q_pos, scale, sel=None, rou
     if rc:
         raise ValueError(f"oracle_decode_latent failed ({rc})")
     return out, lse
+
+
+def e4m3_to_double(b):
+    """Exact values of e4m3 ("fn") bytes; NaN for the NaN codes."""
+    lib = _load()
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    out = np.empty(b.shape, dtype=np.float64)
+    lib.oracle_e4m3_to_double_array(_p(b), _p(out), b.size)
+    return out
+
+
+def dequant_fp8(w8, scale):
+    """bf16 bits [N,K] of the dequantized weight: float32(e4m3 value x block
+    scale), rounded to bf16; w8 [N,K] uint8, scale [ceil(N/128), ceil(K/128)]."""
+    lib = _load()
+    w8 = np.ascontiguousarray(w8, dtype=np.uint8)
+    scale = _f32(scale)
+    N, K = w8.shape
+    if scale.shape != ((N + 127) // 128, (K + 127) // 128):
+        raise ValueError("scale must be [ceil(N/128), ceil(K/128)]")
+    out = np.empty((N, K), dtype=np.uint16)
+    if lib.oracle_dequant_fp8(_p(w8), _p(scale), N, K, _p(out)):
+        raise ValueError("oracle_dequant_fp8 failed")
+    return out
+
+
+def out_proj_fp8(x, w8, scale, nthreads=None):
+    """y = x · dequant(w8, scale)ᵀ: the projection with the FP8 checkpoint
+    weight, dequantized to bf16 first; returns y [M,N] double."""
+    return out_proj(x, dequant_fp8(w8, scale), nthreads)
+
+
+def out_proj_fp8_rows(x, w8, scale, rows, nthreads=None):
+    return out_proj_rows(x, dequant_fp8(w8, scale), rows, nthreads)
 
 
 def out_proj(x, w, nthreads=None):

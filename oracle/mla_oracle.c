@@ -605,3 +605,39 @@ int oracle_out_proj_rows(const uint16_t *x, const uint16_t *w, int M, int K, int
   oproj_ctx c = {x, w, M, K, N, rows, y};
   return run_units(oproj_unit, &c, (long)n_rows, (size_t)K, nthreads);
 }
+
+/* ----------------------------------------------------------- fp8 weights ---- */
+
+/* The checkpoint stores projection weights in FP8 with one float32 scale per
+ * 128 x 128 block (page "Kimi K2 · Transformer blocks" and "Kimi K2 · Mix and
+ * project": parameter counts exclude the FP8 block scales).  The format is
+ * e4m3 of the OCP "fn" variant: sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, no infinities, S.1111.111 is NaN, largest finite value 448.
+ * Decoded exactly to double. */
+double oracle_e4m3_to_double(uint8_t b) {
+  const int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  if (e == 15 && m == 7) return NAN;
+  /* normal: (1 + m/8) 2^(e-7) = (8 + m) 2^(e-10); subnormal: (m/8) 2^-6 = m 2^-9 */
+  const double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+void oracle_e4m3_to_double_array(const uint8_t *b, double *out, size_t n) {
+  for (size_t i = 0; i < n; i++) out[i] = oracle_e4m3_to_double(b[i]);
+}
+
+/* Dequantized weight (reading of the checkpoint format for a bf16 model): the
+ * fp8 value times its block's scale, computed in float32 (the exact product
+ * fits a double, so one rounding to float32), then rounded to bf16.
+ * w8 [N][K], scale [ceil(N/128)][ceil(K/128)], out [N][K] bf16 bits. */
+int oracle_dequant_fp8(const uint8_t *w8, const float *scale, int N, int K, uint16_t *out) {
+  if (N <= 0 || K <= 0) return 1;
+  const int KB = (K + 127) / 128;
+  for (long n = 0; n < N; n++)
+    for (long k = 0; k < K; k++) {
+      const float s = scale[(n / 128) * KB + k / 128];
+      const float prod = (float)(oracle_e4m3_to_double(w8[n * K + k]) * (double)s);
+      out[n * K + k] = bf16_bits((double)prod);
+    }
+  return 0;
+}

@@ -481,6 +481,53 @@ def test_decode_rows_equal_full():
         assert rl[i] == lse[b, h]
 
 
+# ------------------------------------------------------------ fp8 weights
+
+def test_e4m3_decode_matches_torch():
+    """Every byte value decodes to torch's float8_e4m3fn value (NaN codes too)."""
+    b = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(b.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_to_double(b)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_dequant_fp8_matches_torch_and_block_layout():
+    """Dequantization equals torch's float32 product of the e4m3 value and its
+    block's scale, rounded to bf16, bit for bit; ragged N and K; and a scale
+    change in one block moves exactly that block."""
+    N, K = 300, 384
+    g = torch.Generator().manual_seed(1800)
+    w8 = (torch.randn((N, K), generator=g) * 60).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    scale = (torch.rand((3, 3), generator=g) * 1e-3 + 1e-4).to(torch.float32)
+    s_full = scale.repeat_interleave(128, 0).repeat_interleave(128, 1)[:N, :K]
+    want = (torch.from_numpy(w8.copy()).view(torch.float8_e4m3fn).to(torch.float32) * s_full)
+    want = inputs.bits(want.to(torch.bfloat16))
+    got = oracle.dequant_fp8(w8, scale.numpy())
+    assert np.array_equal(got, want)
+    s2 = scale.clone()
+    s2[1, 2] *= 2
+    got2 = oracle.dequant_fp8(w8, s2.numpy())
+    diff = got2 != got
+    assert not diff[:128].any() and not diff[256:].any() and not diff[128:256, :256].any()
+    assert diff[128:256, 256:].any()
+
+
+def test_out_proj_fp8_input_recipe():
+    """The FP8 weight recipe reproduces the bf16 weight to e4m3 precision
+    (relative error below 2^-4 of each block's largest element)."""
+    N, K = 256, 256
+    w = inputs.out_proj_weight(N, K, workload=3).float().numpy()
+    w8, scale = inputs.out_proj_weight_fp8(N, K, workload=3)
+    deq = widen(oracle.dequant_fp8(w8.numpy(), scale.numpy()))
+    for nb in range(2):
+        for kb in range(2):
+            blk = np.s_[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128]
+            assert np.max(np.abs(deq[blk] - w[blk])) <= np.max(np.abs(w[blk])) * 2.0 ** -4
+
+
 # ------------------------------------------------------------------- o_proj
 
 def test_out_proj_matches_float64_matmul():

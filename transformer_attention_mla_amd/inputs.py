@@ -175,6 +175,26 @@ def out_proj_weight(N: int = D_MODEL, K: int = 64 * 128, workload: int = 0, devi
     return normal_bf16((N, K), seed_of(workload, SEED_WO), std=0.02, device=device)
 
 
+def out_proj_weight_fp8(N: int = D_MODEL, K: int = 64 * 128, workload: int = 0, device="cpu"):
+    """The o_proj weight in the checkpoint's FP8 form: the bf16 N(0, 0.02)
+    weight of out_proj_weight, one float32 scale per 128 x 128 block (block
+    amax / 448, the largest e4m3 value), values divided by their scale and
+    converted to e4m3 ("fn") by torch.  Returns (w8 uint8 [N,K], scale float32
+    [ceil(N/128), ceil(K/128)])."""
+    import torch
+
+    w = out_proj_weight(N, K, workload, device).float()
+    NB, KB = (N + 127) // 128, (K + 127) // 128
+    pad = torch.zeros((NB * 128, KB * 128), dtype=torch.float32, device=w.device)
+    pad[:N, :K] = w
+    blocks = pad.view(NB, 128, KB, 128)
+    amax = blocks.abs().amax(dim=(1, 3))
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (blocks / scale[:, None, :, None]).view(NB * 128, KB * 128)[:N, :K]
+    w8 = q.contiguous().to(torch.float8_e4m3fn).view(torch.uint8)
+    return w8, scale.contiguous()
+
+
 def bits(t) -> np.ndarray:
     """uint16 bit patterns of a bf16 tensor (on the host)."""
     import torch
