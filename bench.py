@@ -251,6 +251,41 @@ def decode_latent_figures(mla, inputs, scale, dev, calls=20):
             "traffic": measured_traffic("latent_decode_kernel")}
 
 
+def oproj_fp8_figures(mla, inputs, dev, calls=20):
+    """o_proj with the FP8 checkpoint weight ([7168, 8192] e4m3 + float32 block
+    scales, dequantized to bf16 as it is loaded), at M = 64 (decode) and M =
+    16384 (prefill): median time, GB/s on x + w8 + scales + y, TFLOP/s."""
+    import torch
+
+    K, N = 64 * 128, inputs.D_MODEL
+    w8, sc = inputs.out_proj_weight_fp8(N, K, workload=3, device=dev)
+    res = {}
+    for M in (64, 16384):
+        print(f"o_proj fp8 M={M}", file=sys.stderr, flush=True)
+        x = inputs.normal_bf16((M, K), 90 + M, device=dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(16, mla.mla_out_proj_fp8_workspace_bytes(M, K, N)), dtype=torch.uint8,
+                         device=dev)
+        f = lambda: mla.mla_out_proj_fp8(x, w8, sc, y=y, workspace=ws)
+        for _ in range(3):
+            f()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(calls)]
+        for a, b in ev:
+            a.record()
+            f()
+            b.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)[calls // 2]
+        nb = M * K * 2 + N * K + sc.numel() * 4 + M * N * 2
+        res[f"M{M}"] = {"ms": t, "gbps": nb / t / 1e6, "tflops": oproj_flops(M, K, N) / t / 1e9,
+                        "bytes": nb}
+        del x, y, ws
+    del w8, sc
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -411,6 +446,7 @@ def main():
     if do_d and not args.no_other_configs:
         res["decode_shared_kpe"] = decode_shared_kpe_figures(mla, inputs, scale, dev)
         res["decode_latent"] = decode_latent_figures(mla, inputs, scale, dev)
+        res["oproj_fp8"] = oproj_fp8_figures(mla, inputs, dev)
 
     if do_p and not args.no_cpu_baseline:
         print("cpu baseline", file=sys.stderr, flush=True)

@@ -217,6 +217,27 @@ size_t mla_out_proj_workspace_bytes(int M, int K, int N);
 int mla_out_proj(const mla_bf16 *x, const mla_bf16 *w_o, void *y, int M, int K, int N,
                  void *workspace, size_t workspace_bytes, uint32_t flags, void *stream);
 
+/* The same projection with the weight as the checkpoint stores it: FP8 values
+ * with one float32 scale per 128 x 128 block (pages "Kimi K2 · Transformer
+ * blocks" and "Kimi K2 · Mix and project": the parameter counts exclude the
+ * FP8 block scales).  Each weight element is dequantized as the float32
+ * product of its e4m3 value and its block's scale, rounded to bf16; then
+ * y = x · w_oᵀ as in mla_out_proj.  The weight stream is half as large, which is
+ * what bounds the projection at decode sizes.
+ *
+ *   w8       [N, K]                       uint8  e4m3 (OCP "fn": bias 7, no
+ *                                                infinities, 0x7f/0xff NaN)
+ *   w_scale  [ceil(N/128), K/128]         float  block scales, row-major
+ *   workspace >= mla_out_proj_fp8_workspace_bytes(M, K, N) bytes
+ *   (x, y, M, K, N, flags, stream and the errors as for mla_out_proj; w8 or
+ *   w_scale NULL is MLA_ERR_NULL, misaligned MLA_ERR_ALIGN)
+ */
+size_t mla_out_proj_fp8_workspace_bytes(int M, int K, int N);
+
+int mla_out_proj_fp8(const mla_bf16 *x, const uint8_t *w8, const float *w_scale, void *y, int M,
+                     int K, int N, void *workspace, size_t workspace_bytes, uint32_t flags,
+                     void *stream);
+
 #ifdef __cplusplus
 }
 #endif

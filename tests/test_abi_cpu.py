@@ -176,6 +176,31 @@ def test_decode_latent_rejects(kw, code):
     assert latent(**kw) == code
 
 
+def oproj8(**kw):
+    a = dict(x=A[0], w8=A[1], s=A[2], y=A[3], M=16384, K=8192, N=7168, ws=None, ws_bytes=0, flags=0)
+    a.update(kw)
+    return mla.lib().mla_out_proj_fp8(a["x"], a["w8"], a["s"], a["y"], a["M"], a["K"], a["N"],
+                                      a["ws"], a["ws_bytes"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w8=None), NULL), (dict(s=None), NULL), (dict(y=None), NULL),
+    (dict(flags=8), FLAGS),
+    (dict(M=0), DIM), (dict(K=100), DIM),
+    (dict(M=64), WORKSPACE),
+    (dict(s=ctypes.c_void_p(3 * 16 * GB + 4)), ALIGN),
+    (dict(y=ctypes.c_void_p(3 * 16 * GB + 16)), ALIAS),  # y over the scales
+])
+def test_oproj_fp8_rejects(kw, code):
+    assert oproj8(**kw) == code
+
+
+def test_oproj_fp8_workspace():
+    assert mla.mla_out_proj_fp8_workspace_bytes(64, 8192, 7168) > 0      # split K
+    assert mla.mla_out_proj_fp8_workspace_bytes(16384, 8192, 7168) == 0  # enough tiles
+    assert mla.mla_out_proj_fp8_workspace_bytes(64, 100, 7168) == 0
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), NULL), (dict(w=None), NULL), (dict(y=None), NULL),
     (dict(flags=8), FLAGS),

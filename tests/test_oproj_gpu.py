@@ -100,3 +100,60 @@ def test_attention_then_oproj_workload1(gpu_device):
     # o_proj alone on the GPU's own bf16 attention output
     want_chain = oracle.out_proj(bits(attn.view(B * T, H * 128)), bits(wo))
     check_close(to_host64(y32), want_chain, 1e-3, "o_proj on the GPU's attention output")
+
+
+# ------------------------------------------------------------- FP8 weights
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (17, 256, 100), (64, 8192, 7168), (130, 1024, 300),
+                                   (300, 384, 129), (1000, 512, 1000)])
+def test_oproj_fp8_parity(M, K, N, gpu_device):
+    """The FP8 checkpoint weight, dequantized to bf16 in the kernel's load path:
+    against the oracle's projection with the same dequantization."""
+    say(f"o_proj fp8 parity M={M} K={K} N={N}")
+    x = inputs.normal_bf16((M, K), 30 + M)
+    w8, sc = inputs.out_proj_weight_fp8(N, K, workload=1)
+    want = oracle.out_proj_fp8(bits(x), w8.numpy(), sc.numpy())
+    xg, wg, sg = x.to(gpu_device), w8.to(gpu_device), sc.to(gpu_device)
+    y32 = mla.mla_out_proj_fp8(xg, wg, sg, out_f32=True)
+    y16 = mla.mla_out_proj_fp8(xg, wg, sg)
+    torch.cuda.synchronize()
+    check_close(to_host64(y32), want, TOL, "float32 output vs oracle")
+    check_bf16_is_rne_of_f32(y16, y32)
+    check_bf16_close(y16, want, "bf16 output vs oracle")
+
+
+def test_oproj_fp8_dequant_exact(gpu_device):
+    """Scaled identity: w8 = 1.0 (0x38) on the diagonal, scale 2^-3 in every
+    block, so y = x / 8 bit for bit -- the dequantized weight is exactly 0.125
+    and zero elsewhere, each output one product; and a second block scale
+    pattern (a power of two per block) moves each output by its block's scale."""
+    M, K, N = 70, 1024, 600
+    x = inputs.normal_bf16((M, K), 7)
+    w8 = torch.zeros((N, K), dtype=torch.uint8)
+    w8[torch.arange(N), torch.arange(N)] = 0x38
+    NB, KB = (N + 127) // 128, K // 128
+    sc = torch.full((NB, KB), 0.125, dtype=torch.float32)
+    y = mla.mla_out_proj_fp8(x.to(gpu_device), w8.to(gpu_device), sc.to(gpu_device))
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu(), (x[:, :N].float() * 0.125).to(torch.bfloat16))
+    sc2 = 2.0 ** -torch.arange(NB * KB, dtype=torch.float32).reshape(NB, KB)
+    y2 = mla.mla_out_proj_fp8(x.to(gpu_device), w8.to(gpu_device), sc2.to(gpu_device), out_f32=True)
+    torch.cuda.synchronize()
+    n = torch.arange(N)
+    want = x[:, :N].float() * sc2[n // 128, n // 128]
+    assert torch.equal(y2.cpu(), want)
+
+
+def test_oproj_fp8_large_sampled(gpu_device):
+    """M = 16384, K = 8192, N = 7168 (the prefill projection) on sampled rows."""
+    M, K, N = 16384, 8192, 7168
+    say(f"o_proj fp8 sampled M={M}")
+    x = inputs.normal_bf16((M, K), 78, device=gpu_device)
+    w8, sc = inputs.out_proj_weight_fp8(N, K, workload=3, device=gpu_device)
+    y32 = mla.mla_out_proj_fp8(x, w8, sc, out_f32=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 20)])).astype(np.int32)
+    want = oracle.out_proj_fp8_rows(bits(x), w8.cpu().numpy(), sc.cpu().numpy(), rows)
+    got = to_host64(y32[torch.from_numpy(rows).long().to(gpu_device)])
+    check_close(got, want, TOL, f"{len(rows)} sampled rows")

@@ -18,7 +18,7 @@ __all__ = [
     "mla_prefill_workspace_bytes", "mla_attend_prefill", "mla_decode_splits",
     "mla_decode_workspace_bytes", "mla_attend_decode", "mla_attend_decode_shared_kpe",
     "mla_decode_latent_workspace_bytes", "mla_attend_decode_latent",
-    "mla_out_proj_workspace_bytes",
+    "mla_out_proj_workspace_bytes", "mla_out_proj_fp8_workspace_bytes", "mla_out_proj_fp8",
     "mla_out_proj", "NOPE", "ROPE", "VDIM", "PAIRS",
 ]
 
@@ -73,6 +73,10 @@ def lib():
     L.mla_out_proj_workspace_bytes.argtypes = [I, I, I]
     L.mla_out_proj_workspace_bytes.restype = Z
     L.mla_out_proj.argtypes = [P, P, P, I, I, I, P, Z, U, P]
+    L.mla_out_proj_fp8_workspace_bytes.argtypes = [I, I, I]
+    L.mla_out_proj_fp8_workspace_bytes.restype = Z
+    L.mla_out_proj_fp8.argtypes = [P, P, P, P, I, I, I, P, Z, U, P]
+    L.mla_out_proj_fp8.restype = I
     L.mla_out_proj.restype = I
     _lib = L
     return L
@@ -96,6 +100,10 @@ def mla_decode_splits(B: int, H: int, L: int, num_splits: int = 0) -> int:
 
 def mla_decode_workspace_bytes(B: int, H: int, L: int, num_splits: int = 0) -> int:
     return lib().mla_decode_workspace_bytes(B, H, L, num_splits)
+
+
+def mla_out_proj_fp8_workspace_bytes(M: int, K: int, N: int) -> int:
+    return lib().mla_out_proj_fp8_workspace_bytes(M, K, N)
 
 
 def mla_decode_latent_workspace_bytes(B: int, H: int, L: int, num_splits: int = 0) -> int:
@@ -332,4 +340,28 @@ def mla_out_proj(x, w_o, *, y=None, out_f32=False, workspace=None, stream=None):
                             MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
     if rc:
         raise MlaError(rc, "mla_out_proj")
+    return y
+
+
+def mla_out_proj_fp8(x, w8, w_scale, *, y=None, out_f32=False, workspace=None, stream=None):
+    """y = x · dequant(w8, w_scale)ᵀ with x [M,K] bf16, w8 [N,K] uint8 (e4m3)
+    and w_scale [ceil(N/128), K/128] float32 block scales.  Returns y [M,N]."""
+    torch = _torch()
+    if x.dim() != 2 or w8.dim() != 2:
+        raise ValueError("x must be [M, K] and w8 [N, K]")
+    M, K = x.shape
+    N = w8.shape[0]
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (M, K), dev)
+    _check(w8, "w8", torch.uint8, (N, K), dev)
+    _check(w_scale, "w_scale", torch.float32, ((N + 127) // 128, (K + 127) // 128), dev)
+    odt = torch.float32 if out_f32 else torch.bfloat16
+    if y is None:
+        y = torch.empty((M, N), dtype=odt, device=dev)
+    _check(y, "y", odt, (M, N), dev)
+    workspace, ws_bytes = _workspace(workspace, mla_out_proj_fp8_workspace_bytes(M, K, N), dev)
+    rc = lib().mla_out_proj_fp8(_ptr(x), _ptr(w8), _ptr(w_scale), _ptr(y), M, K, N, _ptr(workspace),
+                                ws_bytes, MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_out_proj_fp8")
     return y

@@ -368,6 +368,51 @@ int mla_out_proj(const mla_bf16* x, const mla_bf16* w_o, void* y, int M, int K, 
   p.splits = splits;
   p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
   p.group_m = 0;  // kernel default
+  p.w8 = nullptr;
+  p.w_scale = nullptr;
+  (void)hipGetLastError();
+  if (mla::launch_oproj(p, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+size_t mla_out_proj_fp8_workspace_bytes(int M, int K, int N) {
+  if (!dims_ok(M, K, N, 1) || K % 128 != 0) return 0;
+  return oproj_ws_bytes(M, N, mla::oproj_choose_splits(M, K, N, true));
+}
+
+int mla_out_proj_fp8(const mla_bf16* x, const uint8_t* w8, const float* w_scale, void* y, int M,
+                     int K, int N, void* workspace, size_t workspace_bytes, uint32_t flags,
+                     void* stream) {
+  if (!x || !w8 || !w_scale || !y) return MLA_ERR_NULL;
+  if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
+  if (!dims_ok(M, K, N, 1) || K % 128 != 0 || (long long)M * N > kMaxElems) return MLA_ERR_DIM;
+  const int splits = mla::oproj_choose_splits(M, K, N, true);
+  const size_t need = oproj_ws_bytes(M, N, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w8) || !aligned16(w_scale) || !aligned16(y) ||
+      !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  const size_t out_elt = (flags & MLA_OUT_F32) ? 4 : 2;
+  const size_t nb = (size_t)(N + 127) / 128, kb = (size_t)K / 128;
+  const Range in[] = {{x, (size_t)M * K * 2}, {w8, (size_t)N * K}, {w_scale, nb * kb * 4}};
+  const Range outs[] = {{y, (size_t)M * N * out_elt}, {need ? workspace : nullptr, need}};
+  if (any_alias(in, 3, outs, 2)) return MLA_ERR_ALIAS;
+  const int dev = check_device();
+  if (dev != MLA_OK) return dev;
+
+  mla::OprojParams p;
+  p.x = x;
+  p.w = nullptr;
+  p.w8 = w8;
+  p.w_scale = w_scale;
+  p.y = y;
+  p.part = static_cast<float*>(need ? workspace : nullptr);
+  p.M = M;
+  p.K = K;
+  p.N = N;
+  p.splits = splits;
+  p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
+  p.group_m = 0;
   (void)hipGetLastError();
   if (mla::launch_oproj(p, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_LAUNCH;
   return MLA_OK;

@@ -121,9 +121,11 @@ struct OprojParams {
   int splits;
   int out_f32;
   int group_m;        // wide kernel: m-tiles per group of the tile order
+  const uint8_t* w8;      // FP8 weight [N][K] (e4m3) instead of w, or null
+  const float* w_scale;   // its float32 scales, [ceil(N/128)][ceil(K/128)]
 };
 
-int oproj_choose_splits(int M, int K, int N);
+int oproj_choose_splits(int M, int K, int N, bool fp8 = false);
 hipError_t launch_oproj(const OprojParams& p, hipStream_t stream);
 
 }  // namespace mla

@@ -44,6 +44,23 @@ constexpr int OTM = OBM / OWM / 32;  // along m
 // consecutive rows and for same-parity rows among 16 consecutive ones.
 __device__ __forceinline__ int rswz(int row) { return (row ^ (row >> 3)) & 7; }
 
+// FP8 weights (e4m3, OCP "fn" variant, as the checkpoint stores them with one
+// float32 scale per 128 x 128 block): 8 values, the float32 product with the
+// block scale rounded to bf16 -- the bf16 weight the projection multiplies.
+__device__ __forceinline__ u32x4 dequant8(u32x2 raw, float s) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int w = (int)(uint32_t)raw[h];
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);  // bytes 0, 1
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);   // bytes 2, 3
+    r[2 * h] = pack_bf16x2(lo[0] * s, lo[1] * s);
+    r[2 * h + 1] = pack_bf16x2(hi[0] * s, hi[1] * s);
+  }
+  return r;
+}
+
+template <bool FP8>
 __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sW[OBN * OBK];
   __shared__ __attribute__((aligned(16))) uint16_t sX[OBM * OBK];
@@ -67,6 +84,9 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
   constexpr int WCH = OBN * 8 / ONT;  // 16-byte chunks per thread per slab
   constexpr int XCH = OBM * 8 / ONT;
   u32x4 rw[WCH], rx[XCH];
+  u32x2 rw8[FP8 ? WCH : 1];
+  float rs[FP8 ? WCH : 1];
+  const int KB = (K + 127) / 128;
 
   auto load = [&](int k0) {
 #pragma unroll
@@ -74,7 +94,12 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
       const int c = tid + i * ONT;
       const int row = c >> 3, ch = c & 7;
       const int n = min(n0 + row, N - 1);
-      rw[i] = ld_global_16(p.w + (size_t)n * K + k0 + ch * 8);
+      if constexpr (FP8) {
+        rw8[i] = ld_global_8(p.w8 + (size_t)n * K + k0 + ch * 8);
+        rs[i] = p.w_scale[(n >> 7) * KB + ((k0 + ch * 8) >> 7)];
+      } else {
+        rw[i] = ld_global_16(p.w + (size_t)n * K + k0 + ch * 8);
+      }
     }
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
@@ -93,6 +118,7 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
     for (int i = 0; i < WCH; ++i) {
       const int c = tid + i * ONT;
       const int row = c >> 3, ch = c & 7;
+      if constexpr (FP8) rw[i] = dequant8(rw8[i], rs[i]);
       *reinterpret_cast<u32x4*>(sW + row * OBK + ((ch ^ rswz(row)) * 8)) = rw[i];
     }
 #pragma unroll
@@ -372,8 +398,8 @@ static bool oproj_use_wide(int M, int K, int N) {
   return wide_tiles >= 256 && (long long)K * 2 * WBM < 0x7fffffffLL;
 }
 
-int oproj_choose_splits(int M, int K, int N) {
-  if (oproj_use_wide(M, K, N)) return 1;
+int oproj_choose_splits(int M, int K, int N, bool fp8) {
+  if (!fp8 && oproj_use_wide(M, K, N)) return 1;
   const long tiles = (long)((M + OBM - 1) / OBM) * ((N + OBN - 1) / OBN);
   const int slabs = K / OBK;
   if (tiles >= 256 || slabs <= 1) return 1;
@@ -390,7 +416,7 @@ int oproj_choose_splits(int M, int K, int N) {
 
 hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
   OprojParams p = p_in;
-  if (p.splits == 1 && oproj_use_wide(p.M, p.K, p.N)) {
+  if (!p.w8 && p.splits == 1 && oproj_use_wide(p.M, p.K, p.N)) {
     const long wide_tiles = (long)((p.M + WBM - 1) / WBM) * ((p.N + WBN - 1) / WBN);
     if (wide_tiles > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (p.group_m <= 0) p.group_m = WGROUP_M;
@@ -400,7 +426,10 @@ hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
   const long tiles = (long)((p.M + OBM - 1) / OBM) * ((p.N + OBN - 1) / OBN);
   if (tiles <= 0 || tiles > 0x7fffffffL || p.splits < 1 || p.splits > 65535)
     return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(oproj_kernel, dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
+  if (p.w8)
+    hipLaunchKernelGGL(oproj_kernel<true>, dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
+  else
+    hipLaunchKernelGGL(oproj_kernel<false>, dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const size_t total = (size_t)p.M * p.N;
