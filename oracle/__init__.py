@@ -72,6 +72,10 @@ def _load():
     lib.oracle_e4m3_to_double_array.argtypes = [P, P, ctypes.c_size_t]
     lib.oracle_dequant_fp8.argtypes = [P, P, I, I, P]
     lib.oracle_dequant_fp8.restype = I
+    lib.oracle_append_kv.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, P]
+    lib.oracle_append_kv.restype = I
+    lib.oracle_prefill_chunk.argtypes = [P, P, P, P, P, P, I, I, D, I, I, I, I, P, P, I]
+    lib.oracle_prefill_chunk.restype = I
     lib.oracle_out_proj.argtypes = [P, P, I, I, I, P, I]
     lib.oracle_out_proj.restype = I
     lib.oracle_out_proj_rows.argtypes = [P, P, I, I, I, I, P, P, I]
@@ -343,6 +347,51 @@ def out_proj_fp8(x, w8, scale, nthreads=None):
 
 def out_proj_fp8_rows(x, w8, scale, rows, nthreads=None):
     return out_proj_rows(x, dequant_fp8(w8, scale), rows, nthreads)
+
+
+def append_kv(k_nope, k_pe, v, R, past, k_nope_cache, kpe_cache, v_cache):
+    """Write a chunk's keys and values into the shared-rotary cache layout at
+    rows past .. past+T-1 (rope key rotated at its position, bf16).  k_nope
+    [B,H,T,128], k_pe [B,1,T,64] or [B,T,64], v [B,H,T,128]; the caches
+    (k_nope_cache [B,H,Lc,128], kpe_cache [B,Lc,64], v_cache [B,H,Lc,128]) are
+    uint16 arrays updated in place."""
+    lib = _load()
+    k_nope, v = _u16(k_nope), _u16(v)
+    k_pe = _u16(k_pe).reshape(k_nope.shape[0], -1, 64)
+    R = _f32(R)
+    B, H, T, _ = k_nope.shape
+    Lc = k_nope_cache.shape[2]
+    for a in (k_nope_cache, kpe_cache, v_cache):
+        if a.dtype != np.uint16 or not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("caches must be contiguous uint16 arrays")
+    if k_nope_cache.shape != (B, H, Lc, 128) or kpe_cache.shape != (B, Lc, 64) or \
+            v_cache.shape != (B, H, Lc, 128) or k_pe.shape != (B, T, 64) or v.shape != (B, H, T, 128):
+        raise ValueError("append_kv shapes")
+    if lib.oracle_append_kv(_p(k_nope), _p(k_pe), _p(v), _p(R), R.shape[0], int(past), B, H, T, Lc,
+                            _p(k_nope_cache), _p(kpe_cache), _p(v_cache)):
+        raise ValueError("oracle_append_kv failed")
+
+
+def prefill_chunk(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, past, scale, nthreads=None):
+    """Chunked prefill: queries [B,H,T,·] at positions past .. past+T-1 against
+    cache rows 0 .. past+t.  Returns out [B,T,H*128] and lse [B,H,T]."""
+    lib = _load()
+    q_nope, q_pe, k_nope_cache, kpe_cache, v_cache = map(
+        _u16, (q_nope, q_pe, k_nope_cache, kpe_cache, v_cache))
+    R = _f32(R)
+    B, H, T, _ = q_nope.shape
+    Lc = k_nope_cache.shape[2]
+    if q_pe.shape != (B, H, T, 64) or k_nope_cache.shape != (B, H, Lc, 128) or \
+            kpe_cache.shape != (B, Lc, 64) or v_cache.shape != (B, H, Lc, 128):
+        raise ValueError("prefill_chunk shapes")
+    out = np.empty((B, T, H * 128), dtype=np.float64)
+    lse = np.empty((B, H, T), dtype=np.float64)
+    rc = lib.oracle_prefill_chunk(_p(q_nope), _p(q_pe), _p(k_nope_cache), _p(kpe_cache),
+                                  _p(v_cache), _p(R), R.shape[0], int(past), float(scale), B, H, T,
+                                  Lc, _p(out), _p(lse), nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_prefill_chunk failed ({rc})")
+    return out, lse
 
 
 def out_proj(x, w, nthreads=None):

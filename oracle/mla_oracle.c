@@ -641,3 +641,84 @@ int oracle_dequant_fp8(const uint8_t *w8, const float *scale, int N, int K, uint
     }
   return 0;
 }
+
+/* ------------------------------------------------ chunked prefill, append ---- */
+
+/* Page "Kimi K2 · Transformer blocks", model-body excerpt: positions of a new
+ * chunk continue from the cached length (position_ids = past .. past+T-1) and
+ * the causal mask is built with that past length; page "Kimi K2 · Mix and
+ * project", excerpt "mla-prefill": the cache is updated with the new keys after
+ * the rotary step, and the scores run over every cached and new key.  Query t
+ * of the chunk (position past + t) sees keys 0 .. past + t.
+ *
+ * Append: the new chunk's keys and values go to rows past .. past+T-1 of the
+ * shared-rotary cache layout; the rope key is rotated at its position and
+ * rounded to bf16 (R1).  k_nope [B][H][T][128], k_pe [B][T][64] (unrotated),
+ * v [B][H][T][128]; caches k_nope_cache [B][H][Lc][128], kpe_cache [B][Lc][64],
+ * v_cache [B][H][Lc][128]. */
+int oracle_append_kv(const uint16_t *k_nope, const uint16_t *k_pe, const uint16_t *v,
+                     const float *R, int r_rows, int past, int B, int H, int T, int Lc,
+                     uint16_t *k_nope_cache, uint16_t *kpe_cache, uint16_t *v_cache) {
+  if (B <= 0 || H <= 0 || T <= 0 || past < 0 || past + T > Lc || past + T > r_rows) return 1;
+  for (long b = 0; b < B; b++)
+    for (long h = 0; h < H; h++)
+      for (long t = 0; t < T; t++) {
+        memcpy(k_nope_cache + ((b * H + h) * Lc + past + t) * OR_NOPE,
+               k_nope + ((b * H + h) * T + t) * OR_NOPE, OR_NOPE * sizeof(uint16_t));
+        memcpy(v_cache + ((b * H + h) * Lc + past + t) * OR_VDIM,
+               v + ((b * H + h) * T + t) * OR_VDIM, OR_VDIM * sizeof(uint16_t));
+      }
+  for (long b = 0; b < B; b++)
+    for (long t = 0; t < T; t++) {
+      double x[OR_ROPE], y[OR_ROPE];
+      for (int d = 0; d < OR_ROPE; d++) x[d] = widen(k_pe[(b * T + t) * OR_ROPE + d]);
+      oracle_rotate_row(x, R + (size_t)(past + t) * OR_PAIRS, y);
+      for (int d = 0; d < OR_ROPE; d++) kpe_cache[(b * Lc + past + t) * OR_ROPE + d] = bf16_bits(y[d]);
+    }
+  return 0;
+}
+
+typedef struct {
+  const uint16_t *q_nope, *q_pe, *k_nope_cache, *kpe_cache, *v_cache;
+  const float *R;
+  int past;
+  double scale;
+  int B, H, T, Lc;
+  double *out, *lse;
+} chunk_ctx;
+
+static void chunk_unit(void *vctx, long unit, double *scratch) {
+  chunk_ctx *c = (chunk_ctx *)vctx;
+  const long t = unit % c->T, bh = unit / c->T;
+  const long b = bh / c->H, h = bh % c->H;
+  const long nk = c->past + t + 1; /* keys 0 .. past + t */
+  double qn[OR_NOPE], qpe[OR_ROPE], qr[OR_ROPE], o[OR_VDIM], l;
+  const long qrow = bh * c->T + t;
+  for (int d = 0; d < OR_NOPE; d++) qn[d] = widen(c->q_nope[qrow * OR_NOPE + d]);
+  for (int d = 0; d < OR_ROPE; d++) qpe[d] = widen(c->q_pe[qrow * OR_ROPE + d]);
+  oracle_rotate_row(qpe, c->R + (size_t)(c->past + t) * OR_PAIRS, qr);
+  for (int d = 0; d < OR_ROPE; d++) qr[d] = oracle_bf16_round(qr[d]);
+  double *kr = scratch + nk;
+  const uint16_t *kp = c->kpe_cache + b * c->Lc * OR_ROPE;
+  for (long j = 0; j < nk; j++)
+    for (int d = 0; d < OR_ROPE; d++) kr[j * OR_ROPE + d] = widen(kp[j * OR_ROPE + d]);
+  rows_t kn = {c->k_nope_cache + bh * c->Lc * OR_NOPE, OR_NOPE};
+  rows_t vv = {c->v_cache + bh * c->Lc * OR_VDIM, OR_VDIM};
+  attend_row(qn, qr, kn, kr, OR_ROPE, vv, nk, c->scale, scratch, o, &l);
+  double *dst = c->out + ((size_t)b * c->T + t) * ((size_t)c->H * OR_VDIM) + (size_t)h * OR_VDIM;
+  for (int d = 0; d < OR_VDIM; d++) dst[d] = o[d];
+  if (c->lse) c->lse[qrow] = l;
+}
+
+/* Chunked prefill over the cache: q_nope [B][H][T][128], q_pe [B][H][T][64]
+ * (unrotated, rotated at past + t); caches as for oracle_append_kv, holding
+ * rows 0 .. past+T-1 (the chunk's own keys already appended); out
+ * [B][T][H*128], lse [B][H][T] or NULL. */
+int oracle_prefill_chunk(const uint16_t *q_nope, const uint16_t *q_pe, const uint16_t *k_nope_cache,
+                         const uint16_t *kpe_cache, const uint16_t *v_cache, const float *R,
+                         int r_rows, int past, double scale, int B, int H, int T, int Lc,
+                         double *out, double *lse, int nthreads) {
+  if (B <= 0 || H <= 0 || T <= 0 || past < 0 || past + T > Lc || past + T > r_rows) return 1;
+  chunk_ctx c = {q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, past, scale, B, H, T, Lc, out, lse};
+  return run_units(chunk_unit, &c, (long)B * H * T, (size_t)(past + T) * (1 + OR_ROPE), nthreads);
+}

@@ -481,6 +481,69 @@ def test_decode_rows_equal_full():
         assert rl[i] == lse[b, h]
 
 
+# ------------------------------------------------- chunked prefill, append
+
+def chunk_case(B, H, T, seed):
+    return (rand_bits((B, H, T, 128), seed), rand_bits((B, H, T, 64), seed + 1),
+            rand_bits((B, H, T, 128), seed + 2), rand_bits((B, 1, T, 64), seed + 3),
+            rand_bits((B, H, T, 128), seed + 4))
+
+
+def empty_caches(B, H, Lc, seed=None):
+    if seed is None:
+        z = lambda *s: np.zeros(s, np.uint16)
+        return z(B, H, Lc, 128), z(B, Lc, 64), z(B, H, Lc, 128)
+    return rand_bits((B, H, Lc, 128), seed), rand_bits((B, Lc, 64), seed + 1), rand_bits((B, H, Lc, 128), seed + 2)
+
+
+def test_chunk_at_zero_equals_prefill():
+    """Append at 0 then the chunked prefill over the cache is the prefill."""
+    B, H, T, Lc = 2, 3, 37, 50
+    qn, qp, kn, kp, v = chunk_case(B, H, T, 2400)
+    R = inputs.rope_angles(Lc)
+    want, wl = oracle.prefill(qn, qp, kn, kp, v, R, SCALE)
+    kc, pc, vc = empty_caches(B, H, Lc, 2410)  # rows past T hold junk
+    oracle.append_kv(kn, kp, v, R, 0, kc, pc, vc)
+    got, gl = oracle.prefill_chunk(qn, qp, kc, pc, vc, R, 0, SCALE)
+    assert np.array_equal(got, want) and np.array_equal(gl, wl)
+
+
+def test_chunks_equal_one_prefill():
+    """A 45-position prefill in chunks of 17 and 28 (append, then attend over
+    the cache): every row equals the single prefill's, bit for bit."""
+    B, H, T1, T2 = 2, 2, 17, 28
+    T = T1 + T2
+    qn, qp, kn, kp, v = chunk_case(B, H, T, 2500)
+    R = inputs.rope_angles(64)
+    want, wl = oracle.prefill(qn, qp, kn, kp, v, R, SCALE)
+    kc, pc, vc = empty_caches(B, H, 64)
+    c = lambda a, s: np.ascontiguousarray(a[:, :, s])
+    oracle.append_kv(c(kn, slice(0, T1)), c(kp, slice(0, T1)), c(v, slice(0, T1)), R, 0, kc, pc, vc)
+    o1, l1 = oracle.prefill_chunk(c(qn, slice(0, T1)), c(qp, slice(0, T1)), kc, pc, vc, R, 0, SCALE)
+    oracle.append_kv(c(kn, slice(T1, T)), c(kp, slice(T1, T)), c(v, slice(T1, T)), R, T1, kc, pc, vc)
+    o2, l2 = oracle.prefill_chunk(c(qn, slice(T1, T)), c(qp, slice(T1, T)), kc, pc, vc, R, T1, SCALE)
+    assert np.array_equal(o1, want[:, :T1]) and np.array_equal(o2, want[:, T1:])
+    assert np.array_equal(l1, wl[:, :, :T1]) and np.array_equal(l2, wl[:, :, T1:])
+
+
+def test_chunk_of_one_equals_decode_and_ignores_later_rows():
+    """A one-position chunk at past = L is the decode of that query over the
+    L + 1 cached keys (shared-rotary layout); cache rows past it are unseen."""
+    B, H, L, Lc = 2, 3, 30, 40
+    kc, pc, vc = empty_caches(B, H, Lc, 2600)
+    qn, qp = rand_bits((B, H, 1, 128), 2610), rand_bits((B, H, 1, 64), 2611)
+    R = inputs.rope_angles(Lc)
+    got, gl = oracle.prefill_chunk(qn, qp, kc, pc, vc, R, L, SCALE)
+    c = lambda a: np.ascontiguousarray(a[:, :, :L + 1]) if a.ndim == 4 else np.ascontiguousarray(a[:, :L + 1])
+    want, wl = oracle.decode_shared_kpe(qn[:, :, 0], qp[:, :, 0], c(kc), c(pc), c(vc), R, L, SCALE)
+    assert np.array_equal(got[:, 0], want) and np.array_equal(gl[:, :, 0], wl)
+    kc2, pc2, vc2 = kc.copy(), pc.copy(), vc.copy()
+    kc2[:, :, L + 1:] = rand_bits(kc2[:, :, L + 1:].shape, 2620)
+    pc2[:, L + 1:] = rand_bits(pc2[:, L + 1:].shape, 2621)
+    g2, _ = oracle.prefill_chunk(qn, qp, kc2, pc2, vc2, R, L, SCALE)
+    assert np.array_equal(g2, got)
+
+
 # ------------------------------------------------------------ fp8 weights
 
 def test_e4m3_decode_matches_torch():
