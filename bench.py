@@ -158,6 +158,28 @@ def other_configs(mla, inputs, w_o, scale, dev, calls=10):
             "rope": wl["rope"]}
         del d, o, ws, y, ws_o
         torch.cuda.empty_cache()
+    # A chunk of 4096 positions after 12288 cached ones (64 heads): append the
+    # chunk's keys into the shared-rotary cache, then attend over all 16384.
+    B, H, T, past = 1, 64, 4096, 12288
+    L = past + T
+    print(f"other config: chunked prefill (T={T} after {past})", file=sys.stderr, flush=True)
+    g = lambda shape, k: inputs.normal_bf16(shape, 7000 + k, device=dev)
+    q_nope, q_pe = g((B, H, T, 128), 0), g((B, H, T, 64), 1)
+    k_nope, k_pe, v = g((B, H, T, 128), 2), g((B, 1, T, 64), 3), g((B, H, T, 128), 4)
+    kc, pc, vc = g((B, H, L, 128), 5), g((B, L, 64), 6), g((B, H, L, 128), 7)
+    R = torch.from_numpy(inputs.rope_angles(L)).to(dev)
+    o = torch.empty((B, T, H * 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mla.mla_prefill_chunk_workspace_bytes(T), dtype=torch.uint8, device=dev)
+    fapp = lambda: mla.mla_append_kv(k_nope, k_pe, v, R, past, kc, pc, vc)
+    fatt = lambda: mla.mla_attend_prefill_chunk(q_nope, q_pe, kc, pc, vc, R, past, scale, out=o,
+                                                workspace=ws)
+    tapp, tatt = med(fapp), med(fatt)
+    fl = 2.0 * (128 + 64 + 128) * B * H * (T * past + T * (T + 1) / 2)
+    out[f"prefill_chunk_B{B}_T{T}_past{past}_H{H}"] = {
+        "append_ms": tapp, "attention_ms": tatt, "attention_tflops": fl / tatt / 1e9,
+        "attention_frac_peak": fl / tatt / 1e9 / PEAK_BF16_TFLOPS}
+    del q_nope, q_pe, k_nope, k_pe, v, kc, pc, vc, o, ws
+    torch.cuda.empty_cache()
     return out
 
 

@@ -110,6 +110,43 @@ int mla_attend_prefill(const mla_bf16 *q_nope, const mla_bf16 *q_pe, const mla_b
                        size_t workspace_bytes, void *out, float *lse, uint32_t flags,
                        void *stream);
 
+/* KV-cache append (page "Kimi K2 · Mix and project", excerpt "mla-prefill": the
+ * cache is updated with the keys after the rotary step; page "Kimi K2 ·
+ * Transformer blocks": new positions continue from the cached length): a chunk
+ * of T positions goes to rows past .. past+T-1 of a cache in the shared-rotary
+ * layout, the rope key rotated at its position (R row past + t) and rounded to
+ * bf16 with the same arithmetic as the prefill's own rotation.
+ *
+ *   k_nope [B, H, T, 128], k_pe [B, 1, T, 64] (unrotated), v [B, H, T, 128]
+ *   k_nope_cache [B, H, L_cap, 128], kpe_cache [B, L_cap, 64], v_cache
+ *   [B, H, L_cap, 128]   caller-owned, written at rows past .. past+T-1 only
+ *   R [r_rows, 32]; past >= 0, past + T <= L_cap and <= r_rows (else MLA_ERR_DIM)
+ *   flags must be 0.
+ */
+int mla_append_kv(const mla_bf16 *k_nope, const mla_bf16 *k_pe, const mla_bf16 *v, const float *R,
+                  int r_rows, int past, int B, int H, int T, int L_cap, mla_bf16 *k_nope_cache,
+                  mla_bf16 *kpe_cache, mla_bf16 *v_cache, uint32_t flags, void *stream);
+
+/* Chunked prefill over the cache (same pages): the T queries sit at positions
+ * past .. past+T-1 (q_pe rotated with R rows past + t) and query t sees cache
+ * rows 0 .. past+t (the chunk's own keys appended first, with mla_append_kv).
+ * With past = 0 and the chunk appended at 0 this is mla_attend_prefill.
+ *
+ *   q_nope [B, H, T, 128], q_pe [B, H, T, 64] (unrotated); caches as for
+ *   mla_append_kv, holding rows 0 .. past+T-1; out [B, T, H*128], lse [B, H, T]
+ *   workspace >= mla_prefill_chunk_workspace_bytes(T) bytes (cos/sin table)
+ *   H * L_cap * 256 must fit in 32 bits (else MLA_ERR_DIM); other arguments
+ *   and errors as for mla_attend_prefill.
+ */
+size_t mla_prefill_chunk_workspace_bytes(int T);
+
+int mla_attend_prefill_chunk(const mla_bf16 *q_nope, const mla_bf16 *q_pe,
+                             const mla_bf16 *k_nope_cache, const mla_bf16 *kpe_cache,
+                             const mla_bf16 *v_cache, const float *R, int r_rows, int past,
+                             float softmax_scale, int B, int H, int T, int L_cap, void *workspace,
+                             size_t workspace_bytes, void *out, float *lse, uint32_t flags,
+                             void *stream);
+
 /* --------------------------------------------------------------- decode --
  * One new query per sequence against L cached keys (page "Kimi K2 · Mix and
  * project", excerpt "mla-prefill": the cache stores keys after the rotary step,

@@ -176,6 +176,49 @@ def test_decode_latent_rejects(kw, code):
     assert latent(**kw) == code
 
 
+def append(**kw):
+    a = dict(kn=A[0], kp=A[1], v=A[2], R=A[3], r_rows=100, past=10, B=1, H=2, T=20, L=64,
+             kc=A[4], pc=A[5], vc=A[6], flags=0)
+    a.update(kw)
+    return mla.lib().mla_append_kv(a["kn"], a["kp"], a["v"], a["R"], a["r_rows"], a["past"], a["B"],
+                                   a["H"], a["T"], a["L"], a["kc"], a["pc"], a["vc"], a["flags"], None)
+
+
+def chunk(**kw):
+    a = dict(qn=A[0], qp=A[1], kc=A[2], pc=A[3], vc=A[4], R=A[5], r_rows=100, past=10, scale=0.07,
+             B=1, H=2, T=20, L=64, ws=A[6], ws_bytes=1 << 20, out=A[7], lse=None, flags=0)
+    a.update(kw)
+    return mla.lib().mla_attend_prefill_chunk(
+        a["qn"], a["qp"], a["kc"], a["pc"], a["vc"], a["R"], a["r_rows"], a["past"], a["scale"],
+        a["B"], a["H"], a["T"], a["L"], a["ws"], a["ws_bytes"], a["out"], a["lse"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), NULL), (dict(pc=None), NULL), (dict(flags=1), FLAGS),
+    (dict(past=-1), DIM), (dict(past=45), DIM), (dict(r_rows=29), DIM), (dict(T=0), DIM),
+    (dict(kc=ctypes.c_void_p(5 * 16 * GB + 8)), ALIGN),
+    (dict(kc=ctypes.c_void_p(1 * 16 * GB + 64)), ALIAS),  # cache over k_nope
+])
+def test_append_rejects(kw, code):
+    assert append(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qn=None), NULL), (dict(vc=None), NULL), (dict(flags=2), FLAGS),
+    (dict(past=-1), DIM), (dict(past=45), DIM), (dict(r_rows=29), DIM), (dict(H=64, L=1 << 18), DIM),
+    (dict(scale=0.0), SCALE), (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE),
+    (dict(out=ctypes.c_void_p(3 * 16 * GB + 32)), ALIAS),  # out over the cache
+])
+def test_prefill_chunk_rejects(kw, code):
+    assert chunk(**kw) == code
+
+
+def test_prefill_chunk_workspace():
+    assert mla.mla_prefill_chunk_workspace_bytes(300) == 300 * 32 * 8 + 256 - (300 * 32 * 8) % 256 \
+        if (300 * 32 * 8) % 256 else 300 * 32 * 8
+    assert mla.mla_prefill_chunk_workspace_bytes(0) == 0
+
+
 def oproj8(**kw):
     a = dict(x=A[0], w8=A[1], s=A[2], y=A[3], M=16384, K=8192, N=7168, ws=None, ws_bytes=0, flags=0)
     a.update(kw)

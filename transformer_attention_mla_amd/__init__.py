@@ -18,6 +18,7 @@ __all__ = [
     "mla_prefill_workspace_bytes", "mla_attend_prefill", "mla_decode_splits",
     "mla_decode_workspace_bytes", "mla_attend_decode", "mla_attend_decode_shared_kpe",
     "mla_decode_latent_workspace_bytes", "mla_attend_decode_latent",
+    "mla_append_kv", "mla_prefill_chunk_workspace_bytes", "mla_attend_prefill_chunk",
     "mla_out_proj_workspace_bytes", "mla_out_proj_fp8_workspace_bytes", "mla_out_proj_fp8",
     "mla_out_proj", "NOPE", "ROPE", "VDIM", "PAIRS",
 ]
@@ -57,6 +58,12 @@ def lib():
     L.mla_prefill_workspace_bytes.restype = Z
     L.mla_attend_prefill.argtypes = [P, P, P, P, P, P, I, F, I, I, I, P, Z, P, P, U, P]
     L.mla_attend_prefill.restype = I
+    L.mla_append_kv.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, P, U, P]
+    L.mla_append_kv.restype = I
+    L.mla_prefill_chunk_workspace_bytes.argtypes = [I]
+    L.mla_prefill_chunk_workspace_bytes.restype = Z
+    L.mla_attend_prefill_chunk.argtypes = [P, P, P, P, P, P, I, I, F, I, I, I, I, P, Z, P, P, U, P]
+    L.mla_attend_prefill_chunk.restype = I
     L.mla_decode_splits.argtypes = [I, I, I, I]
     L.mla_decode_splits.restype = I
     L.mla_decode_workspace_bytes.argtypes = [I, I, I, I]
@@ -365,3 +372,73 @@ def mla_out_proj_fp8(x, w8, w_scale, *, y=None, out_f32=False, workspace=None, s
     if rc:
         raise MlaError(rc, "mla_out_proj_fp8")
     return y
+
+
+def mla_append_kv(k_nope, k_pe, v, R, past, k_nope_cache, kpe_cache, v_cache, *, stream=None):
+    """Write a chunk (k_nope [B,H,T,128], k_pe [B,1,T,64] unrotated, v
+    [B,H,T,128]) into the shared-rotary cache at rows past .. past+T-1
+    (k_nope_cache [B,H,L,128], kpe_cache [B,L,64], v_cache [B,H,L,128])."""
+    torch = _torch()
+    if k_nope.dim() != 4 or k_nope_cache.dim() != 4:
+        raise ValueError("k_nope must be [B, H, T, 128] and k_nope_cache [B, H, L, 128]")
+    B, H, T, _ = k_nope.shape
+    L = k_nope_cache.shape[2]
+    dev = k_nope.device
+    bf = torch.bfloat16
+    _check(k_nope, "k_nope", bf, (B, H, T, NOPE), dev)
+    _check(k_pe, "k_pe", bf, (B, 1, T, ROPE), dev)
+    _check(v, "v", bf, (B, H, T, VDIM), dev)
+    _check(k_nope_cache, "k_nope_cache", bf, (B, H, L, NOPE), dev)
+    _check(kpe_cache, "kpe_cache", bf, (B, L, ROPE), dev)
+    _check(v_cache, "v_cache", bf, (B, H, L, VDIM), dev)
+    if R.dim() != 2:
+        raise ValueError("R must be [r_rows, 32]")
+    _check(R, "R", torch.float32, (R.shape[0], PAIRS), dev)
+    rc = lib().mla_append_kv(_ptr(k_nope), _ptr(k_pe), _ptr(v), _ptr(R), R.shape[0], int(past), B, H,
+                             T, L, _ptr(k_nope_cache), _ptr(kpe_cache), _ptr(v_cache), 0,
+                             _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_append_kv")
+
+
+def mla_prefill_chunk_workspace_bytes(T: int) -> int:
+    return lib().mla_prefill_chunk_workspace_bytes(T)
+
+
+def mla_attend_prefill_chunk(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, past,
+                             softmax_scale, *, out=None, lse=None, want_lse=False, out_f32=False,
+                             workspace=None, stream=None):
+    """Chunked prefill: q_nope [B,H,T,128], q_pe [B,H,T,64] at positions past ..
+    past+T-1 against cache rows 0 .. past+t.  Returns (out [B,T,H*128], lse
+    [B,H,T] or None)."""
+    torch = _torch()
+    if q_nope.dim() != 4 or k_nope_cache.dim() != 4:
+        raise ValueError("q_nope must be [B, H, T, 128] and k_nope_cache [B, H, L, 128]")
+    B, H, T, _ = q_nope.shape
+    L = k_nope_cache.shape[2]
+    dev = q_nope.device
+    bf = torch.bfloat16
+    _check(q_nope, "q_nope", bf, (B, H, T, NOPE), dev)
+    _check(q_pe, "q_pe", bf, (B, H, T, ROPE), dev)
+    _check(k_nope_cache, "k_nope_cache", bf, (B, H, L, NOPE), dev)
+    _check(kpe_cache, "kpe_cache", bf, (B, L, ROPE), dev)
+    _check(v_cache, "v_cache", bf, (B, H, L, VDIM), dev)
+    if R.dim() != 2:
+        raise ValueError("R must be [r_rows, 32]")
+    _check(R, "R", torch.float32, (R.shape[0], PAIRS), dev)
+    odt = torch.float32 if out_f32 else bf
+    if out is None:
+        out = torch.empty((B, T, H * VDIM), dtype=odt, device=dev)
+    _check(out, "out", odt, (B, T, H * VDIM), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H, T), dev)
+    workspace, ws_bytes = _workspace(workspace, mla_prefill_chunk_workspace_bytes(T), dev)
+    rc = lib().mla_attend_prefill_chunk(
+        _ptr(q_nope), _ptr(q_pe), _ptr(k_nope_cache), _ptr(kpe_cache), _ptr(v_cache), _ptr(R),
+        R.shape[0], int(past), float(softmax_scale), B, H, T, L, _ptr(workspace), ws_bytes, _ptr(out),
+        _ptr(lse), MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_attend_prefill_chunk")
+    return out, lse

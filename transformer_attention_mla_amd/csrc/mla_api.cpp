@@ -118,7 +118,9 @@ int mla_attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_b
                        void* stream) {
   if (!q_nope || !q_pe || !k_nope || !k_pe || !v || !R || !out) return MLA_ERR_NULL;
   if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
-  if (!dims_ok(B, H, T, kQK) || r_rows <= 0 || r_rows > kMaxDim || T > r_rows) return MLA_ERR_DIM;
+  if (!dims_ok(B, H, T, kQK) || r_rows <= 0 || r_rows > kMaxDim || T > r_rows ||
+      (size_t)H * T * 256 > 0xffffffffu)
+    return MLA_ERR_DIM;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_SCALE;
   const mla::PrefillWorkspace ws = mla::prefill_workspace_layout(B, T);
   if (!workspace || workspace_bytes < ws.total) return MLA_ERR_WORKSPACE;
@@ -149,10 +151,101 @@ int mla_attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_b
   p.B = B;
   p.H = H;
   p.T = T;
+  p.past = 0;
+  p.LK = T;
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
   p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
+  if (mla::launch_rope_prep(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  if (mla::launch_prefill(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+// ------------------------------------------------ chunked prefill, append
+
+size_t mla_prefill_chunk_workspace_bytes(int T) {
+  if (T <= 0 || T > kMaxDim) return 0;
+  return mla::align_up((size_t)T * mla::kPairs * 8, 256);
+}
+
+int mla_append_kv(const mla_bf16* k_nope, const mla_bf16* k_pe, const mla_bf16* v, const float* R,
+                  int r_rows, int past, int B, int H, int T, int L_cap, mla_bf16* k_nope_cache,
+                  mla_bf16* kpe_cache, mla_bf16* v_cache, uint32_t flags, void* stream) {
+  if (!k_nope || !k_pe || !v || !R || !k_nope_cache || !kpe_cache || !v_cache) return MLA_ERR_NULL;
+  if (flags) return MLA_ERR_FLAGS;
+  if (!dims_ok(B, H, T, kQK) || !dims_ok(B, H, L_cap, kQK) || past < 0 || r_rows <= 0 ||
+      r_rows > kMaxDim || (long long)past + T > L_cap || (long long)past + T > r_rows)
+    return MLA_ERR_DIM;
+  if (!aligned16(k_nope) || !aligned16(k_pe) || !aligned16(v) || !aligned16(R) ||
+      !aligned16(k_nope_cache) || !aligned16(kpe_cache) || !aligned16(v_cache))
+    return MLA_ERR_ALIGN;
+  const size_t bht = (size_t)B * H * T, bhl = (size_t)B * H * L_cap;
+  const Range in[] = {{k_nope, bht * kNope * 2}, {k_pe, (size_t)B * T * kRope * 2},
+                      {v, bht * kV * 2}, {R, (size_t)r_rows * mla::kPairs * 4}};
+  const Range outs[] = {{k_nope_cache, bhl * kNope * 2}, {kpe_cache, (size_t)B * L_cap * kRope * 2},
+                        {v_cache, bhl * kV * 2}};
+  if (any_alias(in, 4, outs, 3)) return MLA_ERR_ALIAS;
+  const int dev = check_device();
+  if (dev != MLA_OK) return dev;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (mla::launch_append_rows(k_nope, k_nope_cache, B * H, T, L_cap, past, s) != hipSuccess ||
+      mla::launch_append_rows(v, v_cache, B * H, T, L_cap, past, s) != hipSuccess ||
+      mla::launch_rope(R, past, k_pe, nullptr, kpe_cache, L_cap, past, B, T, s) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+int mla_attend_prefill_chunk(const mla_bf16* q_nope, const mla_bf16* q_pe,
+                             const mla_bf16* k_nope_cache, const mla_bf16* kpe_cache,
+                             const mla_bf16* v_cache, const float* R, int r_rows, int past,
+                             float softmax_scale, int B, int H, int T, int L_cap, void* workspace,
+                             size_t workspace_bytes, void* out, float* lse, uint32_t flags,
+                             void* stream) {
+  if (!q_nope || !q_pe || !k_nope_cache || !kpe_cache || !v_cache || !R || !out) return MLA_ERR_NULL;
+  if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
+  if (!dims_ok(B, H, T, kQK) || !dims_ok(B, H, L_cap, kQK) || past < 0 || r_rows <= 0 ||
+      r_rows > kMaxDim || (long long)past + T > L_cap || (long long)past + T > r_rows ||
+      (size_t)H * L_cap * 256 > 0xffffffffu)
+    return MLA_ERR_DIM;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_SCALE;
+  const size_t need = mla_prefill_chunk_workspace_bytes(T);
+  if (!workspace || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(k_nope_cache) || !aligned16(kpe_cache) ||
+      !aligned16(v_cache) || !aligned16(R) || !aligned16(out) || !aligned16(lse) ||
+      !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  const size_t bht = (size_t)B * H * T, bhl = (size_t)B * H * L_cap;
+  const size_t out_elt = (flags & MLA_OUT_F32) ? 4 : 2;
+  const Range in[] = {{q_nope, bht * kNope * 2}, {q_pe, bht * kRope * 2},
+                      {k_nope_cache, bhl * kNope * 2}, {kpe_cache, (size_t)B * L_cap * kRope * 2},
+                      {v_cache, bhl * kV * 2}, {R, (size_t)r_rows * mla::kPairs * 4}};
+  const Range outs[] = {{out, bht * kV * out_elt}, {lse, lse ? bht * 4 : 0}, {workspace, need}};
+  if (any_alias(in, 6, outs, 3)) return MLA_ERR_ALIAS;
+  const int dev = check_device();
+  if (dev != MLA_OK) return dev;
+
+  mla::PrefillParams p;
+  p.q_nope = q_nope;
+  p.q_pe = q_pe;
+  p.k_nope = k_nope_cache;
+  p.k_pe = nullptr;  // the cache holds rotated keys
+  p.v = v_cache;
+  p.R = R;
+  p.cs = static_cast<float2*>(workspace);
+  p.kpe_rot = const_cast<uint16_t*>(kpe_cache);
+  p.out = out;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.T = T;
+  p.past = past;
+  p.LK = L_cap;
+  p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
   if (mla::launch_rope_prep(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
   if (mla::launch_prefill(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
   return MLA_OK;

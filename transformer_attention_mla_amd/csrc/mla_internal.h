@@ -37,23 +37,34 @@ inline PrefillWorkspace prefill_workspace_layout(int B, int T) {
 }
 
 struct PrefillParams {
-  const uint16_t* q_nope;
-  const uint16_t* q_pe;
-  const uint16_t* k_nope;
-  const uint16_t* k_pe;
-  const uint16_t* v;
+  const uint16_t* q_nope;  // [B][H][T][128]
+  const uint16_t* q_pe;    // [B][H][T][64], unrotated
+  const uint16_t* k_nope;  // [B][H][LK][128]
+  const uint16_t* k_pe;    // [B][T][64] unrotated (rotated by the prologue), or null
+  const uint16_t* v;       // [B][H][LK][128]
   const float* R;
-  float2* cs;          // workspace
-  uint16_t* kpe_rot;   // workspace
+  float2* cs;          // workspace: (cos, sin) of the queries' positions, [T][32]
+  uint16_t* kpe_rot;   // rotated shared key [B][LK][64]: workspace, or the caller's cache
   void* out;
   float* lse;
   int B, H, T;
+  int past;            // queries sit at positions past .. past+T-1 and see keys 0 .. past+t
+  int LK;              // rows per (sequence, head) of k_nope / v and per sequence of kpe_rot
   float scale_log2;    // softmax_scale * log2(e)
   int out_f32;
   int paired;          // set by launch_prefill: 1 = a workgroup takes query tiles i and NQ-1-i
 };
 
 hipError_t launch_rope_prep(const PrefillParams& p, hipStream_t stream);
+
+// Rotary table and rotated shared key at positions r_off + t, t < T: cs[t]
+// (when cs is set) and dst[b][dst_off + t] (rows of dst_rows) from k_pe[b][t]
+// (when k_pe is set).
+hipError_t launch_rope(const float* R, int r_off, const uint16_t* k_pe, float2* cs, uint16_t* dst,
+                       int dst_rows, int dst_off, int B, int T, hipStream_t stream);
+// Copy rows [B*H][T][128] to rows dst_off .. of [B*H][dst_rows][128] (bf16).
+hipError_t launch_append_rows(const uint16_t* src, uint16_t* dst, int BH, int T, int dst_rows,
+                              int dst_off, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
 // ----------------------------------------------------------------- decode --

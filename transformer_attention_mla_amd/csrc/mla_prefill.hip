@@ -123,6 +123,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const int hf = lane >> 5;
 
   const int H = p.H, T = p.T;
+  const int past = p.past, LK = p.LK;  // key positions 0 .. past+T-1, LK rows per head
   const int HG = (H + G - 1) / G;
   const int NQ = (T + BQ - 1) / BQ;
   const int NP = p.paired ? (NQ + 1) / 2 : NQ;  // query-tile pairs (or single tiles)
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
         c = 15;
       }
       const int hh = min(hg * G + min(gg, G - 1), H - 1);
-      v = ((uint32_t)hh * (uint32_t)T + (uint32_t)akey(R)) * 256u + c * 16;
+      v = ((uint32_t)hh * (uint32_t)LK + (uint32_t)akey(R)) * 256u + c * 16;
       kind[i] = 0;
     } else if (j < CKP) {
       const int s = (j - CK) * 64 + lane;  // slot in the rotated-key region (8 per row)
@@ -188,15 +189,15 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
       const int row = (s % (BK * 16)) / 16;
       const int c = (s % 16) ^ ((row & 3) << 2);
       const int hh = min(hg * G + gg, H - 1);
-      v = ((uint32_t)hh * (uint32_t)T + (uint32_t)row) * 256u + c * 16;
+      v = ((uint32_t)hh * (uint32_t)LK + (uint32_t)row) * 256u + c * 16;
       kind[i] = 2;
     }
     voff[i] = v;
   }
-  const uint16_t* kseq = p.k_nope + (size_t)b * H * T * kNope;
-  const uint16_t* vseq = p.v + (size_t)b * H * T * kV;
-  const uint16_t* pseq = p.kpe_rot + (size_t)b * T * kRope;
-  const uint32_t seq_bytes = (uint32_t)((size_t)H * T * 256);
+  const uint16_t* kseq = p.k_nope + (size_t)b * H * LK * kNope;
+  const uint16_t* vseq = p.v + (size_t)b * H * LK * kV;
+  const uint16_t* pseq = p.kpe_rot + (size_t)b * LK * kRope;
+  const uint32_t seq_bytes = (uint32_t)((size_t)H * LK * 256);
 
   // Copies of one tile: descriptors whose base advances with the tile, and the
   // stage they fill.  Past the last tile the descriptors are empty (nothing is
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     const uint32_t k0 = live ? (uint32_t)(kt * BK) : 0u;
     Copies c;
     c.rK = make_rsrc(kseq + (size_t)k0 * kNope, live ? seq_bytes - k0 * 256u : 0u);
-    c.rP = make_rsrc(pseq + (size_t)k0 * kRope, live ? (uint32_t)(T - (int)k0) * 128u : 0u);
+    c.rP = make_rsrc(pseq + (size_t)k0 * kRope, live ? (uint32_t)(LK - (int)k0) * 128u : 0u);
     c.rV = make_rsrc(vseq + (size_t)k0 * kV, live ? seq_bytes - k0 * 256u : 0u);
     c.buf = buf;
     return c;
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     const int myq = q0 + ln;
     const int myqc = myq < T ? myq : T - 1;
     const int headc = head_ok ? head : H - 1;
-    const int kend = min(T, qt * BQ + BQ);
+    const int kend = past + min(T, qt * BQ + BQ);  // keys of the tile's last query, plus one
     const int nkt = (kend + BK - 1) / BK;
 
     // ---- query fragments (B operand), rotary part rotated in registers
@@ -322,11 +323,11 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
       f32x16 s = {};
 #pragma unroll
       for (int kb = 0; kb < 12; ++kb) s = mfma32x32x16(kf[kb], qf[kb], s);
-      if (k0 + BK - 1 > q0) {  // the tile on this wave's diagonal
+      if (k0 + BK - 1 > past + q0) {  // the tile on this wave's diagonal
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + ((r >> 3) * 16) + hf * 8 + ((r >> 2) & 1) * 4 + (r & 3);
-          if (key > myq) s[r] = -INFINITY;
+          if (key > past + myq) s[r] = -INFINITY;
         }
       }
       float mx = max3(s[0], s[1], s[2]);
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     // kt-1 used (every wave left it before the barrier that opened this
     // iteration) just before waiting at the barrier for tile kt+1.
     auto step = [&](uint8_t* cur, uint8_t* ahead, int kt) {
-      if (head_ok && kt * BK <= q0 + 31) compute(cur, kt);
+      if (head_ok && kt * BK <= past + q0 + 31) compute(cur, kt);
       copy_all(plan(ahead, kt + NSTAGE - 1, nkt));
       if (kt + 1 < nkt) wait_tile(kt + 1);
     };

@@ -1,5 +1,8 @@
 // Rotary prologue of the prefill: cos/sin of the angle table and the rotated
-// shared rotary key.
+// shared rotary key; the same kernel writes the rotated key of a new chunk
+// into the cache (positions continue from the cached length: page "Kimi K2 ·
+// Transformer blocks", model-body excerpt), next to a plain row copy for the
+// chunk's nope keys and values.
 //
 // Page "Kimi K2 · Mix and project", code excerpt "mla-prefill": cos and sin
 // come from the rotary embedding and rotate q_pe and k_pe; the key's rotated
@@ -19,35 +22,66 @@
 
 namespace mla {
 
-__global__ __launch_bounds__(256) void rope_prep_kernel(const float* __restrict__ R,
+__global__ __launch_bounds__(256) void rope_prep_kernel(const float* __restrict__ R, int r_off,
                                                         const uint16_t* __restrict__ k_pe,
                                                         float2* __restrict__ cs,
-                                                        uint16_t* __restrict__ kpe_rot, int B,
-                                                        int T) {
+                                                        uint16_t* __restrict__ dst, int dst_rows,
+                                                        int dst_off, int B, int T) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * kPairs) return;
   const int t = idx / kPairs;
   const int i = idx % kPairs;
   float s, c;
-  sincosf(R[idx], &s, &c);
-  cs[idx] = make_float2(c, s);
+  sincosf(R[(size_t)r_off * kPairs + idx], &s, &c);
+  if (cs) cs[idx] = make_float2(c, s);
+  if (!k_pe) return;
   for (int b = 0; b < B; ++b) {
     const size_t row = ((size_t)b * T + t) * kRope;
+    const size_t out = ((size_t)b * dst_rows + dst_off + t) * kRope;
     const float lo = bf16_to_f32(k_pe[row + i]);
     const float hi = bf16_to_f32(k_pe[row + i + kPairs]);
     const float ylo = fmaf(lo, c, -(hi * s));
     const float yhi = fmaf(hi, c, lo * s);
-    kpe_rot[row + i] = __builtin_bit_cast(uint16_t, f32_to_bf16(ylo));
-    kpe_rot[row + i + kPairs] = __builtin_bit_cast(uint16_t, f32_to_bf16(yhi));
+    dst[out + i] = __builtin_bit_cast(uint16_t, f32_to_bf16(ylo));
+    dst[out + i + kPairs] = __builtin_bit_cast(uint16_t, f32_to_bf16(yhi));
   }
 }
 
-hipError_t launch_rope_prep(const PrefillParams& p, hipStream_t stream) {
-  const int n = p.T * kPairs;
+// Cache append of 256-byte rows: 16 threads per row, one 16-byte piece each.
+__global__ __launch_bounds__(256) void append_rows_kernel(const uint16_t* __restrict__ src,
+                                                          uint16_t* __restrict__ dst, int T,
+                                                          int dst_rows, int dst_off, long n) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const long row = idx >> 4;  // (bh, t)
+  const int piece = (int)(idx & 15);
+  const long bh = row / T;
+  const int t = (int)(row % T);
+  const u32x4 v = ld_global_16(src + row * 128 + piece * 8);
+  *reinterpret_cast<u32x4*>(dst + (bh * dst_rows + dst_off + t) * 128 + piece * 8) = v;
+}
+
+hipError_t launch_rope(const float* R, int r_off, const uint16_t* k_pe, float2* cs, uint16_t* dst,
+                       int dst_rows, int dst_off, int B, int T, hipStream_t stream) {
+  const int n = T * kPairs;
   const int threads = 256;
   const int blocks = (n + threads - 1) / threads;
-  hipLaunchKernelGGL(rope_prep_kernel, dim3(blocks), dim3(threads), 0, stream, p.R, p.k_pe, p.cs,
-                     p.kpe_rot, p.B, p.T);
+  hipLaunchKernelGGL(rope_prep_kernel, dim3(blocks), dim3(threads), 0, stream, R, r_off, k_pe, cs,
+                     dst, dst_rows, dst_off, B, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_prep(const PrefillParams& p, hipStream_t stream) {
+  return launch_rope(p.R, p.past, p.k_pe, p.cs, p.kpe_rot, p.LK, 0, p.B, p.T, stream);
+}
+
+hipError_t launch_append_rows(const uint16_t* src, uint16_t* dst, int BH, int T, int dst_rows,
+                              int dst_off, hipStream_t stream) {
+  const long n = (long)BH * T * 16;
+  const long blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(append_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, T,
+                     dst_rows, dst_off, n);
   return hipGetLastError();
 }
 
