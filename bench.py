@@ -35,14 +35,14 @@ CSRC = os.path.join(REPO, "transformer_attention_mla_amd", "csrc")
 # bytes written).  Each figure holds only for the kernel source it was taken on,
 # identified by a hash of its files; after any change the figure is dropped.
 MEASURED_TRAFFIC = {
-    "prefill_kernel": ("7fc82aeff8bca3d4", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
-                       2056905754, "profiles/prefill_kernel_B4_T4096_H64.txt"),
-    "decode_split_kernel": ("ff99beaccaaec8aa", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                            21477507241, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
-    "decode_split_kernel_shared_kpe": ("ff99beaccaaec8aa", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                                       17374845312, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
-    "latent_decode_kernel": ("b98767469d9e3587", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
-                             657384094, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
+    "prefill_kernel": ("96fb11d933047611", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
+                       2072185010, "profiles/prefill_kernel_B4_T4096_H64.txt"),
+    "decode_split_kernel": ("74734a96e7bbe6a0", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                            21477504147, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
+    "decode_split_kernel_shared_kpe": ("74734a96e7bbe6a0", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                                       17376421633, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
+    "latent_decode_kernel": ("dc66f75c1d8f1f1d", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
+                             657378975, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
 }
 
 
