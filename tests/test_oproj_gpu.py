@@ -20,10 +20,14 @@ def xw(M, K, N, seed):
     return x, w
 
 
-# The last three shapes take the wide-tile kernel (>= 256 tiles of 256 x 256):
-# ragged last m-group and n-tile, a tile count that is not a multiple of the 8
-# XCDs, N not a multiple of 4 (element stores), and an exact 256-multiple.
+# Small M at several K splits, N ragged against the tiles and against 4, M not
+# a multiple of 16.  The last three shapes take the wide-tile kernel (>= 256
+# tiles of 256 x 256): ragged last m-group and n-tile, a tile count that is
+# not a multiple of the 8 XCDs, N not a multiple of 4 (element stores), and an
+# exact 256-multiple.
 @pytest.mark.parametrize("M,K,N", [(1, 128, 1), (17, 256, 100), (130, 1024, 300), (64, 8192, 7168),
+                                   (1, 512, 7168), (33, 1024, 500), (64, 2048, 225), (16, 4096, 447),
+                                   (64, 16384, 300),
                                    (200, 512, 7168), (5, 8192, 33), (300, 128, 129),
                                    (4764, 128, 3803), (4100, 256, 4000), (8192, 512, 2048)])
 def test_oproj_parity(M, K, N, gpu_device):
@@ -56,8 +60,9 @@ def test_oproj_large_sampled(M, gpu_device):
     check_close(got, want, TOL, f"{len(rows)} sampled rows")
 
 
-def test_oproj_selection_weight_exact(gpu_device):
-    M, K, N = 70, 1024, 600
+@pytest.mark.parametrize("M", [70, 37])
+def test_oproj_selection_weight_exact(M, gpu_device):
+    K, N = 1024, 600
     x = inputs.normal_bf16((M, K), 5)
     w = torch.zeros((N, K), dtype=torch.bfloat16)
     w[torch.arange(N), torch.arange(N)] = 1
@@ -105,10 +110,15 @@ def test_attention_then_oproj_workload1(gpu_device):
 # ------------------------------------------------------------- FP8 weights
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 1), (17, 256, 100), (64, 8192, 7168), (130, 1024, 300),
-                                   (300, 384, 129), (1000, 512, 1000)])
+                                   (300, 384, 129), (1000, 512, 1000), (1, 512, 129), (40, 2048, 1000),
+                                   (64, 1024, 7168), (33, 1024, 500), (64, 2048, 225), (16, 4096, 447),
+                                   (64, 16384, 300)])
 def test_oproj_fp8_parity(M, K, N, gpu_device):
     """The FP8 checkpoint weight, dequantized to bf16 in the kernel's load path:
-    against the oracle's projection with the same dequantization."""
+    against the oracle's projection with the same dequantization.  M <= 64
+    with K a multiple of 512 takes the skinny kernel (x shared through LDS,
+    224 features per workgroup): one or several K slices, N ragged against
+    224 and against 4, M not a multiple of 16."""
     say(f"o_proj fp8 parity M={M} K={K} N={N}")
     x = inputs.normal_bf16((M, K), 30 + M)
     w8, sc = inputs.out_proj_weight_fp8(N, K, workload=1)
@@ -122,12 +132,14 @@ def test_oproj_fp8_parity(M, K, N, gpu_device):
     check_bf16_close(y16, want, "bf16 output vs oracle")
 
 
-def test_oproj_fp8_dequant_exact(gpu_device):
+@pytest.mark.parametrize("M", [70, 64])
+def test_oproj_fp8_dequant_exact(M, gpu_device):
     """Scaled identity: w8 = 1.0 (0x38) on the diagonal, scale 2^-3 in every
     block, so y = x / 8 bit for bit -- the dequantized weight is exactly 0.125
     and zero elsewhere, each output one product; and a second block scale
-    pattern (a power of two per block) moves each output by its block's scale."""
-    M, K, N = 70, 1024, 600
+    pattern (a power of two per block) moves each output by its block's scale.
+    M = 64 takes the skinny kernel, M = 70 the tiled one."""
+    K, N = 1024, 600
     x = inputs.normal_bf16((M, K), 7)
     w8 = torch.zeros((N, K), dtype=torch.uint8)
     w8[torch.arange(N), torch.arange(N)] = 0x38

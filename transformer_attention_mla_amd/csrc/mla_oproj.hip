@@ -389,6 +389,159 @@ __global__ __launch_bounds__(256) void oproj_reduce_kernel(OprojParams p) {
   }
 }
 
+// ------------------------------------------------------------- skinny M --
+// M <= 64 with the FP8 weight (decode): the weight stream is the HBM traffic
+// and x is small, so x is shared through LDS and the weight goes straight to
+// registers.  A workgroup of 4 waves owns SF = 224 output features and a K
+// slice of KC <= 1024: it copies x[0..63][slice] into LDS once (16-byte
+// chunks, chunk index XOR (row & 15), so the 16 rows read by one MFMA operand
+// fall in distinct banks), then wave w takes features SF/2 * (w & 1) +
+// [0, 112) and half (w >> 1) of the slice.  Per step of 64 k a wave computes
+// Y[n][m] for its 112 features (7 blocks of 16) and all 64 rows with
+// v_mfma_f32_16x16x32_bf16: A = weight rows straight from global memory
+// (lane: feature 16j + l%16, 16 e4m3 values at k 16(l/16).. that make two
+// MFMA k-slices of 8, dequantized in registers), B = x rows from LDS (lane:
+// row 16mb + l%16, the same k-values); loads run SKD steps ahead, all
+// unconditional so that the compiler waits for the oldest step only.  The
+// two K halves are added in LDS; with more than one workgroup along K the
+// sums go to the float32 partials and the reduction kernel.  (With the bf16
+// weight the tiled kernel, at several workgroups per compute unit, streams
+// the weight faster than this one-workgroup-per-unit layout.)
+constexpr int SF = 224;        // output features per workgroup
+constexpr int SNB = 7;         // 16-feature blocks per wave
+constexpr int SKC_MAX = 1024;  // k per workgroup (x slice: 64 x 1024 bf16 = 128 KiB of LDS)
+constexpr int SKD = 4;         // steps of weight loads in flight per wave
+constexpr int SKSTEP = 64;     // k per step
+
+__global__ __launch_bounds__(256) void oproj_skinny_fp8_kernel(OprojParams p) {
+  __shared__ __attribute__((aligned(16))) u32x4 xs[64 * SKC_MAX / 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, i = lane & 15;
+  const int M = p.M, N = p.N, K = p.K;
+  const int KC = K / gridDim.y;   // k per workgroup: a multiple of 512, at most SKC_MAX
+  const int cpr = KC / 8;         // 16-byte chunks per x row in LDS
+  const int kb = blockIdx.y * KC;
+  const int fh = wave & 1, kh = wave >> 1;
+  const int n0 = blockIdx.x * SF + fh * (SF / 2);
+  const int kw = kb + kh * (KC / 2);     // this wave's first k
+  const int nsteps = KC / 2 / SKSTEP;    // a multiple of SKD (KC is a multiple of 512)
+  const int KB = (K + 127) / 128;
+
+  int nrow[SNB];
+#pragma unroll
+  for (int j = 0; j < SNB; ++j) nrow[j] = min(n0 + j * 16 + i, N - 1);
+
+  struct Frag {
+    u32x4 a[SNB];
+    float sc[SNB];
+  };
+  auto load = [&](Frag& f, int st) {
+    const int k = kw + st * SKSTEP;
+#pragma unroll
+    for (int j = 0; j < SNB; ++j) {
+      f.a[j] = ld_global_16(p.w8 + (size_t)nrow[j] * K + k + q * 16);
+      f.sc[j] = p.w_scale[(nrow[j] >> 7) * KB + (k >> 7)];
+    }
+  };
+
+  Frag fr[SKD];
+#pragma unroll
+  for (int d = 0; d < SKD; ++d) load(fr[d], d);
+
+  // ---- x slice into LDS (rows >= M repeat row M-1; their outputs are not stored)
+  for (int c0 = 0; c0 < 64 * cpr; c0 += 256 * 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u * 256 + tid;
+      const int m = c / cpr, ch = c - m * cpr;
+      v[u] = ld_global_16(p.x + (size_t)min(m, M - 1) * K + kb + ch * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u * 256 + tid;
+      const int m = c / cpr, ch = c - m * cpr;
+      xs[m * cpr + (ch ^ (m & 15))] = v[u];
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc[SNB][4] = {};  // [feature block][row block]
+  auto step = [&](const Frag& f, int st) {
+    const int c0 = (kw - kb + st * SKSTEP) / 8;  // first x chunk (8 k) of the step
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int ch = c0 + 2 * q + sub;
+      bf16x8 b[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) b[mb] = as_bf16x8(xs[(mb * 16 + i) * cpr + (ch ^ i)]);
+#pragma unroll
+      for (int j = 0; j < SNB; ++j) {
+        const bf16x8 a = as_bf16x8(dequant8(u32x2{f.a[j][2 * sub], f.a[j][2 * sub + 1]}, f.sc[j]));
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[j][mb] = mfma16x16x32(a, b[mb], acc[j][mb]);
+      }
+    }
+  };
+  for (int st0 = 0; st0 + SKD < nsteps; st0 += SKD) {
+#pragma unroll
+    for (int d = 0; d < SKD; ++d) {
+      step(fr[d], st0 + d);
+      load(fr[d], st0 + SKD + d);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < SKD; ++d) step(fr[d], nsteps - SKD + d);
+
+  // ---- the two K halves added in LDS (the x slice is no longer read)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(xs) + fh * (SNB * 16 * 64);  // [acc register][lane]
+  if (kh == 1) {
+#pragma unroll
+    for (int j = 0; j < SNB; ++j)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[((j * 4 + mb) * 4 + r) * 64 + lane] = acc[j][mb][r];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int j = 0; j < SNB; ++j)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[j][mb][r] += red[((j * 4 + mb) * 4 + r) * 64 + lane];
+
+  // ---- lane holds y[m][n .. n+3], m = 16mb + l%16, n = n0 + 16j + 4q
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = mb * 16 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < SNB; ++j) {
+      const int n = n0 + j * 16 + q * 4;
+      const f32x4 v = acc[j][mb];
+      if (gridDim.y > 1) {
+        float* dst = p.part + ((size_t)blockIdx.y * M + m) * N + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) dst[r] = v[r];
+      } else if (p.out_f32) {
+        float* dst = static_cast<float*>(p.y) + (size_t)m * N + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) dst[r] = v[r];
+      } else {
+        __bf16* dst = static_cast<__bf16*>(p.y) + (size_t)m * N + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) dst[r] = f32_to_bf16(v[r]);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 // The wide kernel needs enough 256 x 256 tiles to fill the chip, and 32-bit
@@ -398,7 +551,27 @@ static bool oproj_use_wide(int M, int K, int N) {
   return wide_tiles >= 256 && (long long)K * 2 * WBM < 0x7fffffffLL;
 }
 
+// Skinny FP8 kernel (M <= 64): the number of workgroups along K.  Each takes
+// a slice of K that is a multiple of 512 and at most 1024 (its x slice fits
+// in LDS); more slices while the grid is under one workgroup per compute
+// unit.  0: the shape does not fit (the tiled kernel takes it).
+static int oproj_skinny_splits(int M, int K, int N) {
+  if (M > 64 || K % 512 != 0) return 0;
+  const long groups = (N + SF - 1) / SF;
+  int s = 0;
+  for (int c = 1; c <= K / 512; ++c)
+    if (K % (512 * c) == 0 && K / c <= SKC_MAX) {
+      s = c;
+      break;
+    }
+  if (s == 0) return 0;
+  while (groups * s < 256 && K % (512 * 2 * s) == 0) s *= 2;
+  return s;
+}
+
 int oproj_choose_splits(int M, int K, int N, bool fp8) {
+  const int sk = fp8 ? oproj_skinny_splits(M, K, N) : 0;
+  if (sk > 0) return sk;
   if (!fp8 && oproj_use_wide(M, K, N)) return 1;
   const long tiles = (long)((M + OBM - 1) / OBM) * ((N + OBN - 1) / OBN);
   const int slabs = K / OBK;
@@ -423,6 +596,12 @@ hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
     hipLaunchKernelGGL(oproj_wide_kernel, dim3((unsigned)wide_tiles), dim3(WNT), 0, stream, p);
     return hipGetLastError();
   }
+  const int sk = p.w8 ? oproj_skinny_splits(p.M, p.K, p.N) : 0;
+  if (sk > 0) {
+    const long groups = (p.N + SF - 1) / SF;
+    if (groups > 0x7fffffffL || p.splits != sk) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(oproj_skinny_fp8_kernel, dim3((unsigned)groups, (unsigned)sk), dim3(256), 0, stream, p);
+  } else {
   const long tiles = (long)((p.M + OBM - 1) / OBM) * ((p.N + OBN - 1) / OBN);
   if (tiles <= 0 || tiles > 0x7fffffffL || p.splits < 1 || p.splits > 65535)
     return hipErrorInvalidConfiguration;
@@ -430,6 +609,7 @@ hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
     hipLaunchKernelGGL(oproj_kernel<true>, dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
   else
     hipLaunchKernelGGL(oproj_kernel<false>, dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const size_t total = (size_t)p.M * p.N;
