@@ -76,6 +76,8 @@ def _load():
     lib.oracle_append_kv.restype = I
     lib.oracle_prefill_chunk.argtypes = [P, P, P, P, P, P, I, I, D, I, I, I, I, P, P, I]
     lib.oracle_prefill_chunk.restype = I
+    lib.oracle_up_project.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P, P, I]
+    lib.oracle_up_project.restype = I
     lib.oracle_out_proj.argtypes = [P, P, I, I, I, P, I]
     lib.oracle_out_proj.restype = I
     lib.oracle_out_proj_rows.argtypes = [P, P, I, I, I, I, P, P, I]
@@ -313,6 +315,35 @@ def decode_latent(q_nope, q_pe, ckv, kpe, w_kv_b, R, q_pos, scale, sel=None, rou
     if rc:
         raise ValueError(f"oracle_decode_latent failed ({rc})")
     return out, lse
+
+
+def up_project(q_lat, ckv, w_q_b, w_kv_b, rows=None, nthreads=None):
+    """The MLA up-projection: q_lat [B,T,1536] and ckv [B,T,512] (bf16 bits),
+    w_q_b [H*192,1536] (rows h*192.. q_nope, h*192+128.. q_pe of head h) and
+    w_kv_b [H*256,512] (rows h*256.. nope key, h*256+128.. value).  Returns
+    (q_nope, q_pe, k_nope, v) in double, unrounded: [B,H,T,d] each, or with
+    ``rows`` (flat indices b*T + t) [n,H,d]."""
+    lib = _load()
+    q_lat, ckv, w_q_b, w_kv_b = map(_u16, (q_lat, ckv, w_q_b, w_kv_b))
+    if q_lat.ndim != 3 or q_lat.shape[2] != 1536 or ckv.shape != q_lat.shape[:2] + (512,):
+        raise ValueError("q_lat must be [B,T,1536] and ckv [B,T,512]")
+    B, T, _ = q_lat.shape
+    H = w_q_b.shape[0] // 192
+    if w_q_b.shape != (H * 192, 1536) or w_kv_b.shape != (H * 256, 512) or H < 1:
+        raise ValueError("w_q_b must be [H*192,1536] and w_kv_b [H*256,512]")
+    if rows is None:
+        n, prow = 0, None
+        lead = (B, H, T)
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int32).ravel()
+        n, prow = rows.size, _p(rows)
+        lead = (n, H)
+    outs = [np.empty(lead + (d,), dtype=np.float64) for d in (128, 64, 128, 128)]
+    rc = lib.oracle_up_project(_p(q_lat), _p(ckv), _p(w_q_b), _p(w_kv_b), B, T, H, n, prow,
+                               *[_p(o) for o in outs], nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_up_project failed ({rc})")
+    return tuple(outs)
 
 
 def e4m3_to_double(b):

@@ -606,6 +606,74 @@ int oracle_out_proj_rows(const uint16_t *x, const uint16_t *w, int M, int K, int
   return run_units(oproj_unit, &c, (long)n_rows, (size_t)K, nthreads);
 }
 
+/* ------------------------------------------------------ up-projection ---- */
+
+/* The MLA up-projection in front of the attention ([CONFIG]: q_lora_rank
+ * 1536, kv_lora_rank 512, 64 heads of nope 128 + rope 64 query features and
+ * 128 value features; the pages omit its code, and [MIX] "mla-prefill" joins
+ * each head's query as nope then rope and reads the key's nope part and the
+ * value per head).  Two linear maps without bias, held as linear layers hold
+ * them (one row of inputs per output feature):
+ *   q  = q_lat · w_q_bᵀ,  w_q_b [H*192][1536]: head h owns rows h*192 ..,
+ *        the first 128 its q_nope features, the last 64 its (unrotated) q_pe;
+ *   kv = ckv · w_kv_bᵀ,   w_kv_b [H*256][512]: head h owns rows h*256 ..,
+ *        the first 128 its nope key features, the last 128 its value.
+ * Sums in k order in double, unrounded (the model rounds the products to its
+ * bf16 tensors; the tests do so where they compare bf16).  q_lat [B][T][1536],
+ * ckv [B][T][512].  rows NULL: every (b, t), outputs q_nope [B][H][T][128],
+ * q_pe [B][H][T][64], k_nope [B][H][T][128], v [B][H][T][128]; else n_rows
+ * flat row indices b*T + t and outputs [n_rows][H][d]. */
+#define OR_QRANK 1536
+
+typedef struct {
+  const uint16_t *q_lat, *ckv, *w_q_b, *w_kv_b;
+  int B, T, H;
+  const int *rows;
+  double *q_nope, *q_pe, *k_nope, *v;
+} upproj_ctx;
+
+static double dot_bf16(const double *x, const uint16_t *w, int n) {
+  double acc = 0.0;
+  for (int k = 0; k < n; k++) acc += x[k] * widen(w[k]);
+  return acc;
+}
+
+static void upproj_unit(void *vctx, long unit, double *scratch) {
+  upproj_ctx *c = (upproj_ctx *)vctx;
+  const long m = c->rows ? c->rows[unit] : unit;
+  const long b = m / c->T, t = m % c->T;
+  double *xq = scratch, *xc = scratch + OR_QRANK;
+  for (int k = 0; k < OR_QRANK; k++) xq[k] = widen(c->q_lat[m * OR_QRANK + k]);
+  for (int k = 0; k < OR_LATENT; k++) xc[k] = widen(c->ckv[m * OR_LATENT + k]);
+  for (int h = 0; h < c->H; h++) {
+    /* destination row of (b, h, t) in each output */
+    const long r = c->rows ? unit * c->H + h : ((long)b * c->H + h) * c->T + t;
+    const uint16_t *wq = c->w_q_b + (size_t)h * (OR_NOPE + OR_ROPE) * OR_QRANK;
+    const uint16_t *wkv = c->w_kv_b + (size_t)h * (OR_NOPE + OR_VDIM) * OR_LATENT;
+    for (int d = 0; d < OR_NOPE; d++) c->q_nope[r * OR_NOPE + d] = dot_bf16(xq, wq + (size_t)d * OR_QRANK, OR_QRANK);
+    for (int d = 0; d < OR_ROPE; d++)
+      c->q_pe[r * OR_ROPE + d] = dot_bf16(xq, wq + (size_t)(OR_NOPE + d) * OR_QRANK, OR_QRANK);
+    for (int d = 0; d < OR_NOPE; d++)
+      c->k_nope[r * OR_NOPE + d] = dot_bf16(xc, wkv + (size_t)d * OR_LATENT, OR_LATENT);
+    for (int d = 0; d < OR_VDIM; d++)
+      c->v[r * OR_VDIM + d] = dot_bf16(xc, wkv + (size_t)(OR_NOPE + d) * OR_LATENT, OR_LATENT);
+  }
+}
+
+int oracle_up_project(const uint16_t *q_lat, const uint16_t *ckv, const uint16_t *w_q_b,
+                      const uint16_t *w_kv_b, int B, int T, int H, int n_rows, const int *rows,
+                      double *q_nope, double *q_pe, double *k_nope, double *v, int nthreads) {
+  if (B <= 0 || T <= 0 || H <= 0) return 1;
+  if (rows) {
+    if (n_rows < 0) return 1;
+    for (int i = 0; i < n_rows; i++)
+      if (rows[i] < 0 || (long)rows[i] >= (long)B * T) return 1;
+  }
+  upproj_ctx c = {q_lat, ckv, w_q_b, w_kv_b, B, T, H, rows, q_nope, q_pe, k_nope, v};
+  const long units = rows ? (long)n_rows : (long)B * T;
+  return run_units(upproj_unit, &c, units, (size_t)(OR_QRANK + OR_LATENT), nthreads);
+}
+
 /* ----------------------------------------------------------- fp8 weights ---- */
 
 /* The checkpoint stores projection weights in FP8 with one float32 scale per

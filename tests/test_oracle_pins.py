@@ -466,6 +466,88 @@ def test_decode_latent_equals_joined_decode_and_rows():
         assert np.array_equal(ro[i], got[b, h * 128:(h + 1) * 128]) and rl[i] == gl[b, h]
 
 
+# --------------------------------------------------------- up-projection
+
+def up_case(B, T, H, seed):
+    return (rand_bits((B, T, 1536), seed), rand_bits((B, T, 512), seed + 1),
+            rand_bits((H * 192, 1536), seed + 2, std=0.02), rand_bits((H * 256, 512), seed + 3, std=0.02))
+
+
+def test_up_project_selection_weights():
+    """One-hot weight rows (a different latent index per output feature):
+    every output is one latent element exactly, at the place the head split
+    puts it -- head h's q_nope from rows h*192.., its q_pe from h*192+128..,
+    its nope key from rows h*256.., its value from h*256+128.. (pins the head
+    and part slicing and the [B,H,T,d] layout)."""
+    B, T, H = 2, 5, 3
+    ql, ckv, _, _ = up_case(B, T, H, 2400)
+    rng = np.random.default_rng(2405)
+    iq = rng.integers(0, 1536, H * 192)
+    ik = rng.integers(0, 512, H * 256)
+    wq = np.zeros((H * 192, 1536), np.uint16)
+    wq[np.arange(H * 192), iq] = 0x3F80
+    wk = np.zeros((H * 256, 512), np.uint16)
+    wk[np.arange(H * 256), ik] = 0x3F80
+    qn, qp, kn, v = oracle.up_project(ql, ckv, wq, wk)
+    Q, C = widen(ql), widen(ckv)
+    for h in range(H):
+        assert np.array_equal(qn[:, h], Q[:, :, iq[h * 192:h * 192 + 128]])
+        assert np.array_equal(qp[:, h], Q[:, :, iq[h * 192 + 128:(h + 1) * 192]])
+        assert np.array_equal(kn[:, h], C[:, :, ik[h * 256:h * 256 + 128]])
+        assert np.array_equal(v[:, h], C[:, :, ik[h * 256 + 128:(h + 1) * 256]])
+
+
+def test_up_project_one_hot_latent_reads_weight_columns():
+    """A latent row that is one-hot at index k gives, for every head and
+    feature, the weight's k-th column (the transposition of the linear layer:
+    y = x · Wᵀ with W [out, in]); rows are independent of each other."""
+    B, T, H = 1, 4, 2
+    _, _, wq, wk = up_case(B, T, H, 2500)
+    ql = np.zeros((B, T, 1536), np.uint16)
+    ckv = np.zeros((B, T, 512), np.uint16)
+    ks_q, ks_c = [7, 1535, 0, 800], [3, 511, 256, 0]
+    for t in range(T):
+        ql[0, t, ks_q[t]] = 0x3F80
+        ckv[0, t, ks_c[t]] = 0x3F80
+    qn, qp, kn, v = oracle.up_project(ql, ckv, wq, wk)
+    Wq, Wk = widen(wq).reshape(H, 192, 1536), widen(wk).reshape(H, 256, 512)
+    for t in range(T):
+        assert np.array_equal(qn[0, :, t], Wq[:, :128, ks_q[t]])
+        assert np.array_equal(qp[0, :, t], Wq[:, 128:, ks_q[t]])
+        assert np.array_equal(kn[0, :, t], Wk[:, :128, ks_c[t]])
+        assert np.array_equal(v[0, :, t], Wk[:, 128:, ks_c[t]])
+
+
+def test_up_project_feeds_the_latent_decode():
+    """Keys and values up-projected from a latent cache, rounded to bf16 and
+    attended by the shared-rotary decode, give the latent decode's output
+    (whose own up-projection is separate code): the kv half agrees with the
+    latent reading.  Random weights are checked against numpy's float64
+    matmul, and selected rows equal the full result."""
+    B, T, H = 2, 19, 3
+    ql, ckv, wq, wk = up_case(B, T, H, 2600)
+    qn, qp, kn, v = oracle.up_project(ql, ckv, wq, wk)
+    q = widen(ql) @ widen(wq).T
+    kv = widen(ckv) @ widen(wk).T
+    qh, kvh = q.reshape(B, T, H, 192).transpose(0, 2, 1, 3), kv.reshape(B, T, H, 256).transpose(0, 2, 1, 3)
+    assert np.max(np.abs(qn - qh[..., :128])) < 1e-12 and np.max(np.abs(qp - qh[..., 128:])) < 1e-12
+    assert np.max(np.abs(kn - kvh[..., :128])) < 1e-12 and np.max(np.abs(v - kvh[..., 128:])) < 1e-12
+    qpos = T + 4
+    R = inputs.rope_angles(qpos + 1)
+    dq_n, dq_p = rand_bits((B, H, 128), 2610), rand_bits((B, H, 64), 2611)
+    kpe = rand_bits((B, T, 64), 2612)
+    want, wl = oracle.decode_latent(dq_n, dq_p, ckv, kpe, wk, R, qpos, SCALE)
+    got, gl = oracle.decode_shared_kpe(dq_n, dq_p, to_bits(rne_bf16(kn)), kpe, to_bits(rne_bf16(v)), R,
+                                       qpos, SCALE)
+    assert np.max(np.abs(got - want)) < 1e-13 and np.max(np.abs(gl - wl)) < 1e-13
+    rows = np.array([T + 3, 0, 2 * T - 1], np.int32)
+    r = oracle.up_project(ql, ckv, wq, wk, rows=rows)
+    for i, m in enumerate(rows):
+        b, t = divmod(int(m), T)
+        for full, part in zip((qn, qp, kn, v), r):
+            assert np.array_equal(part[i], full[b, :, t])
+
+
 def test_decode_rows_equal_full():
     B, H, L = 2, 3, 30
     qn = rand_bits((B, H, 128), 1400)
