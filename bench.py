@@ -180,6 +180,21 @@ def other_configs(mla, inputs, w_o, scale, dev, calls=10):
         "attention_frac_peak": fl / tatt / 1e9 / PEAK_BF16_TFLOPS}
     del q_nope, q_pe, k_nope, k_pe, v, kc, pc, vc, o, ws
     torch.cuda.empty_cache()
+    # The up-projection in front of the prefill at B=4, T=4096, 64 heads: q
+    # from the rank-1536 latent, nope key and value from the rank-512 latent.
+    B, T, H = 4, 4096, 64
+    print(f"other config: up-projection (B={B} T={T})", file=sys.stderr, flush=True)
+    d = inputs.up_project_inputs(B, T, H, workload=3, device=dev)
+    outs = [torch.empty((B, H, T, w), dtype=torch.bfloat16, device=dev) for w in (128, 64, 128, 128)]
+    fup = lambda: mla.mla_up_project(d["q_lat"], d["ckv"], d["w_q_b"], d["w_kv_b"], outs=outs)
+    tup = med(fup)
+    fl = 2.0 * B * T * (1536 * H * 192 + 512 * H * 256)
+    nbytes = 2 * (B * T * (1536 + 512) + H * 192 * 1536 + H * 256 * 512 + B * H * T * (128 + 64 + 128 + 128))
+    out[f"up_project_B{B}_T{T}_H{H}"] = {
+        "ms": tup, "tflops": fl / tup / 1e9, "frac_peak": fl / tup / 1e9 / PEAK_BF16_TFLOPS,
+        "hbm_gbps": nbytes / tup / 1e6, "per_call": f"{fl:.4e} flops, {nbytes} bytes"}
+    del d, outs
+    torch.cuda.empty_cache()
     return out
 
 

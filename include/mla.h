@@ -275,6 +275,36 @@ int mla_out_proj_fp8(const mla_bf16 *x, const uint8_t *w8, const float *w_scale,
                      int K, int N, void *workspace, size_t workspace_bytes, uint32_t flags,
                      void *stream);
 
+/* ------------------------------------------------------- up-projection --
+ * The MLA up-projection in front of the attention: the query from its
+ * rank-1536 latent and the nope key and value from the rank-512 latent
+ * (page "Block input", config.json: q_lora_rank 1536, kv_lora_rank 512, 64
+ * heads of 128 nope + 64 rope query features and 128 value features; page
+ * "Kimi K2 · Mix and project", excerpt "mla-prefill": each head's query is
+ * its nope part then its rope part, and the key's nope part and the value
+ * are read per head).  Two linear maps without bias, each weight held as the
+ * linear layer holds it (row n = the input weights of output feature n):
+ *
+ *   q_lat   [B, T, 1536]  bf16   the query latent (after its normalisation)
+ *   ckv     [B, T, 512]   bf16   the key/value latent (after its normalisation)
+ *   w_q_b   [H*192, 1536] bf16   rows h*192 .. +127: head h's q_nope features,
+ *                                rows h*192+128 .. +63: its q_pe features
+ *   w_kv_b  [H*256, 512]  bf16   rows h*256 .. +127: head h's nope key,
+ *                                rows h*256+128 .. +127: its value
+ *   q_nope  [B, H, T, 128], q_pe [B, H, T, 64] (unrotated: the rotary step is
+ *   the attention's), k_nope [B, H, T, 128], v [B, H, T, 128]: outputs in the
+ *   layouts mla_attend_prefill takes; bf16, or float32 with MLA_OUT_F32.
+ *
+ * Float32 accumulation over the latent, one rounding per output.  No
+ * workspace.  Errors: a NULL pointer MLA_ERR_NULL; B, T, H < 1 or too large
+ * MLA_ERR_DIM; a pointer not 16-byte aligned MLA_ERR_ALIGN; an output
+ * overlapping an input or another output MLA_ERR_ALIAS; unknown flag bits
+ * MLA_ERR_FLAGS.  Asynchronous on `stream`.
+ */
+int mla_up_project(const mla_bf16 *q_lat, const mla_bf16 *ckv, const mla_bf16 *w_q_b,
+                   const mla_bf16 *w_kv_b, int B, int T, int H, void *q_nope, void *q_pe,
+                   void *k_nope, void *v, uint32_t flags, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -254,3 +254,23 @@ def test_oproj_fp8_workspace():
 ])
 def test_oproj_rejects(kw, code):
     assert oproj(**kw) == code
+
+
+def up(**kw):
+    a = dict(ql=A[0], c=A[1], wq=A[2], wk=A[3], B=4, T=4096, H=64, qn=A[4], qp=A[5], kn=A[6], v=A[7],
+             flags=0)
+    a.update(kw)
+    return mla.lib().mla_up_project(a["ql"], a["c"], a["wq"], a["wk"], a["B"], a["T"], a["H"], a["qn"],
+                                    a["qp"], a["kn"], a["v"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ql=None), NULL), (dict(wk=None), NULL), (dict(v=None), NULL), (dict(flags=4), FLAGS),
+    (dict(B=0), DIM), (dict(T=-1), DIM), (dict(H=0), DIM), (dict(B=1 << 20, T=1 << 12), DIM),
+    (dict(qp=ctypes.c_void_p(5 * 16 * GB + 8)), ALIGN),
+    (dict(kn=ctypes.c_void_p(1 * 16 * GB + 64)), ALIAS),   # k_nope over q_lat
+    (dict(v=ctypes.c_void_p(4 * 16 * GB + 256)), ALIAS),   # v over w_kv_b
+    (dict(v=ctypes.c_void_p(5 * 16 * GB + 256)), ALIAS),   # v over q_nope
+])
+def test_up_project_rejects(kw, code):
+    assert up(**kw) == code

@@ -20,7 +20,7 @@ __all__ = [
     "mla_decode_latent_workspace_bytes", "mla_attend_decode_latent",
     "mla_append_kv", "mla_prefill_chunk_workspace_bytes", "mla_attend_prefill_chunk",
     "mla_out_proj_workspace_bytes", "mla_out_proj_fp8_workspace_bytes", "mla_out_proj_fp8",
-    "mla_out_proj", "NOPE", "ROPE", "VDIM", "PAIRS",
+    "mla_out_proj", "mla_up_project", "NOPE", "ROPE", "VDIM", "PAIRS", "LATENT", "Q_RANK",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 MLA_OUT_F32 = 0x1
 NOPE, ROPE, VDIM, PAIRS = 128, 64, 128, 32
 LATENT = 512  # kv_lora_rank
+Q_RANK = 1536  # q_lora_rank
 
 _lib = None
 
@@ -85,6 +86,8 @@ def lib():
     L.mla_out_proj_fp8.argtypes = [P, P, P, P, I, I, I, P, Z, U, P]
     L.mla_out_proj_fp8.restype = I
     L.mla_out_proj.restype = I
+    L.mla_up_project.argtypes = [P, P, P, P, I, I, I, P, P, P, P, U, P]
+    L.mla_up_project.restype = I
     _lib = L
     return L
 
@@ -348,6 +351,35 @@ def mla_out_proj(x, w_o, *, y=None, out_f32=False, workspace=None, stream=None):
     if rc:
         raise MlaError(rc, "mla_out_proj")
     return y
+
+
+def mla_up_project(q_lat, ckv, w_q_b, w_kv_b, *, outs=None, out_f32=False, stream=None):
+    """The MLA up-projection: q_lat [B,T,1536] and ckv [B,T,512] bf16, w_q_b
+    [H*192,1536] and w_kv_b [H*256,512] bf16.  Returns (q_nope [B,H,T,128],
+    q_pe [B,H,T,64] unrotated, k_nope [B,H,T,128], v [B,H,T,128]), bf16 or
+    float32; ``outs`` may hold the four output tensors."""
+    torch = _torch()
+    if q_lat.dim() != 3 or w_q_b.dim() != 2:
+        raise ValueError("q_lat must be [B, T, 1536] and w_q_b [H*192, 1536]")
+    B, T = q_lat.shape[:2]
+    H = w_q_b.shape[0] // (NOPE + ROPE)
+    dev = q_lat.device
+    _check(q_lat, "q_lat", torch.bfloat16, (B, T, Q_RANK), dev)
+    _check(ckv, "ckv", torch.bfloat16, (B, T, LATENT), dev)
+    _check(w_q_b, "w_q_b", torch.bfloat16, (H * (NOPE + ROPE), Q_RANK), dev)
+    _check(w_kv_b, "w_kv_b", torch.bfloat16, (H * (NOPE + VDIM), LATENT), dev)
+    odt = torch.float32 if out_f32 else torch.bfloat16
+    shapes = [(B, H, T, NOPE), (B, H, T, ROPE), (B, H, T, NOPE), (B, H, T, VDIM)]
+    if outs is None:
+        outs = [torch.empty(sh, dtype=odt, device=dev) for sh in shapes]
+    for t, sh, name in zip(outs, shapes, ("q_nope", "q_pe", "k_nope", "v")):
+        _check(t, name, odt, sh, dev)
+    rc = lib().mla_up_project(_ptr(q_lat), _ptr(ckv), _ptr(w_q_b), _ptr(w_kv_b), B, T, H,
+                              *[_ptr(t) for t in outs], MLA_OUT_F32 if out_f32 else 0,
+                              _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_up_project")
+    return tuple(outs)
 
 
 def mla_out_proj_fp8(x, w8, w_scale, *, y=None, out_f32=False, workspace=None, stream=None):

@@ -468,6 +468,64 @@ int mla_out_proj(const mla_bf16* x, const mla_bf16* w_o, void* y, int M, int K, 
   return MLA_OK;
 }
 
+int mla_up_project(const mla_bf16* q_lat, const mla_bf16* ckv, const mla_bf16* w_q_b,
+                   const mla_bf16* w_kv_b, int B, int T, int H, void* q_nope, void* q_pe,
+                   void* k_nope, void* v, uint32_t flags, void* stream) {
+  if (!q_lat || !ckv || !w_q_b || !w_kv_b || !q_nope || !q_pe || !k_nope || !v) return MLA_ERR_NULL;
+  if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
+  if (!dims_ok(B, T, H, mla::kQK + kV) || (long long)B * T > 0x7fffffffLL ||
+      (long long)H * (kNope + kV) > 0x7fffffffLL)
+    return MLA_ERR_DIM;
+  if (!aligned16(q_lat) || !aligned16(ckv) || !aligned16(w_q_b) || !aligned16(w_kv_b) ||
+      !aligned16(q_nope) || !aligned16(q_pe) || !aligned16(k_nope) || !aligned16(v))
+    return MLA_ERR_ALIGN;
+  const size_t M = (size_t)B * T, rows = (size_t)B * H * T;
+  const size_t elt = (flags & MLA_OUT_F32) ? 4 : 2;
+  const Range in[] = {{q_lat, M * mla::kQRank * 2},
+                      {ckv, M * mla::kLatent * 2},
+                      {w_q_b, (size_t)H * kQK * mla::kQRank * 2},
+                      {w_kv_b, (size_t)H * (kNope + kV) * mla::kLatent * 2}};
+  const Range outs[] = {{q_nope, rows * kNope * elt},
+                        {q_pe, rows * kRope * elt},
+                        {k_nope, rows * kNope * elt},
+                        {v, rows * kV * elt}};
+  if (any_alias(in, 4, outs, 4)) return MLA_ERR_ALIAS;
+  const int dev = check_device();
+  if (dev != MLA_OK) return dev;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  mla::OprojParams p;
+  p.part = nullptr;
+  p.M = (int)M;
+  p.splits = 1;
+  p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
+  p.group_m = 0;
+  p.w8 = nullptr;
+  p.w_scale = nullptr;
+  p.T = T;
+  p.d0 = kNope;
+  // q = q_lat · w_q_bᵀ: per head 128 q_nope then 64 q_pe features
+  p.x = q_lat;
+  p.w = w_q_b;
+  p.K = mla::kQRank;
+  p.N = H * kQK;
+  p.hd = kQK;
+  p.y = q_nope;
+  p.y1 = q_pe;
+  (void)hipGetLastError();
+  if (mla::launch_oproj(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  // kv = ckv · w_kv_bᵀ: per head 128 nope key then 128 value features
+  p.x = ckv;
+  p.w = w_kv_b;
+  p.K = mla::kLatent;
+  p.N = H * (kNope + kV);
+  p.hd = kNope + kV;
+  p.y = k_nope;
+  p.y1 = v;
+  if (mla::launch_oproj(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
 size_t mla_out_proj_fp8_workspace_bytes(int M, int K, int N) {
   if (!dims_ok(M, K, N, 1) || K % 128 != 0) return 0;
   return oproj_ws_bytes(M, N, mla::oproj_choose_splits(M, K, N, true));

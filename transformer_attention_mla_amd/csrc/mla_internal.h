@@ -122,6 +122,9 @@ LatentWorkspace latent_workspace_layout(int B, int H, int splits);
 int latent_choose_splits(int B, int L, int requested);
 hipError_t launch_decode_latent(const LatentParams& p, hipStream_t stream);
 
+// ---------------------------------------------------------- up-projection --
+constexpr int kQRank = 1536;  // q_lora_rank
+
 // ----------------------------------------------------------------- o_proj --
 struct OprojParams {
   const uint16_t* x;  // [M][K]
@@ -134,6 +137,11 @@ struct OprojParams {
   int group_m;        // wide kernel: m-tiles per group of the tile order
   const uint8_t* w8;      // FP8 weight [N][K] (e4m3) instead of w, or null
   const float* w_scale;   // its float32 scales, [ceil(N/128)][ceil(K/128)]
+  // Head-major split store (hd > 0; splits 1, bf16 weight): row m = b*T + t,
+  // column n = h*hd + d goes to y [B][H][T][d0] at d < d0, else to y1
+  // [B][H][T][hd-d0] at d - d0 (H = N / hd; hd and d0 multiples of 32).
+  int hd = 0, d0 = 0, T = 0;
+  void* y1 = nullptr;
 };
 
 int oproj_choose_splits(int M, int K, int N, bool fp8 = false);

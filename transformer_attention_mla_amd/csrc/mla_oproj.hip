@@ -60,6 +60,63 @@ __device__ __forceinline__ u32x4 dequant8(u32x2 raw, float s) {
   return r;
 }
 
+// Output features n .. n+3 (n a multiple of 4) of row m, unless they are past
+// N: row-major y [M][N] in float32 or bf16.
+__device__ __forceinline__ void store_y4(const OprojParams& p, int m, int n, float v0, float v1,
+                                         float v2, float v3) {
+  const int N = p.N;
+  if (p.out_f32) {
+    float* dst = static_cast<float*>(p.y) + (size_t)m * N + n;
+    if (n + 3 < N && (N & 3) == 0) {
+      *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
+    } else {
+      if (n < N) dst[0] = v0;
+      if (n + 1 < N) dst[1] = v1;
+      if (n + 2 < N) dst[2] = v2;
+      if (n + 3 < N) dst[3] = v3;
+    }
+  } else {
+    __bf16* dst = static_cast<__bf16*>(p.y) + (size_t)m * N + n;
+    if (n + 3 < N && (N & 3) == 0) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+    } else {
+      if (n < N) dst[0] = f32_to_bf16(v0);
+      if (n + 1 < N) dst[1] = f32_to_bf16(v1);
+      if (n + 2 < N) dst[2] = f32_to_bf16(v2);
+      if (n + 3 < N) dst[3] = f32_to_bf16(v3);
+    }
+  }
+}
+
+// Head-major split store.  Row m = b*T + t maps to split_row(m) = b*H*T + t;
+// a block of 32 output features from nb (a multiple of 32; hd, d0 and N are
+// multiples of 32, so the block lies in one part of one head) to split_col.
+struct SplitCol {
+  void* base;       // y or y1
+  size_t head_off;  // h*T rows
+  int width, d;     // the part's row width and the block's first feature in it
+};
+__device__ __forceinline__ size_t split_row(const OprojParams& p, int m) {
+  const int b = m / p.T;
+  return (size_t)b * (p.N / p.hd) * p.T + (m - b * p.T);
+}
+__device__ __forceinline__ SplitCol split_col(const OprojParams& p, int nb) {
+  const int h = nb / p.hd, d = nb - h * p.hd;
+  const bool first = d < p.d0;
+  return SplitCol{first ? p.y : p.y1, (size_t)h * p.T, first ? p.d0 : p.hd - p.d0,
+                  first ? d : d - p.d0};
+}
+// Features c.d + dn .. +3 of the block for the row at split_row r.
+__device__ __forceinline__ void store_split4(const OprojParams& p, const SplitCol& c, size_t r, int dn,
+                                             float v0, float v1, float v2, float v3) {
+  const size_t off = (r + c.head_off) * c.width + c.d + dn;
+  if (p.out_f32)
+    *reinterpret_cast<f32x4*>(static_cast<float*>(c.base) + off) = f32x4{v0, v1, v2, v3};
+  else
+    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(c.base) + off) =
+        u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sW[OBN * OBK];
@@ -150,6 +207,25 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
   }
 
   // ---- epilogue: lane holds y[m][n..n+3] for m = m-block + ln
+  if (p.hd > 0) {
+#pragma unroll
+    for (int jm = 0; jm < OTM; ++jm) {
+      const int m = m0 + wm * (OTM * 32) + jm * 32 + ln;
+      if (m >= M) continue;
+      const size_t r = split_row(p, m);
+#pragma unroll
+      for (int i = 0; i < OTN; ++i) {
+        const int nb = n0 + wn * (OTN * 32) + i * 32;
+        if (nb >= N) continue;
+        const SplitCol c = split_col(p, nb);
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          store_split4(p, c, r, gq * 8 + hf * 4, acc[i][jm][gq * 4 + 0], acc[i][jm][gq * 4 + 1],
+                       acc[i][jm][gq * 4 + 2], acc[i][jm][gq * 4 + 3]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int jm = 0; jm < OTM; ++jm) {
     const int m = m0 + wm * (OTM * 32) + jm * 32 + ln;
@@ -171,26 +247,8 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
             if (n + 2 < N) dst[2] = v2;
             if (n + 3 < N) dst[3] = v3;
           }
-        } else if (p.out_f32) {
-          float* dst = static_cast<float*>(p.y) + (size_t)m * N + n;
-          if (n + 3 < N && (N & 3) == 0) {
-            *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
-          } else {
-            if (n < N) dst[0] = v0;
-            if (n + 1 < N) dst[1] = v1;
-            if (n + 2 < N) dst[2] = v2;
-            if (n + 3 < N) dst[3] = v3;
-          }
         } else {
-          __bf16* dst = static_cast<__bf16*>(p.y) + (size_t)m * N + n;
-          if (n + 3 < N && (N & 3) == 0) {
-            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          } else {
-            if (n < N) dst[0] = f32_to_bf16(v0);
-            if (n + 1 < N) dst[1] = f32_to_bf16(v1);
-            if (n + 2 < N) dst[2] = f32_to_bf16(v2);
-            if (n + 3 < N) dst[3] = f32_to_bf16(v3);
-          }
+          store_y4(p, m, n, v0, v1, v2, v3);
         }
       }
   }
@@ -339,6 +397,25 @@ __global__ __launch_bounds__(WNT) void oproj_wide_kernel(OprojParams p) {
     mma(f1);
   }
 
+  if (p.hd > 0) {
+#pragma unroll
+    for (int jm = 0; jm < WTM; ++jm) {
+      const int m = m0 + wm * (WTM * 32) + jm * 32 + ln;
+      if (m >= M) continue;
+      const size_t r = split_row(p, m);
+#pragma unroll
+      for (int i = 0; i < WTN; ++i) {
+        const int nb = n0 + wn * (WTN * 32) + i * 32;
+        if (nb >= N) continue;
+        const SplitCol c = split_col(p, nb);
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          store_split4(p, c, r, gq * 8 + hf * 4, acc[i][jm][gq * 4 + 0], acc[i][jm][gq * 4 + 1],
+                       acc[i][jm][gq * 4 + 2], acc[i][jm][gq * 4 + 3]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int jm = 0; jm < WTM; ++jm) {
     const int m = m0 + wm * (WTM * 32) + jm * 32 + ln;
@@ -350,27 +427,7 @@ __global__ __launch_bounds__(WNT) void oproj_wide_kernel(OprojParams p) {
         const int n = n0 + wn * (WTN * 32) + i * 32 + gq * 8 + hf * 4;
         const float v0 = acc[i][jm][gq * 4 + 0], v1 = acc[i][jm][gq * 4 + 1];
         const float v2 = acc[i][jm][gq * 4 + 2], v3 = acc[i][jm][gq * 4 + 3];
-        if (p.out_f32) {
-          float* dst = static_cast<float*>(p.y) + (size_t)m * N + n;
-          if (n + 3 < N && (N & 3) == 0) {
-            *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
-          } else {
-            if (n < N) dst[0] = v0;
-            if (n + 1 < N) dst[1] = v1;
-            if (n + 2 < N) dst[2] = v2;
-            if (n + 3 < N) dst[3] = v3;
-          }
-        } else {
-          __bf16* dst = static_cast<__bf16*>(p.y) + (size_t)m * N + n;
-          if (n + 3 < N && (N & 3) == 0) {
-            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          } else {
-            if (n < N) dst[0] = f32_to_bf16(v0);
-            if (n + 1 < N) dst[1] = f32_to_bf16(v1);
-            if (n + 2 < N) dst[2] = f32_to_bf16(v2);
-            if (n + 3 < N) dst[3] = f32_to_bf16(v3);
-          }
-        }
+        store_y4(p, m, n, v0, v1, v2, v3);
       }
   }
 }
@@ -589,6 +646,9 @@ int oproj_choose_splits(int M, int K, int N, bool fp8) {
 
 hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
   OprojParams p = p_in;
+  if (p.hd > 0 && (p.splits != 1 || p.w8 || p.T <= 0 || p.M % p.T != 0 || p.N % p.hd != 0 ||
+                   p.hd % 32 != 0 || p.d0 % 32 != 0 || p.d0 <= 0 || p.d0 >= p.hd || !p.y1))
+    return hipErrorInvalidConfiguration;
   if (!p.w8 && p.splits == 1 && oproj_use_wide(p.M, p.K, p.N)) {
     const long wide_tiles = (long)((p.M + WBM - 1) / WBM) * ((p.N + WBN - 1) / WBN);
     if (wide_tiles > 0x7fffffffL) return hipErrorInvalidConfiguration;

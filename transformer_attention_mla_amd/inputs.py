@@ -25,6 +25,7 @@ PAIRS = ROT_DIM // 2
 SEED_Q_NOPE, SEED_Q_PE, SEED_K_NOPE, SEED_K_PE, SEED_V, SEED_WO, SEED_KC, SEED_VC = range(8)
 SEED_KNC, SEED_KPC = 8, 9  # shared-rotary cache layout: nope keys, rope keys
 SEED_CKV, SEED_WKVB = 10, 11  # latent cache, up-projection weight
+SEED_QLAT, SEED_WQB = 12, 13  # query latent, its up-projection weight
 
 # The five workloads: (kind, B, T or L) with 64 heads.
 WORKLOADS = {
@@ -151,6 +152,16 @@ def decode_shared_kpe_inputs(B: int, H: int, L: int, q_pos: int, workload: int =
     R = torch.from_numpy(rope_angles(q_pos + 1)).to(device)
     return dict(q_nope=q_nope, q_pe=q_pe, k_nope_cache=k_nope_cache, kpe_cache=kpe_cache,
                 v_cache=v_cache, R=R, q_pos=q_pos)
+
+
+def up_project_inputs(B: int, T: int, H: int, workload: int = 0, device="cpu"):
+    """The up-projection's inputs: q_lat [B,T,1536] and ckv [B,T,512] (the two
+    latents after their normalisations, unit scale: N(0,1)), w_q_b
+    [H*192,1536] and w_kv_b [H*256,512] N(0, 0.02) (the configuration's
+    initializer range), all bf16."""
+    g = lambda shape, k, std=1.0: normal_bf16(shape, seed_of(workload, k), std=std, device=device)
+    return dict(q_lat=g((B, T, 1536), SEED_QLAT), ckv=g((B, T, 512), SEED_CKV),
+                w_q_b=g((H * 192, 1536), SEED_WQB, 0.02), w_kv_b=g((H * 256, 512), SEED_WKVB, 0.02))
 
 
 def decode_latent_inputs(B: int, H: int, L: int, q_pos: int, workload: int = 0, device="cpu"):
