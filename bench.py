@@ -35,14 +35,14 @@ CSRC = os.path.join(REPO, "transformer_attention_mla_amd", "csrc")
 # bytes written).  Each figure holds only for the kernel source it was taken on,
 # identified by a hash of its files; after any change the figure is dropped.
 MEASURED_TRAFFIC = {
-    "prefill_kernel": ("96fb11d933047611", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
-                       2072185010, "profiles/prefill_kernel_B4_T4096_H64.txt"),
-    "decode_split_kernel": ("74734a96e7bbe6a0", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                            21477504147, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
-    "decode_split_kernel_shared_kpe": ("74734a96e7bbe6a0", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                                       17376421633, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
-    "latent_decode_kernel": ("dc66f75c1d8f1f1d", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
-                             657378975, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
+    "prefill_kernel": ("ce684b201e3d1a48", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
+                       2076978398, "profiles/prefill_kernel_B4_T4096_H64.txt"),
+    "decode_split_kernel": ("ef9b64db157bd59b", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                            21477510335, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
+    "decode_split_kernel_shared_kpe": ("ef9b64db157bd59b", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                                       17375854633, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
+    "latent_decode_kernel": ("6fceba74ac8b333a", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
+                             657383377, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
 }
 
 
