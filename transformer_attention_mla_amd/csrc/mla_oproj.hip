@@ -11,9 +11,9 @@
 // LDS read.  The kernel computes the transposed tile Yᵀ = W·Xᵀ with
 // v_mfma_f32_32x32x16_bf16 so that each lane ends with 4 consecutive output
 // features of one row (one 8- or 16-byte store).  Tiles of 128 (n) × 128 (m)
-// per workgroup of 4 waves; k is staged 64 at a time through registers into
-// XOR-swizzled LDS, the next slab's global loads being issued before the
-// current slab is multiplied.  For small M the K range is split over
+// (× 64 when M <= 64) per workgroup of 4 waves; k is staged 64 at a time
+// through registers into XOR-swizzled LDS, the next slab's global loads being
+// issued before the current slab is multiplied.  For small M the K range is split over
 // workgroups (float32 partials in the caller's workspace, then a reduction
 // kernel) so the weight stream is spread over every compute unit.
 //
@@ -32,13 +32,12 @@ namespace mla {
 namespace {
 
 constexpr int OBN = 128;  // rows of w (output features) per tile
-constexpr int OBM = 128;  // rows of x per tile
+constexpr int OBM = 128;  // rows of x per tile (64 when M <= 64: no idle half tile)
 constexpr int OBK = 64;   // k per LDS slab
 constexpr int OWN = 2;    // waves along n
 constexpr int OWM = 2;    // waves along m
 constexpr int ONT = 64 * OWN * OWM;
 constexpr int OTN = OBN / OWN / 32;  // 32x32 blocks per wave along n
-constexpr int OTM = OBM / OWM / 32;  // along m
 
 // Chunk swizzle for 128-byte LDS rows (8 chunks of 16 B): distinct for any 8
 // consecutive rows and for same-parity rows among 16 consecutive ones.
@@ -117,10 +116,12 @@ __device__ __forceinline__ void store_split4(const OprojParams& p, const SplitCo
         u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
 }
 
-template <bool FP8>
+template <bool FP8, int BM>
 __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
+  constexpr int OTM = BM / OWM / 32;  // 32x32 blocks per wave along m
+  static_assert(OTM >= 1 && BM % (OWM * 32) == 0, "x tile");
   __shared__ __attribute__((aligned(16))) uint16_t sW[OBN * OBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[OBM * OBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[BM * OBK];
 
   const int M = p.M, N = p.N, K = p.K;
   const int tiles_n = (N + OBN - 1) / OBN;
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
   const int split = blockIdx.y;
   const int tn = tile % tiles_n;
   const int tm = tile / tiles_n;
-  const int n0 = tn * OBN, m0 = tm * OBM;
+  const int n0 = tn * OBN, m0 = tm * BM;
   const int kslabs = K / OBK / p.splits;
   const int kbeg = split * kslabs * OBK;
 
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
   const int wn = wave % OWN, wm = wave / OWN;
 
   constexpr int WCH = OBN * 8 / ONT;  // 16-byte chunks per thread per slab
-  constexpr int XCH = OBM * 8 / ONT;
+  constexpr int XCH = BM * 8 / ONT;
   u32x4 rw[WCH], rx[XCH];
   u32x2 rw8[FP8 ? WCH : 1];
   float rs[FP8 ? WCH : 1];
@@ -633,13 +634,15 @@ int oproj_choose_splits(int M, int K, int N, bool fp8) {
   const long tiles = (long)((M + OBM - 1) / OBM) * ((N + OBN - 1) / OBN);
   const int slabs = K / OBK;
   if (tiles >= 256 || slabs <= 1) return 1;
-  // Spread the weight stream over the chip: aim for >= 512 workgroups, keep
-  // >= 4 slabs (256 k) per split, and split K into equal whole slabs.
+  // Spread the weight stream over the chip: aim for >= 256 workgroups (at
+  // M = 64, N = 7168, K = 8192: 8 splits, 448 workgroups, 33 us against
+  // 48 us for 16 splits, whose float32 partials cost more than they spread),
+  // keep >= 4 slabs (256 k) per split, and split K into equal whole slabs.
   int best = 1;
   for (int s = 2; s <= slabs / 4; ++s) {
     if (slabs % s) continue;
     best = s;
-    if (tiles * s >= 512) break;
+    if (tiles * s >= 256) break;
   }
   return best;
 }
@@ -665,10 +668,17 @@ hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
   const long tiles = (long)((p.M + OBM - 1) / OBM) * ((p.N + OBN - 1) / OBN);
   if (tiles <= 0 || tiles > 0x7fffffffL || p.splits < 1 || p.splits > 65535)
     return hipErrorInvalidConfiguration;
-  if (p.w8)
-    hipLaunchKernelGGL(oproj_kernel<true>, dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
+  // M <= 64 is one m-tile at either height; the 64-row tile loads and
+  // multiplies no rows past M.
+  const bool m64 = p.M <= 64;
+  if (p.w8 && m64)
+    hipLaunchKernelGGL((oproj_kernel<true, 64>), dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
+  else if (p.w8)
+    hipLaunchKernelGGL((oproj_kernel<true, OBM>), dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
+  else if (m64)
+    hipLaunchKernelGGL((oproj_kernel<false, 64>), dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
   else
-    hipLaunchKernelGGL(oproj_kernel<false>, dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
+    hipLaunchKernelGGL((oproj_kernel<false, OBM>), dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
