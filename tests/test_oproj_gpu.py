@@ -112,13 +112,13 @@ def test_attention_then_oproj_workload1(gpu_device):
 @pytest.mark.parametrize("M,K,N", [(1, 128, 1), (17, 256, 100), (64, 8192, 7168), (130, 1024, 300),
                                    (300, 384, 129), (1000, 512, 1000), (1, 512, 129), (40, 2048, 1000),
                                    (64, 1024, 7168), (33, 1024, 500), (64, 2048, 225), (16, 4096, 447),
-                                   (64, 16384, 300)])
+                                   (64, 16384, 300), (40, 384, 200), (3, 640, 129)])
 def test_oproj_fp8_parity(M, K, N, gpu_device):
     """The FP8 checkpoint weight, dequantized to bf16 in the kernel's load path:
     against the oracle's projection with the same dequantization.  M <= 64
-    with K a multiple of 512 takes the skinny kernel (x shared through LDS,
-    224 features per workgroup): one or several K slices, N ragged against
-    224 and against 4, M not a multiple of 16."""
+    takes the 64-row tile with 128-deep slabs (one or several K splits, N
+    ragged against the 128-feature tile and against 4, M not a multiple of
+    16); larger M the 128-row tile with 64-deep slabs."""
     say(f"o_proj fp8 parity M={M} K={K} N={N}")
     x = inputs.normal_bf16((M, K), 30 + M)
     w8, sc = inputs.out_proj_weight_fp8(N, K, workload=1)
@@ -138,7 +138,7 @@ def test_oproj_fp8_dequant_exact(M, gpu_device):
     block, so y = x / 8 bit for bit -- the dequantized weight is exactly 0.125
     and zero elsewhere, each output one product; and a second block scale
     pattern (a power of two per block) moves each output by its block's scale.
-    M = 64 takes the skinny kernel, M = 70 the tiled one."""
+    M = 64 takes the 64-row tile with 128-deep slabs, M = 70 the 128-row tile."""
     K, N = 1024, 600
     x = inputs.normal_bf16((M, K), 7)
     w8 = torch.zeros((N, K), dtype=torch.uint8)

@@ -33,7 +33,7 @@ namespace {
 
 constexpr int OBN = 128;  // rows of w (output features) per tile
 constexpr int OBM = 128;  // rows of x per tile (64 when M <= 64: no idle half tile)
-constexpr int OBK = 64;   // k per LDS slab
+constexpr int OBK = 64;   // k per LDS slab (128 for the FP8 weight at M <= 64)
 constexpr int OWN = 2;    // waves along n
 constexpr int OWM = 2;    // waves along m
 constexpr int ONT = 64 * OWN * OWM;
@@ -42,6 +42,8 @@ constexpr int OTN = OBN / OWN / 32;  // 32x32 blocks per wave along n
 // Chunk swizzle for 128-byte LDS rows (8 chunks of 16 B): distinct for any 8
 // consecutive rows and for same-parity rows among 16 consecutive ones.
 __device__ __forceinline__ int rswz(int row) { return (row ^ (row >> 3)) & 7; }
+// The same for 256-byte rows (16 chunks): distinct for any 16 consecutive rows.
+__device__ __forceinline__ int rswz16(int row) { return (row ^ (row >> 4)) & 15; }
 
 // FP8 weights (e4m3, OCP "fn" variant, as the checkpoint stores them with one
 // float32 scale per 128 x 128 block): 8 values, the float32 product with the
@@ -116,12 +118,15 @@ __device__ __forceinline__ void store_split4(const OprojParams& p, const SplitCo
         u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
 }
 
-template <bool FP8, int BM>
+template <bool FP8, int BM, int BK>
 __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
   constexpr int OTM = BM / OWM / 32;  // 32x32 blocks per wave along m
+  constexpr int CH = BK / 8;          // 16-byte chunks per LDS row
   static_assert(OTM >= 1 && BM % (OWM * 32) == 0, "x tile");
-  __shared__ __attribute__((aligned(16))) uint16_t sW[OBN * OBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[BM * OBK];
+  static_assert(CH == 8 || CH == 16, "slab depth");
+  auto swz = [](int row) { return CH == 16 ? rswz16(row) : rswz(row); };
+  __shared__ __attribute__((aligned(16))) uint16_t sW[OBN * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[BM * BK];
 
   const int M = p.M, N = p.N, K = p.K;
   const int tiles_n = (N + OBN - 1) / OBN;
@@ -130,8 +135,8 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
   const int tn = tile % tiles_n;
   const int tm = tile / tiles_n;
   const int n0 = tn * OBN, m0 = tm * BM;
-  const int kslabs = K / OBK / p.splits;
-  const int kbeg = split * kslabs * OBK;
+  const int kslabs = K / BK / p.splits;
+  const int kbeg = split * kslabs * BK;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,8 +144,8 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
   const int ln = lane & 31, hf = lane >> 5;
   const int wn = wave % OWN, wm = wave / OWN;
 
-  constexpr int WCH = OBN * 8 / ONT;  // 16-byte chunks per thread per slab
-  constexpr int XCH = BM * 8 / ONT;
+  constexpr int WCH = OBN * CH / ONT;  // 16-byte chunks per thread per slab
+  constexpr int XCH = BM * CH / ONT;
   u32x4 rw[WCH], rx[XCH];
   u32x2 rw8[FP8 ? WCH : 1];
   float rs[FP8 ? WCH : 1];
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
       const int c = tid + i * ONT;
-      const int row = c >> 3, ch = c & 7;
+      const int row = c / CH, ch = c % CH;
       const int n = min(n0 + row, N - 1);
       if constexpr (FP8) {
         rw8[i] = ld_global_8(p.w8 + (size_t)n * K + k0 + ch * 8);
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int c = tid + i * ONT;
-      const int row = c >> 3, ch = c & 7;
+      const int row = c / CH, ch = c % CH;
       const int m = min(m0 + row, M - 1);
       rx[i] = ld_global_16(p.x + (size_t)m * K + k0 + ch * 8);
     }
@@ -175,30 +180,30 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
       const int c = tid + i * ONT;
-      const int row = c >> 3, ch = c & 7;
+      const int row = c / CH, ch = c % CH;
       if constexpr (FP8) rw[i] = dequant8(rw8[i], rs[i]);
-      *reinterpret_cast<u32x4*>(sW + row * OBK + ((ch ^ rswz(row)) * 8)) = rw[i];
+      *reinterpret_cast<u32x4*>(sW + row * BK + ((ch ^ swz(row)) * 8)) = rw[i];
     }
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int c = tid + i * ONT;
-      const int row = c >> 3, ch = c & 7;
-      *reinterpret_cast<u32x4*>(sX + row * OBK + ((ch ^ rswz(row)) * 8)) = rx[i];
+      const int row = c / CH, ch = c % CH;
+      *reinterpret_cast<u32x4*>(sX + row * BK + ((ch ^ swz(row)) * 8)) = rx[i];
     }
     __syncthreads();
-    if (ks + 1 < kslabs) load(kbeg + (ks + 1) * OBK);
+    if (ks + 1 < kslabs) load(kbeg + (ks + 1) * BK);
 #pragma unroll
-    for (int kk = 0; kk < OBK / 16; ++kk) {
+    for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 a[OTN], bb[OTM];
 #pragma unroll
       for (int i = 0; i < OTN; ++i) {
         const int row = wn * (OTN * 32) + i * 32 + ln;
-        a[i] = *reinterpret_cast<const bf16x8*>(sW + row * OBK + (((kk * 2 + hf) ^ rswz(row)) * 8));
+        a[i] = *reinterpret_cast<const bf16x8*>(sW + row * BK + (((kk * 2 + hf) ^ swz(row)) * 8));
       }
 #pragma unroll
       for (int jm = 0; jm < OTM; ++jm) {
         const int row = wm * (OTM * 32) + jm * 32 + ln;
-        bb[jm] = *reinterpret_cast<const bf16x8*>(sX + row * OBK + (((kk * 2 + hf) ^ rswz(row)) * 8));
+        bb[jm] = *reinterpret_cast<const bf16x8*>(sX + row * BK + (((kk * 2 + hf) ^ swz(row)) * 8));
       }
 #pragma unroll
       for (int i = 0; i < OTN; ++i)
@@ -447,159 +452,6 @@ __global__ __launch_bounds__(256) void oproj_reduce_kernel(OprojParams p) {
   }
 }
 
-// ------------------------------------------------------------- skinny M --
-// M <= 64 with the FP8 weight (decode): the weight stream is the HBM traffic
-// and x is small, so x is shared through LDS and the weight goes straight to
-// registers.  A workgroup of 4 waves owns SF = 224 output features and a K
-// slice of KC <= 1024: it copies x[0..63][slice] into LDS once (16-byte
-// chunks, chunk index XOR (row & 15), so the 16 rows read by one MFMA operand
-// fall in distinct banks), then wave w takes features SF/2 * (w & 1) +
-// [0, 112) and half (w >> 1) of the slice.  Per step of 64 k a wave computes
-// Y[n][m] for its 112 features (7 blocks of 16) and all 64 rows with
-// v_mfma_f32_16x16x32_bf16: A = weight rows straight from global memory
-// (lane: feature 16j + l%16, 16 e4m3 values at k 16(l/16).. that make two
-// MFMA k-slices of 8, dequantized in registers), B = x rows from LDS (lane:
-// row 16mb + l%16, the same k-values); loads run SKD steps ahead, all
-// unconditional so that the compiler waits for the oldest step only.  The
-// two K halves are added in LDS; with more than one workgroup along K the
-// sums go to the float32 partials and the reduction kernel.  (With the bf16
-// weight the tiled kernel, at several workgroups per compute unit, streams
-// the weight faster than this one-workgroup-per-unit layout.)
-constexpr int SF = 224;        // output features per workgroup
-constexpr int SNB = 7;         // 16-feature blocks per wave
-constexpr int SKC_MAX = 1024;  // k per workgroup (x slice: 64 x 1024 bf16 = 128 KiB of LDS)
-constexpr int SKD = 4;         // steps of weight loads in flight per wave
-constexpr int SKSTEP = 64;     // k per step
-
-__global__ __launch_bounds__(256) void oproj_skinny_fp8_kernel(OprojParams p) {
-  __shared__ __attribute__((aligned(16))) u32x4 xs[64 * SKC_MAX / 8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = lane >> 4, i = lane & 15;
-  const int M = p.M, N = p.N, K = p.K;
-  const int KC = K / gridDim.y;   // k per workgroup: a multiple of 512, at most SKC_MAX
-  const int cpr = KC / 8;         // 16-byte chunks per x row in LDS
-  const int kb = blockIdx.y * KC;
-  const int fh = wave & 1, kh = wave >> 1;
-  const int n0 = blockIdx.x * SF + fh * (SF / 2);
-  const int kw = kb + kh * (KC / 2);     // this wave's first k
-  const int nsteps = KC / 2 / SKSTEP;    // a multiple of SKD (KC is a multiple of 512)
-  const int KB = (K + 127) / 128;
-
-  int nrow[SNB];
-#pragma unroll
-  for (int j = 0; j < SNB; ++j) nrow[j] = min(n0 + j * 16 + i, N - 1);
-
-  struct Frag {
-    u32x4 a[SNB];
-    float sc[SNB];
-  };
-  auto load = [&](Frag& f, int st) {
-    const int k = kw + st * SKSTEP;
-#pragma unroll
-    for (int j = 0; j < SNB; ++j) {
-      f.a[j] = ld_global_16(p.w8 + (size_t)nrow[j] * K + k + q * 16);
-      f.sc[j] = p.w_scale[(nrow[j] >> 7) * KB + (k >> 7)];
-    }
-  };
-
-  Frag fr[SKD];
-#pragma unroll
-  for (int d = 0; d < SKD; ++d) load(fr[d], d);
-
-  // ---- x slice into LDS (rows >= M repeat row M-1; their outputs are not stored)
-  for (int c0 = 0; c0 < 64 * cpr; c0 += 256 * 8) {
-    u32x4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = c0 + u * 256 + tid;
-      const int m = c / cpr, ch = c - m * cpr;
-      v[u] = ld_global_16(p.x + (size_t)min(m, M - 1) * K + kb + ch * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = c0 + u * 256 + tid;
-      const int m = c / cpr, ch = c - m * cpr;
-      xs[m * cpr + (ch ^ (m & 15))] = v[u];
-    }
-  }
-  __syncthreads();
-
-  f32x4 acc[SNB][4] = {};  // [feature block][row block]
-  auto step = [&](const Frag& f, int st) {
-    const int c0 = (kw - kb + st * SKSTEP) / 8;  // first x chunk (8 k) of the step
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int ch = c0 + 2 * q + sub;
-      bf16x8 b[4];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) b[mb] = as_bf16x8(xs[(mb * 16 + i) * cpr + (ch ^ i)]);
-#pragma unroll
-      for (int j = 0; j < SNB; ++j) {
-        const bf16x8 a = as_bf16x8(dequant8(u32x2{f.a[j][2 * sub], f.a[j][2 * sub + 1]}, f.sc[j]));
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[j][mb] = mfma16x16x32(a, b[mb], acc[j][mb]);
-      }
-    }
-  };
-  for (int st0 = 0; st0 + SKD < nsteps; st0 += SKD) {
-#pragma unroll
-    for (int d = 0; d < SKD; ++d) {
-      step(fr[d], st0 + d);
-      load(fr[d], st0 + SKD + d);
-    }
-  }
-#pragma unroll
-  for (int d = 0; d < SKD; ++d) step(fr[d], nsteps - SKD + d);
-
-  // ---- the two K halves added in LDS (the x slice is no longer read)
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(xs) + fh * (SNB * 16 * 64);  // [acc register][lane]
-  if (kh == 1) {
-#pragma unroll
-    for (int j = 0; j < SNB; ++j)
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[((j * 4 + mb) * 4 + r) * 64 + lane] = acc[j][mb][r];
-  }
-  __syncthreads();
-  if (kh == 1) return;
-#pragma unroll
-  for (int j = 0; j < SNB; ++j)
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[j][mb][r] += red[((j * 4 + mb) * 4 + r) * 64 + lane];
-
-  // ---- lane holds y[m][n .. n+3], m = 16mb + l%16, n = n0 + 16j + 4q
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int m = mb * 16 + i;
-    if (m >= M) continue;
-#pragma unroll
-    for (int j = 0; j < SNB; ++j) {
-      const int n = n0 + j * 16 + q * 4;
-      const f32x4 v = acc[j][mb];
-      if (gridDim.y > 1) {
-        float* dst = p.part + ((size_t)blockIdx.y * M + m) * N + n;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < N) dst[r] = v[r];
-      } else if (p.out_f32) {
-        float* dst = static_cast<float*>(p.y) + (size_t)m * N + n;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < N) dst[r] = v[r];
-      } else {
-        __bf16* dst = static_cast<__bf16*>(p.y) + (size_t)m * N + n;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < N) dst[r] = f32_to_bf16(v[r]);
-      }
-    }
-  }
-}
-
 }  // namespace
 
 // The wide kernel needs enough 256 x 256 tiles to fill the chip, and 32-bit
@@ -609,35 +461,21 @@ static bool oproj_use_wide(int M, int K, int N) {
   return wide_tiles >= 256 && (long long)K * 2 * WBM < 0x7fffffffLL;
 }
 
-// Skinny FP8 kernel (M <= 64): the number of workgroups along K.  Each takes
-// a slice of K that is a multiple of 512 and at most 1024 (its x slice fits
-// in LDS); more slices while the grid is under one workgroup per compute
-// unit.  0: the shape does not fit (the tiled kernel takes it).
-static int oproj_skinny_splits(int M, int K, int N) {
-  if (M > 64 || K % 512 != 0) return 0;
-  const long groups = (N + SF - 1) / SF;
-  int s = 0;
-  for (int c = 1; c <= K / 512; ++c)
-    if (K % (512 * c) == 0 && K / c <= SKC_MAX) {
-      s = c;
-      break;
-    }
-  if (s == 0) return 0;
-  while (groups * s < 256 && K % (512 * 2 * s) == 0) s *= 2;
-  return s;
-}
+// k per LDS slab of the small-tile kernel: 128 for the FP8 weight at M <= 64
+// (16 KiB of weight per slab, as for the bf16 weight at 64; 29 us against 33
+// us at M = 64, K = 8192, N = 7168), 64 otherwise (at M = 16384 the deeper
+// slab measured 2.49 ms against 2.35).
+static int oproj_slab_k(int M, bool fp8) { return fp8 && M <= 64 ? 2 * OBK : OBK; }
 
 int oproj_choose_splits(int M, int K, int N, bool fp8) {
-  const int sk = fp8 ? oproj_skinny_splits(M, K, N) : 0;
-  if (sk > 0) return sk;
   if (!fp8 && oproj_use_wide(M, K, N)) return 1;
   const long tiles = (long)((M + OBM - 1) / OBM) * ((N + OBN - 1) / OBN);
-  const int slabs = K / OBK;
+  const int slabs = K / oproj_slab_k(M, fp8);
   if (tiles >= 256 || slabs <= 1) return 1;
   // Spread the weight stream over the chip: aim for >= 256 workgroups (at
   // M = 64, N = 7168, K = 8192: 8 splits, 448 workgroups, 33 us against
   // 48 us for 16 splits, whose float32 partials cost more than they spread),
-  // keep >= 4 slabs (256 k) per split, and split K into equal whole slabs.
+  // keep >= 4 slabs per split, and split K into equal whole slabs.
   int best = 1;
   for (int s = 2; s <= slabs / 4; ++s) {
     if (slabs % s) continue;
@@ -659,27 +497,22 @@ hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
     hipLaunchKernelGGL(oproj_wide_kernel, dim3((unsigned)wide_tiles), dim3(WNT), 0, stream, p);
     return hipGetLastError();
   }
-  const int sk = p.w8 ? oproj_skinny_splits(p.M, p.K, p.N) : 0;
-  if (sk > 0) {
-    const long groups = (p.N + SF - 1) / SF;
-    if (groups > 0x7fffffffL || p.splits != sk) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(oproj_skinny_fp8_kernel, dim3((unsigned)groups, (unsigned)sk), dim3(256), 0, stream, p);
-  } else {
   const long tiles = (long)((p.M + OBM - 1) / OBM) * ((p.N + OBN - 1) / OBN);
-  if (tiles <= 0 || tiles > 0x7fffffffL || p.splits < 1 || p.splits > 65535)
+  const int bk = oproj_slab_k(p.M, p.w8 != nullptr);
+  if (tiles <= 0 || tiles > 0x7fffffffL || p.splits < 1 || p.splits > 65535 || p.K % (bk * p.splits) != 0)
     return hipErrorInvalidConfiguration;
   // M <= 64 is one m-tile at either height; the 64-row tile loads and
   // multiplies no rows past M.
+  const dim3 grid((unsigned)tiles, (unsigned)p.splits);
   const bool m64 = p.M <= 64;
   if (p.w8 && m64)
-    hipLaunchKernelGGL((oproj_kernel<true, 64>), dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
+    hipLaunchKernelGGL((oproj_kernel<true, 64, 2 * OBK>), grid, dim3(ONT), 0, stream, p);
   else if (p.w8)
-    hipLaunchKernelGGL((oproj_kernel<true, OBM>), dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
+    hipLaunchKernelGGL((oproj_kernel<true, OBM, OBK>), grid, dim3(ONT), 0, stream, p);
   else if (m64)
-    hipLaunchKernelGGL((oproj_kernel<false, 64>), dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
+    hipLaunchKernelGGL((oproj_kernel<false, 64, OBK>), grid, dim3(ONT), 0, stream, p);
   else
-    hipLaunchKernelGGL((oproj_kernel<false, OBM>), dim3((unsigned)tiles, (unsigned)p.splits), dim3(ONT), 0, stream, p);
-  }
+    hipLaunchKernelGGL((oproj_kernel<false, OBM, OBK>), grid, dim3(ONT), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const size_t total = (size_t)p.M * p.N;
