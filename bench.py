@@ -340,8 +340,9 @@ def main():
                          "write 1 GiB) three times, to scale hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
-              "multi-GPU path to measure.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "multi-GPU path to measure (heads and sequences would shard with one exchange after "
+              "o_proj).", file=sys.stderr)
         sys.exit(2)
 
     import torch
