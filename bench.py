@@ -56,6 +56,24 @@ def measured_traffic(kernel):
     return nbytes if h.hexdigest()[:16] == digest else None
 
 
+def measured_copy_gbps(torch, dev, reps=5):
+    """Device copy rate on this GPU: 1 GiB read and 1 GiB written by an
+    elementwise kernel, best of a few runs (bytes read + written per second)."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.neg(src, out=dst)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return 2.0 * (1 << 30) / (best * 1e-3) / 1e9
+
+
 def prefill_flops(B, H, T):
     return 2.0 * (128 + 64 + 128) * T * (T + 1) / 2 * B * H
 
@@ -464,12 +482,15 @@ def main():
             "hbm_gbps": bd / td / 1e9, "frac_hbm": bd / td / 1e9 / PEAK_HBM_GBPS,
             "splits": mla.mla_decode_splits(Bd, Hd, L, args.decode_splits),
             "oproj_ms": avg["decode_oproj"], "oproj_gbps": bo / tod / 1e9}
+        copy_gbps = measured_copy_gbps(torch, dev)
         res["roofline_decode"] = {"bound": "hbm", "achieved": bd / td / 1e9, "peak": PEAK_HBM_GBPS,
                                   "unit": "GB/s", "frac": bd / td / 1e9 / PEAK_HBM_GBPS,
                                   "traffic": (measured_traffic("decode_split_kernel")
                                               if args.decode_splits == 0 else None),
                                   "kernel": "decode_split_kernel",
-                                  "per_launch": f"{bd} bytes"}
+                                  "per_launch": f"{bd} bytes",
+                                  "measured_copy_gbps": copy_gbps,
+                                  "frac_of_measured_copy": bd / td / 1e9 / copy_gbps}
         parts.append(f"decode B={Bd} L={L} H={Hd} q_pos={q_pos} + o_proj [{Bd}x{K_O}]x[{K_O}x{N_O}]")
         cfg.update({"decode_batch": Bd, "decode_kv_len": L})
         if not do_p:
