@@ -74,6 +74,53 @@ def measured_copy_gbps(torch, dev, reps=5):
     return 2.0 * (1 << 30) / (best * 1e-3) / 1e9
 
 
+class Timer:
+    """Median call time with HIP events on the current stream, warm and cold.
+
+    warm: back-to-back calls (inputs and weights may sit in the 256 MB MALL and
+    the L2s).  cold: before each timed call, outside the event pair, a 512 MB
+    scratch buffer is written, which evicts the MALL and the L2s, so the call
+    reads its inputs and weights from HBM."""
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush(self):
+        self.scratch.fill_(1)
+
+    def median(self, fn, calls, cold=False, untimed=3):
+        torch = self.torch
+        for _ in range(untimed):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(calls)]
+        for a, b in ev:
+            if cold:
+                self.flush()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        return t[len(t) // 2]
+
+    def both(self, fn, calls):
+        return {"cold": self.median(fn, calls, cold=True), "warm": self.median(fn, calls)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def prefill_flops(B, H, T):
     return 2.0 * (128 + 64 + 128) * T * (T + 1) / 2 * B * H
 
@@ -124,17 +171,52 @@ def cpu_baseline(d, B, H, T, R, scale, budget_s):
     flops = prefill_flops(1, n, T)
     last_b, last_h = (n - 1) // H, (n - 1) % H
     return {"value": flops / tn / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"every row of the first {n} (sequence, head) units (through sequence {last_b}, "
-                      f"head {last_h}) of the B={B} T={T} H={H} workload; {flops / 1e9:.1f} GFLOP in "
-                      f"{tn:.2f} s, fp64",
+            "cpu_model": cpu_model(),
+            "sample": f"every row of the first {n} (sequence, head) units in sequence-major order "
+                      f"(through sequence {last_b}, head {last_h}) of the B={B} T={T} H={H} "
+                      f"workload; {flops / 1e9:.1f} GFLOP in {tn:.2f} s, fp64",
             "seconds": round(tn, 3)}
 
 
-def other_configs(mla, inputs, w_o, scale, dev, calls=10):
+def cpu_baseline_decode(dd, Bd, Hd, L, q_pos, R, scale, budget_s):
+    """Time the oracle's decode on a bounded sample of the decode workload:
+    every head of the first nb sequences, nb chosen from a one-sequence
+    calibration for about budget_s seconds; GB/s on the same algorithmic bytes
+    as the GPU figure (every cached key and value byte of those (sequence,
+    head) units once, plus q and the output)."""
+    import numpy as np
+    import oracle
+    from transformer_attention_mla_amd import inputs
+
+    threads = oracle.default_threads()
+
+    def run(nb):
+        sl = lambda t: inputs.bits(t[0:nb])
+        qn, qp, kc, vc = sl(dd["q_nope"]), sl(dd["q_pe"]), sl(dd["k_cache"]), sl(dd["v_cache"])
+        sel = np.stack([np.repeat(np.arange(nb, dtype=np.int32), Hd),
+                        np.tile(np.arange(Hd, dtype=np.int32), nb)], 1).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.decode_rows(qn, qp, kc, vc, R, q_pos, scale, sel, nthreads=threads)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    nb = max(1, min(Bd, 24, int(budget_s / max(t1, 1e-3))))
+    tn = t1 if nb == 1 else run(nb)
+    nbytes = decode_bytes(nb, Hd, L)
+    return {"value": nbytes / tn / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"all {Hd} heads of the first {nb} sequences of the B={Bd} L={L} decode "
+                      f"workload; {nbytes / 1e9:.2f} GB of cached keys and values in {tn:.2f} s, "
+                      f"fp64", "seconds": round(tn, 3)}
+
+
+def other_configs(mla, inputs, w_o, scale, dev, timer):
     """Prefill attention and o_proj at the other prefill workloads (T = 64,
     1024 with plain rotary angles; T = 16384 with the YaRN table), each call
-    timed with HIP events after 3 untimed ones; median per call.  Reported
-    beside the main line, not part of it."""
+    timed with HIP events after 3 untimed ones; median per call, cold (MALL
+    and L2 flushed before each call) and warm (back to back); 200 calls at
+    T <= 1024, 10 at T = 16384.  Reported beside the main line, not part of
+    it."""
     import torch
 
     out = {}
@@ -153,27 +235,19 @@ def other_configs(mla, inputs, w_o, scale, dev, calls=10):
                                             d["R"], scale, out=o, workspace=ws)
         fo = lambda: mla.mla_out_proj(o.view(M, K_O), w_o, y=y, workspace=ws_o)
 
-        def med(fn):
-            for _ in range(3):
-                fn()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(calls)]
-            for a, b in ev:
-                a.record()
-                fn()
-                b.record()
-            torch.cuda.synchronize()
-            t = sorted(a.elapsed_time(b) for a, b in ev)
-            return t[len(t) // 2]
-
-        ta, to = med(fa), med(fo)
+        calls = 200 if T <= 1024 else 10
+        ta, to = timer.both(fa, calls), timer.both(fo, calls)
         fl_a, fl_o = prefill_flops(B, H, T), oproj_flops(M, K_O, N_O)
+        ob = oproj_bytes(M, K_O, N_O)
         out[f"prefill_B{B}_T{T}_H{H}"] = {
-            "attention_ms": ta, "attention_tflops": fl_a / ta / 1e9,
-            "attention_frac_peak": fl_a / ta / 1e9 / PEAK_BF16_TFLOPS,
-            "oproj_ms": to, "oproj_tflops": fl_o / to / 1e9,
-            "oproj_gbps": oproj_bytes(M, K_O, N_O) / to / 1e6,
-            "rope": wl["rope"]}
+            "attention_ms": ta["cold"], "attention_ms_warm": ta["warm"],
+            "attention_tflops": fl_a / ta["cold"] / 1e9,
+            "attention_tflops_warm": fl_a / ta["warm"] / 1e9,
+            "attention_frac_peak": fl_a / ta["cold"] / 1e9 / PEAK_BF16_TFLOPS,
+            "oproj_ms_cold": to["cold"], "oproj_ms_warm": to["warm"],
+            "oproj_tflops_cold": fl_o / to["cold"] / 1e9, "oproj_tflops_warm": fl_o / to["warm"] / 1e9,
+            "oproj_gbps_cold": ob / to["cold"] / 1e6, "oproj_gbps_warm": ob / to["warm"] / 1e6,
+            "calls": calls, "rope": wl["rope"]}
         del d, o, ws, y, ws_o
         torch.cuda.empty_cache()
     # A chunk of 4096 positions after 12288 cached ones (64 heads): append the
@@ -181,22 +255,20 @@ def other_configs(mla, inputs, w_o, scale, dev, calls=10):
     B, H, T, past = 1, 64, 4096, 12288
     L = past + T
     print(f"other config: chunked prefill (T={T} after {past})", file=sys.stderr, flush=True)
-    g = lambda shape, k: inputs.normal_bf16(shape, 7000 + k, device=dev)
-    q_nope, q_pe = g((B, H, T, 128), 0), g((B, H, T, 64), 1)
-    k_nope, k_pe, v = g((B, H, T, 128), 2), g((B, 1, T, 64), 3), g((B, H, T, 128), 4)
-    kc, pc, vc = g((B, H, L, 128), 5), g((B, L, 64), 6), g((B, H, L, 128), 7)
-    R = torch.from_numpy(inputs.rope_angles(L)).to(dev)
+    c = inputs.chunk_inputs(B, H, T, past, seed=7000, device=dev)
+    q_nope, q_pe, k_nope, k_pe, v = (c[k] for k in ("q_nope", "q_pe", "k_nope", "k_pe", "v"))
+    kc, pc, vc, R = c["k_nope_cache"], c["kpe_cache"], c["v_cache"], c["R"]
     o = torch.empty((B, T, H * 128), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(mla.mla_prefill_chunk_workspace_bytes(T), dtype=torch.uint8, device=dev)
     fapp = lambda: mla.mla_append_kv(k_nope, k_pe, v, R, past, kc, pc, vc)
     fatt = lambda: mla.mla_attend_prefill_chunk(q_nope, q_pe, kc, pc, vc, R, past, scale, out=o,
                                                 workspace=ws)
-    tapp, tatt = med(fapp), med(fatt)
+    tapp, tatt = timer.median(fapp, 10), timer.median(fatt, 10)
     fl = 2.0 * (128 + 64 + 128) * B * H * (T * past + T * (T + 1) / 2)
     out[f"prefill_chunk_B{B}_T{T}_past{past}_H{H}"] = {
         "append_ms": tapp, "attention_ms": tatt, "attention_tflops": fl / tatt / 1e9,
         "attention_frac_peak": fl / tatt / 1e9 / PEAK_BF16_TFLOPS}
-    del q_nope, q_pe, k_nope, k_pe, v, kc, pc, vc, o, ws
+    del c, q_nope, q_pe, k_nope, k_pe, v, kc, pc, vc, o, ws
     torch.cuda.empty_cache()
     # The up-projection in front of the prefill at B=4, T=4096, 64 heads: q
     # from the rank-1536 latent, nope key and value from the rank-512 latent.
@@ -205,12 +277,13 @@ def other_configs(mla, inputs, w_o, scale, dev, calls=10):
     d = inputs.up_project_inputs(B, T, H, workload=3, device=dev)
     outs = [torch.empty((B, H, T, w), dtype=torch.bfloat16, device=dev) for w in (128, 64, 128, 128)]
     fup = lambda: mla.mla_up_project(d["q_lat"], d["ckv"], d["w_q_b"], d["w_kv_b"], outs=outs)
-    tup = med(fup)
+    tup = timer.both(fup, 10)
     fl = 2.0 * B * T * (1536 * H * 192 + 512 * H * 256)
     nbytes = 2 * (B * T * (1536 + 512) + H * 192 * 1536 + H * 256 * 512 + B * H * T * (128 + 64 + 128 + 128))
     out[f"up_project_B{B}_T{T}_H{H}"] = {
-        "ms": tup, "tflops": fl / tup / 1e9, "frac_peak": fl / tup / 1e9 / PEAK_BF16_TFLOPS,
-        "hbm_gbps": nbytes / tup / 1e6, "per_call": f"{fl:.4e} flops, {nbytes} bytes"}
+        "ms_cold": tup["cold"], "ms_warm": tup["warm"], "tflops_cold": fl / tup["cold"] / 1e9,
+        "tflops_warm": fl / tup["warm"] / 1e9, "frac_peak_cold": fl / tup["cold"] / 1e9 / PEAK_BF16_TFLOPS,
+        "hbm_gbps_cold": nbytes / tup["cold"] / 1e6, "per_call": f"{fl:.4e} flops, {nbytes} bytes"}
     del d, outs
     torch.cuda.empty_cache()
     return out
@@ -306,10 +379,36 @@ def decode_latent_figures(mla, inputs, scale, dev, calls=20):
             "traffic": measured_traffic("latent_decode_kernel")}
 
 
-def oproj_fp8_figures(mla, inputs, dev, calls=20):
+def oproj_figures(mla, inputs, w_o, dev, timer, calls=20):
+    """o_proj with the bf16 weight at M = 64 (decode) and M = 16384 (prefill),
+    timed alone: median time cold (MALL and L2 flushed before each call) and
+    warm (back to back), GB/s on x + w + y, TFLOP/s."""
+    import torch
+
+    N, K = w_o.shape
+    res = {}
+    for M in (64, 16384):
+        print(f"o_proj bf16 M={M}", file=sys.stderr, flush=True)
+        x = inputs.normal_bf16((M, K), 90 + M, device=dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(16, mla.mla_out_proj_workspace_bytes(M, K, N)), dtype=torch.uint8,
+                         device=dev)
+        t = timer.both(lambda: mla.mla_out_proj(x, w_o, y=y, workspace=ws), calls)
+        nb = oproj_bytes(M, K, N)
+        res[f"M{M}"] = {"ms_cold": t["cold"], "ms_warm": t["warm"],
+                        "gbps_cold": nb / t["cold"] / 1e6, "gbps_warm": nb / t["warm"] / 1e6,
+                        "tflops_cold": oproj_flops(M, K, N) / t["cold"] / 1e9,
+                        "tflops_warm": oproj_flops(M, K, N) / t["warm"] / 1e9, "bytes": nb}
+        del x, y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def oproj_fp8_figures(mla, inputs, dev, timer, calls=20):
     """o_proj with the FP8 checkpoint weight ([7168, 8192] e4m3 + float32 block
     scales, dequantized to bf16 as it is loaded), at M = 64 (decode) and M =
-    16384 (prefill): median time, GB/s on x + w8 + scales + y, TFLOP/s."""
+    16384 (prefill): median time cold and warm, GB/s on x + w8 + scales + y,
+    TFLOP/s."""
     import torch
 
     K, N = 64 * 128, inputs.D_MODEL
@@ -322,19 +421,12 @@ def oproj_fp8_figures(mla, inputs, dev, calls=20):
         ws = torch.empty(max(16, mla.mla_out_proj_fp8_workspace_bytes(M, K, N)), dtype=torch.uint8,
                          device=dev)
         f = lambda: mla.mla_out_proj_fp8(x, w8, sc, y=y, workspace=ws)
-        for _ in range(3):
-            f()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(calls)]
-        for a, b in ev:
-            a.record()
-            f()
-            b.record()
-        torch.cuda.synchronize()
-        t = sorted(a.elapsed_time(b) for a, b in ev)[calls // 2]
+        t = timer.both(f, calls)
         nb = M * K * 2 + N * K + sc.numel() * 4 + M * N * 2
-        res[f"M{M}"] = {"ms": t, "gbps": nb / t / 1e6, "tflops": oproj_flops(M, K, N) / t / 1e9,
-                        "bytes": nb}
+        res[f"M{M}"] = {"ms_cold": t["cold"], "ms_warm": t["warm"],
+                        "gbps_cold": nb / t["cold"] / 1e6, "gbps_warm": nb / t["warm"] / 1e6,
+                        "tflops_cold": oproj_flops(M, K, N) / t["cold"] / 1e9,
+                        "tflops_warm": oproj_flops(M, K, N) / t["warm"] / 1e9, "bytes": nb}
         del x, y, ws
     del w8, sc
     torch.cuda.empty_cache()
@@ -500,16 +592,25 @@ def main():
     cfg["workload"] = "; ".join(parts)
     res["config"] = cfg
 
-    if do_p and not args.no_other_configs:
-        res["other_configs"] = other_configs(mla, inputs, w_o, scale, dev)
-    if do_d and not args.no_other_configs:
-        res["decode_shared_kpe"] = decode_shared_kpe_figures(mla, inputs, scale, dev)
-        res["decode_latent"] = decode_latent_figures(mla, inputs, scale, dev)
-        res["oproj_fp8"] = oproj_fp8_figures(mla, inputs, dev)
+    if not args.no_other_configs:
+        timer = Timer(torch, dev)
+        if do_p:
+            res["other_configs"] = other_configs(mla, inputs, w_o, scale, dev, timer)
+        if do_d:
+            res["decode_shared_kpe"] = decode_shared_kpe_figures(mla, inputs, scale, dev)
+            res["decode_latent"] = decode_latent_figures(mla, inputs, scale, dev)
+        res["oproj"] = oproj_figures(mla, inputs, w_o, dev, timer)
+        res["oproj_fp8"] = oproj_fp8_figures(mla, inputs, dev, timer)
+        del timer
+        torch.cuda.empty_cache()
 
     if do_p and not args.no_cpu_baseline:
         print("cpu baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(d, B, H, T, d["R"].cpu().numpy(), scale, args.cpu_budget)
+        if do_d:
+            print("cpu baseline, decode", file=sys.stderr, flush=True)
+            res["cpu_baseline"]["decode"] = cpu_baseline_decode(
+                dd, Bd, Hd, L, q_pos, dd["R"].cpu().numpy(), scale, args.cpu_budget / 3)
     print(json.dumps(res), flush=True)
 
 

@@ -11,10 +11,11 @@
  *   keys, and mix the 128-wide values.  Excerpt "mla-output": head outputs are
  *   transposed to [B, T, 64·128] (head-major) and go through o_proj, an
  *   8,192 → 7,168 linear map without bias (the parameter table of that page;
- *   the page's explanation: the only step that mixes heads).
+ *   per the page's explanation, no earlier step combines different heads).
  *   page "Kimi K2 · Transformer blocks", I/O header: R [T positions, 32 pairs]
- *   and the causal mask M [T queries, T keys]; the model-body excerpt numbers
- *   positions from the cached length (0 for a prefill without cache).
+ *   and the causal mask M [T queries, T keys]; in the model-body excerpt the
+ *   position ids start right after the tokens already cached (at 0 for a
+ *   prefill without cache).
  *   page "Block input", config.json: 64 heads, qk_nope_head_dim 128,
  *   qk_rope_head_dim 64, v_head_dim 128, attention_bias false, bfloat16.
  *
@@ -112,7 +113,7 @@ int mla_attend_prefill(const mla_bf16 *q_nope, const mla_bf16 *q_pe, const mla_b
 
 /* KV-cache append (page "Kimi K2 · Mix and project", excerpt "mla-prefill": the
  * cache is updated with the keys after the rotary step; page "Kimi K2 ·
- * Transformer blocks": new positions continue from the cached length): a chunk
+ * Transformer blocks": position ids start after the cached tokens): a chunk
  * of T positions goes to rows past .. past+T-1 of a cache in the shared-rotary
  * layout, the rope key rotated at its position (R row past + t) and rounded to
  * bf16 with the same arithmetic as the prefill's own rotation.

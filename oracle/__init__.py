@@ -76,6 +76,8 @@ def _load():
     lib.oracle_append_kv.restype = I
     lib.oracle_prefill_chunk.argtypes = [P, P, P, P, P, P, I, I, D, I, I, I, I, P, P, I]
     lib.oracle_prefill_chunk.restype = I
+    lib.oracle_prefill_chunk_rows.argtypes = [P, P, P, P, P, P, I, I, D, I, I, I, I, I, P, P, P, I]
+    lib.oracle_prefill_chunk_rows.restype = I
     lib.oracle_up_project.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P, P, I]
     lib.oracle_up_project.restype = I
     lib.oracle_out_proj.argtypes = [P, P, I, I, I, P, I]
@@ -422,6 +424,33 @@ def prefill_chunk(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, past, scale
                                   Lc, _p(out), _p(lse), nthreads or default_threads())
     if rc:
         raise ValueError(f"oracle_prefill_chunk failed ({rc})")
+    return out, lse
+
+
+def prefill_chunk_rows(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, past, scale, sel,
+                       nthreads=None):
+    """Selected rows of the chunked prefill: ``sel`` is an int array [n,3] of
+    (b, h, t); query t sits at position past + t and sees cache rows
+    0 .. past + t.  Returns out [n,128] and lse [n]."""
+    lib = _load()
+    q_nope, q_pe, k_nope_cache, kpe_cache, v_cache = map(
+        _u16, (q_nope, q_pe, k_nope_cache, kpe_cache, v_cache))
+    R = _f32(R)
+    B, H, T, _ = q_nope.shape
+    Lc = k_nope_cache.shape[2]
+    if q_pe.shape != (B, H, T, 64) or k_nope_cache.shape != (B, H, Lc, 128) or \
+            kpe_cache.shape != (B, Lc, 64) or v_cache.shape != (B, H, Lc, 128):
+        raise ValueError("prefill_chunk_rows shapes")
+    sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 3)
+    n = sel.shape[0]
+    out = np.empty((n, 128), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = lib.oracle_prefill_chunk_rows(_p(q_nope), _p(q_pe), _p(k_nope_cache), _p(kpe_cache),
+                                       _p(v_cache), _p(R), R.shape[0], int(past), float(scale), B,
+                                       H, T, Lc, n, _p(sel), _p(out), _p(lse),
+                                       nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_prefill_chunk_rows failed ({rc})")
     return out, lse
 
 

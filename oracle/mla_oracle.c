@@ -8,14 +8,14 @@
  * precision on bf16 inputs that are widened exactly.  Sources (the pages):
  *   [MIX]    page "Kimi K2 · Mix and project": the I/O header (A, V -> delta_attn),
  *            the output-projection parameter table (8,192 x 7,168), the remark
- *            that the projection is the only step mixing heads, and the code
+ *            that no step before the projection combines heads, and the code
  *            excerpts "mla-prefill" (rotary, query/key join with the shared
  *            rotary key, scaled scores, additive mask, fp32 softmax, value mix)
  *            and "mla-output" (head transpose, flatten to 64*128, o_proj).
  *   [BLOCKS] page "Kimi K2 · Transformer blocks": block-stack I/O header
  *            (R [T positions, 32 pairs], M [T queries, T keys]) and the model-body
- *            excerpt that numbers positions from the cached length and builds
- *            the causal mask.
+ *            excerpt, whose position ids start after the already cached
+ *            tokens and which builds the causal mask.
  *   [CONFIG] page "Block input", config.json excerpt: 64 heads, nope 128,
  *            rope 64, value 128, hidden 7168, attention_bias false, bfloat16.
  *
@@ -251,7 +251,7 @@ static void prefill_unit(void *vctx, long unit, double *scratch) {
   const uint16_t *qp_src = c->q_pe + (bh * c->T + t) * OR_ROPE;
   for (int d = 0; d < OR_NOPE; d++) qn[d] = widen(qn_src[d]);
   for (int d = 0; d < OR_ROPE; d++) qpe[d] = widen(qp_src[d]);
-  /* The query sits at position t (positions start at the cached length, here
+  /* The query sits at position t (position ids start after the cached tokens, here
    * 0, [BLOCKS] model body); rotate, then round (R1). */
   oracle_rotate_row(qpe, c->R + (size_t)t * OR_PAIRS, qr);
   for (int d = 0; d < OR_ROPE; d++) qr[d] = oracle_bf16_round(qr[d]);
@@ -713,7 +713,7 @@ int oracle_dequant_fp8(const uint8_t *w8, const float *scale, int N, int K, uint
 /* ------------------------------------------------ chunked prefill, append ---- */
 
 /* Page "Kimi K2 · Transformer blocks", model-body excerpt: positions of a new
- * chunk continue from the cached length (position_ids = past .. past+T-1) and
+ * chunk start after the cached tokens (position_ids = past .. past+T-1) and
  * the causal mask is built with that past length; page "Kimi K2 · Mix and
  * project", excerpt "mla-prefill": the cache is updated with the new keys after
  * the rotary step, and the scores run over every cached and new key.  Query t
@@ -752,13 +752,23 @@ typedef struct {
   int past;
   double scale;
   int B, H, T, Lc;
+  const int *sel; /* NULL: every (b,h,t); else n_sel (b, h, t) triples */
   double *out, *lse;
 } chunk_ctx;
 
 static void chunk_unit(void *vctx, long unit, double *scratch) {
   chunk_ctx *c = (chunk_ctx *)vctx;
-  const long t = unit % c->T, bh = unit / c->T;
-  const long b = bh / c->H, h = bh % c->H;
+  long t, b, h;
+  if (c->sel) {
+    b = c->sel[3 * unit];
+    h = c->sel[3 * unit + 1];
+    t = c->sel[3 * unit + 2];
+  } else {
+    t = unit % c->T;
+    h = (unit / c->T) % c->H;
+    b = unit / ((long)c->T * c->H);
+  }
+  const long bh = b * c->H + h;
   const long nk = c->past + t + 1; /* keys 0 .. past + t */
   double qn[OR_NOPE], qpe[OR_ROPE], qr[OR_ROPE], o[OR_VDIM], l;
   const long qrow = bh * c->T + t;
@@ -773,6 +783,11 @@ static void chunk_unit(void *vctx, long unit, double *scratch) {
   rows_t kn = {c->k_nope_cache + bh * c->Lc * OR_NOPE, OR_NOPE};
   rows_t vv = {c->v_cache + bh * c->Lc * OR_VDIM, OR_VDIM};
   attend_row(qn, qr, kn, kr, OR_ROPE, vv, nk, c->scale, scratch, o, &l);
+  if (c->sel) {
+    for (int d = 0; d < OR_VDIM; d++) c->out[unit * OR_VDIM + d] = o[d];
+    if (c->lse) c->lse[unit] = l;
+    return;
+  }
   double *dst = c->out + ((size_t)b * c->T + t) * ((size_t)c->H * OR_VDIM) + (size_t)h * OR_VDIM;
   for (int d = 0; d < OR_VDIM; d++) dst[d] = o[d];
   if (c->lse) c->lse[qrow] = l;
@@ -787,6 +802,27 @@ int oracle_prefill_chunk(const uint16_t *q_nope, const uint16_t *q_pe, const uin
                          int r_rows, int past, double scale, int B, int H, int T, int Lc,
                          double *out, double *lse, int nthreads) {
   if (B <= 0 || H <= 0 || T <= 0 || past < 0 || past + T > Lc || past + T > r_rows) return 1;
-  chunk_ctx c = {q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, past, scale, B, H, T, Lc, out, lse};
+  chunk_ctx c = {q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, past, scale, B, H, T, Lc,
+                 NULL, out, lse};
   return run_units(chunk_unit, &c, (long)B * H * T, (size_t)(past + T) * (1 + OR_ROPE), nthreads);
+}
+
+/* Selected rows of the chunked prefill: sel holds n_sel (b, h, t) triples;
+ * out [n_sel][128], lse [n_sel] or NULL.  Each row is the same computation as
+ * in oracle_prefill_chunk (query at position past + t over cache rows
+ * 0 .. past + t). */
+int oracle_prefill_chunk_rows(const uint16_t *q_nope, const uint16_t *q_pe,
+                              const uint16_t *k_nope_cache, const uint16_t *kpe_cache,
+                              const uint16_t *v_cache, const float *R, int r_rows, int past,
+                              double scale, int B, int H, int T, int Lc, int n_sel, const int *sel,
+                              double *out, double *lse, int nthreads) {
+  if (B <= 0 || H <= 0 || T <= 0 || past < 0 || past + T > Lc || past + T > r_rows || n_sel < 0)
+    return 1;
+  for (int i = 0; i < n_sel; i++)
+    if (sel[3 * i] < 0 || sel[3 * i] >= B || sel[3 * i + 1] < 0 || sel[3 * i + 1] >= H ||
+        sel[3 * i + 2] < 0 || sel[3 * i + 2] >= T)
+      return 1;
+  chunk_ctx c = {q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, past, scale, B, H, T, Lc,
+                 sel, out, lse};
+  return run_units(chunk_unit, &c, (long)n_sel, (size_t)(past + T) * (1 + OR_ROPE), nthreads);
 }

@@ -142,3 +142,84 @@ def test_chunk_long_history(gpu_device):
                                     R.numpy(), past, SCALE)
     check_close(to_host64(o32), want, TOL, "float32 output vs oracle")
     check_close(to_host64(lse), wl, TOL, "lse vs oracle")
+
+
+def _chunk_sampled_check(c, past, heads, rows_per_head, dev, label):
+    """Append the chunk, run the chunked prefill (float32 and bf16 stores) and
+    compare sampled (head, row) outputs with the oracle, row by row."""
+    B, H, T = c["q_nope"].shape[:3]
+    caches = [c["k_nope_cache"], c["kpe_cache"], c["v_cache"]]
+    mla.mla_append_kv(c["k_nope"], c["k_pe"], c["v"], c["R"], past, *caches)
+    o32, lse = mla.mla_attend_prefill_chunk(c["q_nope"], c["q_pe"], *caches, c["R"], past, SCALE,
+                                            out_f32=True, want_lse=True)
+    o16, _ = mla.mla_attend_prefill_chunk(c["q_nope"], c["q_pe"], *caches, c["R"], past, SCALE)
+    torch.cuda.synchronize()
+    check_bf16_is_rne_of_f32(o16, o32)
+    R = c["R"].cpu().numpy()
+    for (b, h), rows in zip(heads, rows_per_head):
+        one = lambda t: bits(t[b:b + 1, h:h + 1])
+        sel = np.stack([np.zeros_like(rows), np.zeros_like(rows), rows], 1)
+        want, wl = oracle.prefill_chunk_rows(one(c["q_nope"]), one(c["q_pe"]), one(caches[0]),
+                                             bits(caches[1][b:b + 1]), one(caches[2]), R, past,
+                                             SCALE, sel)
+        idx = torch.from_numpy(rows).long().to(dev)
+        check_close(to_host64(o32[b, idx, h * 128:(h + 1) * 128]), want, TOL,
+                    f"{label} b={b} h={h} {len(rows)} rows")
+        check_close(to_host64(lse[b, h, idx]), wl, TOL, f"{label} b={b} h={h} lse")
+        check_bf16_close(o16[b, idx, h * 128:(h + 1) * 128], want, f"{label} b={b} h={h} bf16")
+
+
+def test_chunk_paired_schedule_every_row(gpu_device):
+    """B=4, H=64, T=1024 after 500 cached positions: enough work that every
+    workgroup takes a pair of query tiles (the schedule of the long chunks);
+    every row of four heads against the oracle."""
+    B, H, T, past = 4, 64, 1024, 500
+    say(f"prefill chunk paired schedule B={B} H={H} T={T} past={past}")
+    c = inputs.chunk_inputs(B, H, T, past, seed=3600, device=gpu_device)
+    rows = np.arange(T, dtype=np.int32)
+    heads = [(0, 0), (1, 21), (2, 42), (3, 63)]
+    _chunk_sampled_check(c, past, heads, [rows] * len(heads), gpu_device, "paired")
+
+
+def test_chunk_benchmark_launch_sampled(gpu_device):
+    """The chunk the benchmark times (B=1, H=64, a 4096-position chunk after
+    12288 cached positions, same inputs and launch): first 128, last 128 and
+    256 random rows of three heads against the oracle."""
+    B, H, T, past = 1, 64, 4096, 12288
+    say(f"prefill chunk benchmark launch B={B} H={H} T={T} past={past}")
+    c = inputs.chunk_inputs(B, H, T, past, seed=7000, device=gpu_device)
+    rng = np.random.default_rng(12288)
+    heads = [(0, 0), (0, 31), (0, 63)]
+    rows = []
+    for _ in heads:
+        r = set(range(128)) | set(range(T - 128, T)) | set(rng.integers(0, T, 256).tolist())
+        rows.append(np.array(sorted(r), np.int32))
+    _chunk_sampled_check(c, past, heads, rows, gpu_device, "benchmark chunk")
+
+
+@pytest.mark.parametrize("B,H,T,past,L", [(2, 3, 45, 19, 100), (4, 64, 1000, 77, 1200)])
+def test_chunk_unwritten_rows_never_reach_the_output(B, H, T, past, L, gpu_device):
+    """Cache rows at and past past + T (never written by the append) holding
+    bf16 NaN, +inf or -inf give outputs bit-identical to zero-filled rows
+    (past + T is not a multiple of the 32-key tile, so the last key tile
+    straddles it; the second case takes the paired schedule)."""
+    say(f"prefill chunk unwritten rows B={B} H={H} T={T} past={past} L={L}")
+    d = chunk_inputs(B, H, T, 3700 + T)
+    R = torch.from_numpy(inputs.rope_angles(L)).to(gpu_device)
+    hist = [t.to(gpu_device) for t in junk_caches(B, H, L, 3710)]
+    outs = []
+    for fill in (0x0000, 0x7FC0, 0x7F80, 0xFF80):  # zero, NaN, +inf, -inf
+        caches = [t.clone() for t in hist]
+        caches[0][:, :, past + T:].view(torch.int16).fill_(fill - (1 << 16 if fill >= 1 << 15 else 0))
+        caches[1][:, past + T:].view(torch.int16).fill_(fill - (1 << 16 if fill >= 1 << 15 else 0))
+        caches[2][:, :, past + T:].view(torch.int16).fill_(fill - (1 << 16 if fill >= 1 << 15 else 0))
+        mla.mla_append_kv(d["k_nope"].to(gpu_device), d["k_pe"].to(gpu_device), d["v"].to(gpu_device),
+                          R, past, *caches)
+        o, l = run_chunk(d, caches, R, past, gpu_device, out_f32=True, want_lse=True)
+        assert torch.isfinite(o).all() and torch.isfinite(l).all(), f"fill {fill:#06x}"
+        outs.append((o, l))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    want, _ = oracle.prefill_chunk(bits(d["q_nope"]), bits(d["q_pe"]),
+                                   *[bits(t) for t in caches], R.cpu().numpy(), past, SCALE)
+    check_close(to_host64(outs[0][0]), want, TOL, "float32 output vs oracle")

@@ -107,6 +107,61 @@ def test_attention_then_oproj_workload1(gpu_device):
     check_close(to_host64(y32), want_chain, 1e-3, "o_proj on the GPU's attention output")
 
 
+def test_attention_then_oproj_workload2(gpu_device):
+    """The whole step at the 1024-position workload, every output: the GPU's
+    bf16 attention output into o_proj (float32 store) against the oracle's
+    projection of its own bf16-rounded attention output (max-abs 1e-2)."""
+    w_ = inputs.WORKLOADS[2]
+    B, H, T = w_["B"], w_["H"], w_["T"]
+    say("attention + o_proj, workload 2")
+    d = inputs.prefill_inputs(B, H, T, workload=2)
+    wo = inputs.out_proj_weight(workload=2)
+    o, _ = oracle.prefill(bits(d["q_nope"]), bits(d["q_pe"]), bits(d["k_nope"]), bits(d["k_pe"]),
+                          bits(d["v"]), d["R"].numpy(), SCALE, want_lse=False)
+    o16_bits = bits(torch.from_numpy(oracle.bf16_round(o).reshape(B * T, H * 128)).to(torch.bfloat16))
+    want = oracle.out_proj(o16_bits, bits(wo))
+    g = {k: v.to(gpu_device) for k, v in d.items()}
+    attn, _ = mla.mla_attend_prefill(g["q_nope"], g["q_pe"], g["k_nope"], g["k_pe"], g["v"], g["R"],
+                                     SCALE)
+    y32 = mla.mla_out_proj(attn.view(B * T, H * 128), wo.to(gpu_device), out_f32=True)
+    torch.cuda.synchronize()
+    check_close(to_host64(y32), want, TOL, "delta_attn (float32 store) vs oracle")
+
+
+def test_attention_then_oproj_workload3_sampled(gpu_device):
+    """The whole step at B=4, T=4096 in the benchmark's launch: for sampled
+    (sequence, position) rows the oracle computes the attention of all 64
+    heads, rounds it to bf16 and projects it; the GPU's projected rows
+    (float32 store) must agree within 1e-2."""
+    w_ = inputs.WORKLOADS[3]
+    B, H, T = w_["B"], w_["H"], w_["T"]
+    say("attention + o_proj, workload 3 sampled rows")
+    d = inputs.prefill_inputs(B, H, T, workload=3, device=gpu_device)
+    wo = inputs.out_proj_weight(workload=3, device=gpu_device)
+    attn, _ = mla.mla_attend_prefill(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], d["R"],
+                                     SCALE)
+    y32 = mla.mla_out_proj(attn.view(B * T, H * 128), wo, out_f32=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(33)
+    picks = [(0, 0), (0, T - 1), (B - 1, T - 1), (1, 255), (2, 256), (3, 2047)]
+    picks += [(int(rng.integers(0, B)), int(rng.integers(0, T))) for _ in range(10)]
+    R = d["R"].cpu().numpy()
+    wo_bits = bits(wo)
+    worst = 0.0
+    for b in sorted({p[0] for p in picks}):
+        ts = np.array(sorted({t for bb, t in picks if bb == b}), np.int32)
+        sel = np.array([[0, h, t] for t in ts for h in range(H)], np.int32)
+        one = lambda x: bits(x[b:b + 1])
+        o, _ = oracle.prefill_rows(one(d["q_nope"]), one(d["q_pe"]), one(d["k_nope"]),
+                                   one(d["k_pe"]), one(d["v"]), R, SCALE, sel)
+        x16 = oracle.bf16_round(o.reshape(len(ts), H * 128))
+        x_bits = bits(torch.from_numpy(x16).to(torch.bfloat16))
+        want = oracle.out_proj(x_bits, wo_bits)
+        got = to_host64(y32[torch.from_numpy(b * T + ts).long().to(gpu_device)])
+        worst = max(worst, check_close(got, want, TOL, f"b={b} {len(ts)} rows"))
+    say(f"  worst {worst:.3e}")
+
+
 # ------------------------------------------------------------- FP8 weights
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 1), (17, 256, 100), (64, 8192, 7168), (130, 1024, 300),

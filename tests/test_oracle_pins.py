@@ -626,6 +626,32 @@ def test_chunk_of_one_equals_decode_and_ignores_later_rows():
     assert np.array_equal(g2, got)
 
 
+def test_chunk_rows_equal_full_and_ignore_rows_past_the_chunk():
+    """Sampled rows of the chunked prefill equal the full chunked prefill's
+    rows bit for bit, and NaN / infinity in cache rows at or past past + T
+    (never written by the append) change nothing."""
+    B, H, T, past, Lc = 2, 3, 19, 23, 57
+    qn, qp, kn, kp, v = chunk_case(B, H, T, 2700)
+    R = inputs.rope_angles(Lc)
+    kc, pc, vc = empty_caches(B, H, Lc)
+    hist = empty_caches(B, H, past, 2710)
+    kc[:, :, :past], pc[:, :past], vc[:, :, :past] = hist
+    oracle.append_kv(kn, kp, v, R, past, kc, pc, vc)
+    out, lse = oracle.prefill_chunk(qn, qp, kc, pc, vc, R, past, SCALE)
+    sel = np.array([[0, 0, 0], [1, 2, T - 1], [0, 1, 7], [1, 0, 13], [1, 1, T - 1]], np.int32)
+    ro, rl = oracle.prefill_chunk_rows(qn, qp, kc, pc, vc, R, past, SCALE, sel)
+    for i, (b, h, t) in enumerate(sel):
+        assert np.array_equal(ro[i], out[b, t, h * 128:(h + 1) * 128])
+        assert rl[i] == lse[b, h, t]
+    for bad in (0x7FC0, 0x7F80, 0xFF80):  # bf16 NaN, +inf, -inf
+        kc2, pc2, vc2 = kc.copy(), pc.copy(), vc.copy()
+        kc2[:, :, past + T:] = bad
+        pc2[:, past + T:] = bad
+        vc2[:, :, past + T:] = bad
+        o2, l2 = oracle.prefill_chunk(qn, qp, kc2, pc2, vc2, R, past, SCALE)
+        assert np.array_equal(o2, out) and np.array_equal(l2, lse)
+
+
 # ------------------------------------------------------------ fp8 weights
 
 def test_e4m3_decode_matches_torch():

@@ -5,8 +5,8 @@
 // updated with keys that are already rotated and joined ([k_nope | rot(k_pe)],
 // 192 wide) and with the values; scores are Q·Kᵀ·softmax_scale, the softmax
 // runs in float32 and mixes the 128-wide values.  The new query is rotated at
-// its own position (page "Kimi K2 · Transformer blocks": positions continue
-// from the cached length).
+// its own position (page "Kimi K2 · Transformer blocks": position ids start
+// after the tokens already cached).
 //
 // Two cache layouts: joined key rows [nope 128 | rotated rope 64] per head,
 // or nope rows per head plus one rotated rope key per position shared by all

@@ -2,7 +2,7 @@
 // inputs, float32 accumulation, no bias.
 //
 // Page "Kimi K2 · Mix and project": parameter table (8,192 × 7,168 output
-// projection), explanation (the only step that mixes heads) and code excerpt
+// projection), explanation (no earlier step combines heads) and code excerpt
 // "mla-output" (o_proj applied to the head-major [B, T, 64·128] output);
 // page "Block input", config.json: attention_bias false.
 //

@@ -152,10 +152,12 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
 
   // ---- asynchronous tile copies.  Copy i of copying wave w moves chunk
   // j = (w + NCW i) (a spare copy repeats chunk j - NCW).  Lane offsets inside the
-  // sequence's tensor are fixed; the buffer descriptor's base advances with the
-  // tile.  One descriptor per tensor and sequence: rows past the end of the
-  // tensor read as zero; rows past T inside it belong to the next head and are
-  // masked.
+  // head's rows are fixed; the buffer descriptor's base advances with the tile.
+  // One descriptor per tensor and (sequence, head), whose extent ends at the
+  // last row that holds data (position past+T-1): rows beyond it read as zero,
+  // so cache rows the caller never wrote (any bit pattern, NaN included) reach
+  // neither the scores nor the value product.
+  static_assert(G == 1, "per-head copy descriptors assume one head per workgroup");
   uint32_t voff[DPW];
   int kind[DPW];  // 0 k_nope, 1 rotated key, 2 V (wave-uniform)
 #pragma unroll
@@ -174,8 +176,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
         R = BK - 1;
         c = 15;
       }
-      const int hh = min(hg * G + min(gg, G - 1), H - 1);
-      v = ((uint32_t)hh * (uint32_t)LK + (uint32_t)akey(R)) * 256u + c * 16;
+      v = (uint32_t)akey(R) * 256u + c * 16;
       kind[i] = 0;
     } else if (j < CKP) {
       const int s = (j - CK) * 64 + lane;  // slot in the rotated-key region (8 per row)
@@ -185,19 +186,18 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
       kind[i] = 1;
     } else {
       const int s = (j - CKP) * 64 + lane;  // slot in the V region (16 per row)
-      const int gg = s / (BK * 16);
-      const int row = (s % (BK * 16)) / 16;
+      const int row = s / 16;
       const int c = (s % 16) ^ ((row & 3) << 2);
-      const int hh = min(hg * G + gg, H - 1);
-      v = ((uint32_t)hh * (uint32_t)LK + (uint32_t)row) * 256u + c * 16;
+      v = (uint32_t)row * 256u + c * 16;
       kind[i] = 2;
     }
     voff[i] = v;
   }
-  const uint16_t* kseq = p.k_nope + (size_t)b * H * LK * kNope;
-  const uint16_t* vseq = p.v + (size_t)b * H * LK * kV;
+  const int headc = head_ok ? head : H - 1;
+  const uint16_t* khead = p.k_nope + ((size_t)b * H + headc) * LK * kNope;
+  const uint16_t* vhead = p.v + ((size_t)b * H + headc) * LK * kV;
   const uint16_t* pseq = p.kpe_rot + (size_t)b * LK * kRope;
-  const uint32_t seq_bytes = (uint32_t)((size_t)H * LK * 256);
+  const uint32_t nvis = (uint32_t)(past + p.T);  // rows 0 .. past+T-1 hold data
 
   // Copies of one tile: descriptors whose base advances with the tile, and the
   // stage they fill.  Past the last tile the descriptors are empty (nothing is
@@ -211,9 +211,10 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     const bool live = kt < nkt;
     const uint32_t k0 = live ? (uint32_t)(kt * BK) : 0u;
     Copies c;
-    c.rK = make_rsrc(kseq + (size_t)k0 * kNope, live ? seq_bytes - k0 * 256u : 0u);
-    c.rP = make_rsrc(pseq + (size_t)k0 * kRope, live ? (uint32_t)(LK - (int)k0) * 128u : 0u);
-    c.rV = make_rsrc(vseq + (size_t)k0 * kV, live ? seq_bytes - k0 * 256u : 0u);
+    // live tiles start below kend <= nvis, so the extents are positive
+    c.rK = make_rsrc(khead + (size_t)k0 * kNope, live ? (nvis - k0) * 256u : 0u);
+    c.rP = make_rsrc(pseq + (size_t)k0 * kRope, live ? (nvis - k0) * 128u : 0u);
+    c.rV = make_rsrc(vhead + (size_t)k0 * kV, live ? (nvis - k0) * 256u : 0u);
     c.buf = buf;
     return c;
   };
@@ -266,7 +267,6 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     const int q0 = qt * BQ + qb * 32;
     const int myq = q0 + ln;
     const int myqc = myq < T ? myq : T - 1;
-    const int headc = head_ok ? head : H - 1;
     const int kend = past + min(T, qt * BQ + BQ);  // keys of the tile's last query, plus one
     const int nkt = (kend + BK - 1) / BK;
 

@@ -1,6 +1,6 @@
 // Rotary prologue of the prefill: cos/sin of the angle table and the rotated
 // shared rotary key; the same kernel writes the rotated key of a new chunk
-// into the cache (positions continue from the cached length: page "Kimi K2 ·
+// into the cache (position ids start after the cached tokens: page "Kimi K2 ·
 // Transformer blocks", model-body excerpt), next to a plain row copy for the
 // chunk's nope keys and values.
 //

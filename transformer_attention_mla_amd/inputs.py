@@ -181,6 +181,23 @@ def decode_latent_inputs(B: int, H: int, L: int, q_pos: int, workload: int = 0, 
     return dict(q_nope=q_nope, q_pe=q_pe, ckv=ckv, kpe=kpe, w_kv_b=w_kv_b, R=R, q_pos=q_pos)
 
 
+def chunk_inputs(B: int, H: int, T: int, past: int, seed: int = 7000, device="cpu"):
+    """A prefill chunk of T positions after `past` cached ones: q_nope, q_pe,
+    k_nope, k_pe, v of the chunk (bf16 N(0,1)), the shared-rotary caches
+    k_nope_cache [B,H,L,128], kpe_cache [B,L,64], v_cache [B,H,L,128] with
+    L = past + T (every row N(0,1): rows 0..past-1 stand for the history, rows
+    past.. are overwritten by the append) and R with L rows.  Seeds
+    seed + k, k = 0..7."""
+    import torch
+
+    L = past + T
+    g = lambda shape, k: normal_bf16(shape, seed + k, device=device)
+    return dict(q_nope=g((B, H, T, 128), 0), q_pe=g((B, H, T, 64), 1), k_nope=g((B, H, T, 128), 2),
+                k_pe=g((B, 1, T, 64), 3), v=g((B, H, T, 128), 4), k_nope_cache=g((B, H, L, 128), 5),
+                kpe_cache=g((B, L, 64), 6), v_cache=g((B, H, L, 128), 7),
+                R=torch.from_numpy(rope_angles(L)).to(device))
+
+
 def out_proj_weight(N: int = D_MODEL, K: int = 64 * 128, workload: int = 0, device="cpu"):
     """w_o [N, K] bf16 N(0, 0.02), stored as the linear layer stores it."""
     return normal_bf16((N, K), seed_of(workload, SEED_WO), std=0.02, device=device)
