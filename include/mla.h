@@ -111,6 +111,29 @@ int mla_attend_prefill(const mla_bf16 *q_nope, const mla_bf16 *q_pe, const mla_b
                        size_t workspace_bytes, void *out, float *lse, uint32_t flags,
                        void *stream);
 
+/* Allocation-free variant of mla_attend_prefill, for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * computation and results (bit for bit) as mla_attend_prefill, without
+ * `workspace` / `workspace_bytes`: the cos/sin table and the rotated shared key
+ * go to a static buffer of MLA_PREFILL_NOALLOC_SCRATCH_BYTES that each GPU
+ * holds for the life of the process.  The call needs
+ * mla_prefill_workspace_bytes(B, H, T) = T·256 + B·T·128 bytes (each part
+ * rounded up to 256); sizes beyond MLA_PREFILL_NOALLOC_SCRATCH_BYTES (16 MiB:
+ * e.g. B·T up to 98,304 positions at T = 16384, 129,024 at T = 1024) return
+ * MLA_ERR_WORKSPACE before anything is enqueued.  No device memory is
+ * allocated or freed by this call.  Every call on one GPU uses that GPU's
+ * single buffer, so calls that overlap in time on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller; the buffer
+ * needs no clearing (each call writes what it reads).  Other errors as for
+ * mla_attend_prefill. */
+#define MLA_PREFILL_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int mla_attend_prefill_noalloc(const mla_bf16 *q_nope, const mla_bf16 *q_pe,
+                               const mla_bf16 *k_nope, const mla_bf16 *k_pe, const mla_bf16 *v,
+                               const float *R, int r_rows, float softmax_scale, int B, int H,
+                               int T, void *out, float *lse, uint32_t flags, void *stream);
+
 /* KV-cache append (page "Kimi K2 · Mix and project", excerpt "mla-prefill": the
  * cache is updated with the keys after the rotary step; page "Kimi K2 ·
  * Transformer blocks": position ids start after the cached tokens): a chunk

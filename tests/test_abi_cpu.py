@@ -133,6 +133,35 @@ def test_prefill_rejects(kw, code):
     assert prefill(**kw) == code
 
 
+def prefill_noalloc(**kw):
+    a = dict(q_nope=A[0], q_pe=A[1], k_nope=A[2], k_pe=A[3], v=A[4], R=A[5], r_rows=1 << 20,
+             scale=0.07, B=1, H=2, T=64, out=A[7], lse=None, flags=0)
+    a.update(kw)
+    return mla.lib().mla_attend_prefill_noalloc(a["q_nope"], a["q_pe"], a["k_nope"], a["k_pe"],
+                                                a["v"], a["R"], a["r_rows"], a["scale"], a["B"],
+                                                a["H"], a["T"], a["out"], a["lse"], a["flags"], None)
+
+
+# Every case fails validation: B * T beyond the static buffer (16 MiB holds
+# T*256 + B*T*128 bytes) is MLA_ERR_WORKSPACE, before any device call.
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_nope=None), NULL), (dict(out=None), NULL), (dict(flags=2), FLAGS),
+    (dict(T=0), DIM), (dict(scale=0.0), SCALE),
+    (dict(B=7, T=16384), WORKSPACE), (dict(B=1, T=65536), WORKSPACE),
+    (dict(B=127, T=1024), WORKSPACE),
+    (dict(q_pe=ctypes.c_void_p(2 * 16 * GB + 8)), ALIGN),
+    (dict(out=ctypes.c_void_p(1 * 16 * GB + 4096)), ALIAS),
+])
+def test_prefill_noalloc_rejects(kw, code):
+    assert prefill_noalloc(**kw) == code
+
+
+def test_prefill_noalloc_limit_matches_workspace_formula():
+    limit = 16 << 20
+    assert mla.mla_prefill_workspace_bytes(6, 1, 16384) <= limit < mla.mla_prefill_workspace_bytes(7, 1, 16384)
+    assert mla.mla_prefill_workspace_bytes(126, 1, 1024) <= limit < mla.mla_prefill_workspace_bytes(127, 1, 1024)
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(kc=None), NULL), (dict(out=None), NULL),
     (dict(flags=4), FLAGS),

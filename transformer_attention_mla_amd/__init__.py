@@ -58,6 +58,8 @@ def lib():
     L.mla_prefill_workspace_bytes.argtypes = [I, I, I]
     L.mla_prefill_workspace_bytes.restype = Z
     L.mla_attend_prefill.argtypes = [P, P, P, P, P, P, I, F, I, I, I, P, Z, P, P, U, P]
+    L.mla_attend_prefill_noalloc.argtypes = [P, P, P, P, P, P, I, F, I, I, I, P, P, U, P]
+    L.mla_attend_prefill_noalloc.restype = I
     L.mla_attend_prefill.restype = I
     L.mla_append_kv.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, P, U, P]
     L.mla_append_kv.restype = I
@@ -206,6 +208,44 @@ def mla_attend_prefill(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, out=N
                                   MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
     if rc:
         raise MlaError(rc, "mla_attend_prefill")
+    return out, lse
+
+
+def mla_attend_prefill_noalloc(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, out=None,
+                               lse=None, want_lse=False, out_f32=False, stream=None):
+    """mla_attend_prefill without a workspace argument: the library's static
+    per-device buffer (MLA_PREFILL_NOALLOC_SCRATCH_BYTES) holds the cos/sin
+    table and the rotated shared key.  Same shapes and results; calls that
+    overlap on one GPU race.  Allocates `out` / `lse` here only when they are
+    not given (pass them to allocate nothing at all)."""
+    torch = _torch()
+    if q_nope.dim() != 4:
+        raise ValueError("q_nope must be [B, H, T, 128]")
+    B, H, T, _ = q_nope.shape
+    dev = q_nope.device
+    bf = torch.bfloat16
+    _check(q_nope, "q_nope", bf, (B, H, T, NOPE), dev)
+    _check(q_pe, "q_pe", bf, (B, H, T, ROPE), dev)
+    _check(k_nope, "k_nope", bf, (B, H, T, NOPE), dev)
+    _check(k_pe, "k_pe", bf, (B, 1, T, ROPE), dev)
+    _check(v, "v", bf, (B, H, T, VDIM), dev)
+    if R.dim() != 2:
+        raise ValueError("R must be [r_rows, 32]")
+    _check(R, "R", torch.float32, (R.shape[0], PAIRS), dev)
+    odt = torch.float32 if out_f32 else bf
+    if out is None:
+        out = torch.empty((B, T, H * VDIM), dtype=odt, device=dev)
+    _check(out, "out", odt, (B, T, H * VDIM), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H, T), dev)
+    rc = lib().mla_attend_prefill_noalloc(_ptr(q_nope), _ptr(q_pe), _ptr(k_nope), _ptr(k_pe),
+                                          _ptr(v), _ptr(R), R.shape[0], float(softmax_scale), B, H,
+                                          T, _ptr(out), _ptr(lse), MLA_OUT_F32 if out_f32 else 0,
+                                          _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_attend_prefill_noalloc")
     return out, lse
 
 

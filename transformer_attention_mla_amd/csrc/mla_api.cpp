@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "mla.h"
 #include "mla_internal.h"
@@ -111,11 +112,18 @@ size_t mla_prefill_workspace_bytes(int B, int H, int T) {
   return mla::prefill_workspace_layout(B, T).total;
 }
 
-int mla_attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16* k_nope,
-                       const mla_bf16* k_pe, const mla_bf16* v, const float* R, int r_rows,
-                       float softmax_scale, int B, int H, int T, void* workspace,
-                       size_t workspace_bytes, void* out, float* lse, uint32_t flags,
-                       void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by mla_attend_prefill and mla_attend_prefill_noalloc.  `scratch` is
+// null for the caller-workspace entry point; otherwise it resolves the static
+// buffer once the arguments are validated (it needs the current device).
+int attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16* k_nope,
+                   const mla_bf16* k_pe, const mla_bf16* v, const float* R, int r_rows,
+                   float softmax_scale, int B, int H, int T, void* workspace,
+                   size_t workspace_bytes, void* out, float* lse, uint32_t flags, void* stream,
+                   void* (*scratch)(int* status)) {
   if (!q_nope || !q_pe || !k_nope || !k_pe || !v || !R || !out) return MLA_ERR_NULL;
   if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
   if (!dims_ok(B, H, T, kQK) || r_rows <= 0 || r_rows > kMaxDim || T > r_rows ||
@@ -123,7 +131,8 @@ int mla_attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_b
     return MLA_ERR_DIM;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_SCALE;
   const mla::PrefillWorkspace ws = mla::prefill_workspace_layout(B, T);
-  if (!workspace || workspace_bytes < ws.total) return MLA_ERR_WORKSPACE;
+  if (!scratch && !workspace) return MLA_ERR_WORKSPACE;
+  if (workspace_bytes < ws.total) return MLA_ERR_WORKSPACE;
   if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(k_nope) || !aligned16(k_pe) ||
       !aligned16(v) || !aligned16(R) || !aligned16(out) || !aligned16(lse) || !aligned16(workspace))
     return MLA_ERR_ALIGN;
@@ -132,10 +141,16 @@ int mla_attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_b
   const Range in[] = {{q_nope, bht * kNope * 2}, {q_pe, bht * kRope * 2}, {k_nope, bht * kNope * 2},
                       {k_pe, (size_t)B * T * kRope * 2}, {v, bht * kV * 2},
                       {R, (size_t)r_rows * mla::kPairs * 4}};
-  const Range outs[] = {{out, bht * kV * out_elt}, {lse, lse ? bht * 4 : 0}, {workspace, ws.total}};
+  const Range outs[] = {{out, bht * kV * out_elt}, {lse, lse ? bht * 4 : 0},
+                        {workspace, scratch ? 0 : ws.total}};
   if (any_alias(in, 6, outs, 3)) return MLA_ERR_ALIAS;
   const int dev = check_device();
   if (dev != MLA_OK) return dev;
+  if (scratch) {
+    int st = MLA_OK;
+    workspace = scratch(&st);
+    if (st != MLA_OK) return st;
+  }
 
   mla::PrefillParams p;
   p.q_nope = q_nope;
@@ -160,6 +175,66 @@ int mla_attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_b
   if (mla::launch_rope_prep(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
   if (mla::launch_prefill(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
   return MLA_OK;
+}
+
+}  // namespace
+
+// Static workspace of mla_attend_prefill_noalloc: the cos/sin table and the
+// rotated shared key of one call.  Each device holds its own copy for the
+// life of the process.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address is taken once per device with
+// hipGetSymbolAddress and only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[MLA_PREFILL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's `scratch` (the current device, already
+// checked to be gfx950).  Resolved on the first call on each device.
+void* device_scratch(int* status) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = MLA_ERR_DEVICE;
+    return nullptr;
+  }
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      *status = MLA_ERR_DEVICE;
+      return nullptr;
+    }
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16* k_nope,
+                       const mla_bf16* k_pe, const mla_bf16* v, const float* R, int r_rows,
+                       float softmax_scale, int B, int H, int T, void* workspace,
+                       size_t workspace_bytes, void* out, float* lse, uint32_t flags,
+                       void* stream) {
+  return attend_prefill(q_nope, q_pe, k_nope, k_pe, v, R, r_rows, softmax_scale, B, H, T,
+                        workspace, workspace_bytes, out, lse, flags, stream, nullptr);
+}
+
+int mla_attend_prefill_noalloc(const mla_bf16* q_nope, const mla_bf16* q_pe,
+                               const mla_bf16* k_nope, const mla_bf16* k_pe, const mla_bf16* v,
+                               const float* R, int r_rows, float softmax_scale, int B, int H,
+                               int T, void* out, float* lse, uint32_t flags, void* stream) {
+  return attend_prefill(q_nope, q_pe, k_nope, k_pe, v, R, r_rows, softmax_scale, B, H, T, nullptr,
+                        MLA_PREFILL_NOALLOC_SCRATCH_BYTES, out, lse, flags, stream,
+                        device_scratch);
 }
 
 // ------------------------------------------------ chunked prefill, append
