@@ -72,6 +72,11 @@ def _load():
     lib.oracle_e4m3_to_double_array.argtypes = [P, P, ctypes.c_size_t]
     lib.oracle_dequant_fp8.argtypes = [P, P, I, I, P]
     lib.oracle_dequant_fp8.restype = I
+    lib.oracle_e4m3_from_float_array.argtypes = [P, P, ctypes.c_size_t]
+    lib.oracle_act_quant.argtypes = [P, I, I, P, P]
+    lib.oracle_act_quant.restype = I
+    lib.oracle_out_proj_fp8_dyn.argtypes = [P, P, P, I, I, I, P, I]
+    lib.oracle_out_proj_fp8_dyn.restype = I
     lib.oracle_append_kv.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, P]
     lib.oracle_append_kv.restype = I
     lib.oracle_prefill_chunk.argtypes = [P, P, P, P, P, P, I, I, D, I, I, I, I, P, P, I]
@@ -370,6 +375,50 @@ def dequant_fp8(w8, scale):
     if lib.oracle_dequant_fp8(_p(w8), _p(scale), N, K, _p(out)):
         raise ValueError("oracle_dequant_fp8 failed")
     return out
+
+
+def e4m3_from_float(v):
+    """e4m3 ("fn") codes of float32 values, round to nearest even; values that
+    round above 448 (and NaN) give NaN codes."""
+    lib = _load()
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib.oracle_e4m3_from_float_array(_p(v), _p(out), v.size)
+    return out
+
+
+def act_quant(x):
+    """Dynamic activation quantization of x [M,K] (bf16 bits): per row and
+    128-column block, scale = max(amax, 1e-4) / 448 in float32 and codes
+    e4m3(x / scale).  Returns (q uint8 [M,K], scale float32 [M,ceil(K/128)])."""
+    lib = _load()
+    x = _u16(x)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, (K + 127) // 128), dtype=np.float32)
+    if lib.oracle_act_quant(_p(x), M, K, _p(q), _p(s)):
+        raise ValueError("oracle_act_quant failed")
+    return q, s
+
+
+def out_proj_fp8_dyn(x, w8, scale, nthreads=None):
+    """y = dequant(act_quant(x)) · dequant(w8, scale)ᵀ in double: the
+    projection with FP8 activations (dynamic 1 x 128 scales) and the FP8
+    checkpoint weight (128 x 128 block scales).  x [M,K] bf16 bits, w8 [N,K]
+    uint8, scale [ceil(N/128), ceil(K/128)] float32; returns y [M,N] double."""
+    lib = _load()
+    x = _u16(x)
+    w8 = np.ascontiguousarray(w8, dtype=np.uint8)
+    scale = _f32(scale)
+    M, K = x.shape
+    N = w8.shape[0]
+    if w8.shape != (N, K) or scale.shape != ((N + 127) // 128, (K + 127) // 128):
+        raise ValueError("out_proj_fp8_dyn shapes")
+    y = np.empty((M, N), dtype=np.float64)
+    if lib.oracle_out_proj_fp8_dyn(_p(x), _p(w8), _p(scale), M, K, N, _p(y),
+                                   nthreads or default_threads()):
+        raise ValueError("oracle_out_proj_fp8_dyn failed")
+    return y
 
 
 def out_proj_fp8(x, w8, scale, nthreads=None):

@@ -710,6 +710,118 @@ int oracle_dequant_fp8(const uint8_t *w8, const float *scale, int N, int K, uint
   return 0;
 }
 
+/* ------------------------------------ FP8 activations (dynamic scheme) ---- */
+
+/* Page "Block input", config.json quantization_config: fmt e4m3, weight blocks
+ * of 128 x 128, activation_scheme "dynamic" -- the activations are quantized
+ * at run time.  The pages give no recipe for the dynamic activation scales;
+ * the reading here is the public recipe of the model family's FP8 format
+ * (DeepSeek-V3 technical report, fine-grained quantization: activations in
+ * 1 x 128 tiles per token, weights in 128 x 128 blocks; its reference
+ * per-token cast in the DeepGEMM repository): per row and 128-column block,
+ * amax = max |x| in float32, clamped below at 1e-4; scale = amax / 448 (the
+ * largest e4m3 value), in float32; q = e4m3(x / scale), the division in
+ * float32, the conversion rounding to nearest even.  The projection is then
+ * the plain product of the dequantized operands (q times its scale, for x and
+ * for the weight), here in double. */
+
+/* e4m3 ("fn") code of a float: round to nearest even on the format's grid
+ * (spacing 2^(E-3) for |v| in [2^E, 2^(E+1)), E >= -6; 2^-9 below 2^-6); a
+ * magnitude that rounds above 448 has no code and gives NaN (0x7F with the
+ * sign), as does NaN. */
+uint8_t oracle_e4m3_from_float(float v) {
+  const double x = (double)v;
+  if (isnan(x)) return 0x7F;
+  const uint8_t sign = signbit(x) ? 0x80 : 0;
+  const double a = fabs(x);
+  if (a == 0.0) return sign;
+  int E;
+  frexp(a, &E); /* a = f 2^E, f in [0.5, 1): a in [2^(E-1), 2^E) */
+  E -= 1;       /* a in [2^E, 2^(E+1)) */
+  if (E < -6) E = -6;
+  const double spacing = ldexp(1.0, E - 3);
+  const double r = nearbyint(a / spacing) * spacing; /* exact: a/spacing is a scaled float */
+  if (r > 448.0) return (uint8_t)(sign | 0x7F);
+  if (r < ldexp(1.0, -6)) return (uint8_t)(sign | (uint8_t)(r / ldexp(1.0, -9))); /* subnormal */
+  int E2;
+  frexp(r, &E2);
+  E2 -= 1;
+  const int m = (int)(r / ldexp(1.0, E2 - 3)) - 8;
+  return (uint8_t)(sign | ((E2 + 7) << 3) | m);
+}
+
+void oracle_e4m3_from_float_array(const float *v, uint8_t *out, size_t n) {
+  for (size_t i = 0; i < n; i++) out[i] = oracle_e4m3_from_float(v[i]);
+}
+
+/* Activation quantization of x [M][K] (bf16 bits): q [M][K] e4m3 codes and
+ * scale [M][KB] float32, KB = ceil(K/128) (the last block may be shorter). */
+int oracle_act_quant(const uint16_t *x, int M, int K, uint8_t *q, float *scale) {
+  if (M <= 0 || K <= 0) return 1;
+  const int KB = (K + 127) / 128;
+  for (long m = 0; m < M; m++)
+    for (int kb = 0; kb < KB; kb++) {
+      const int k0 = kb * 128, k1 = k0 + 128 < K ? k0 + 128 : K;
+      float amax = 0.0f;
+      for (int k = k0; k < k1; k++) {
+        const float a = fabsf((float)widen(x[m * K + k]));
+        if (a > amax) amax = a;
+      }
+      if (amax < 1e-4f) amax = 1e-4f;
+      const float s = amax / 448.0f;
+      scale[m * KB + kb] = s;
+      for (int k = k0; k < k1; k++) q[m * K + k] = oracle_e4m3_from_float((float)widen(x[m * K + k]) / s);
+    }
+  return 0;
+}
+
+typedef struct {
+  const double *xd, *wd; /* dequantized operands [M][K], [N][K] */
+  int M, K, N;
+  double *y;
+} fp8dyn_ctx;
+
+static void fp8dyn_unit(void *vctx, long unit, double *scratch) {
+  (void)scratch;
+  fp8dyn_ctx *c = (fp8dyn_ctx *)vctx;
+  const double *xr = c->xd + unit * c->K;
+  for (int n = 0; n < c->N; n++) {
+    const double *wr = c->wd + (long)n * c->K;
+    double acc = 0.0;
+    for (int k = 0; k < c->K; k++) acc += xr[k] * wr[k];
+    c->y[unit * c->N + n] = acc;
+  }
+}
+
+/* y [M][N] = dequant(act_quant(x)) · dequant(w8, w_scale)ᵀ in double, no bias:
+ * x [M][K] bf16 bits, w8 [N][K] e4m3 codes, w_scale [ceil(N/128)][ceil(K/128)]. */
+int oracle_out_proj_fp8_dyn(const uint16_t *x, const uint8_t *w8, const float *w_scale, int M,
+                            int K, int N, double *y, int nthreads) {
+  if (M <= 0 || K <= 0 || N <= 0) return 1;
+  const int KB = (K + 127) / 128;
+  uint8_t *q = (uint8_t *)malloc((size_t)M * K);
+  float *sx = (float *)malloc((size_t)M * KB * sizeof(float));
+  double *xd = (double *)malloc((size_t)M * K * sizeof(double));
+  double *wd = (double *)malloc((size_t)N * K * sizeof(double));
+  int rc = 2;
+  if (q && sx && xd && wd) {
+    oracle_act_quant(x, M, K, q, sx);
+    for (long m = 0; m < M; m++)
+      for (int k = 0; k < K; k++)
+        xd[m * K + k] = oracle_e4m3_to_double(q[m * K + k]) * (double)sx[m * KB + k / 128];
+    for (long n = 0; n < N; n++)
+      for (int k = 0; k < K; k++)
+        wd[n * K + k] = oracle_e4m3_to_double(w8[n * K + k]) * (double)w_scale[(n / 128) * KB + k / 128];
+    fp8dyn_ctx c = {xd, wd, M, K, N, y};
+    rc = run_units(fp8dyn_unit, &c, (long)M, 1, nthreads);
+  }
+  free(q);
+  free(sx);
+  free(xd);
+  free(wd);
+  return rc;
+}
+
 /* ------------------------------------------------ chunked prefill, append ---- */
 
 /* Page "Kimi K2 · Transformer blocks", model-body excerpt: positions of a new

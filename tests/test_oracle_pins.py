@@ -686,6 +686,73 @@ def test_dequant_fp8_matches_torch_and_block_layout():
     assert diff[128:256, 256:].any()
 
 
+def test_e4m3_encode_matches_torch():
+    """Round to nearest even on the e4m3 grid, as torch converts float32 to
+    float8_e4m3fn: random values over the whole range, exact ties between
+    neighbours (normal and subnormal), the rounding edge above 448 and
+    zeros."""
+    g = torch.Generator().manual_seed(11)
+    e = torch.randint(-12, 9, (20000,), generator=g).to(torch.float32)
+    v = (torch.rand(20000, generator=g) * 2 - 1) * torch.pow(2.0, e)
+    codes = torch.arange(0, 127, dtype=torch.uint8)
+    grid = codes.view(torch.float8_e4m3fn).to(torch.float32)
+    ties = (grid[:-1] + grid[1:]) / 2  # exact in float32
+    extra = torch.tensor([448.0, 455.0, 464.0, 464.5, 480.0, 0.0, -0.0, 2.0 ** -10, 2.0 ** -12,
+                          3 * 2.0 ** -11, 1e-30])
+    vals = torch.cat([v, ties, -ties, grid, -grid, extra, -extra])
+    want = vals.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_from_float(vals.numpy())
+    # NaN results compare by being NaN codes (torch and the oracle both set 0x7F | sign)
+    assert np.array_equal(got, want)
+
+
+def test_act_quant_matches_the_published_per_token_cast():
+    """Per row and 128-column block: amax (clamped at 1e-4) / 448 and e4m3 of
+    x / scale, written here directly in torch float32 (the reference per-token
+    cast of the FP8 recipe), including a zero block, a tiny block and a ragged
+    last block."""
+    M, K = 9, 300
+    g = torch.Generator().manual_seed(12)
+    x = (torch.randn((M, K), generator=g) * 3).to(torch.bfloat16)
+    x[1, 128:256] = 0
+    x[2, :128] = (torch.randn(128, generator=g) * 1e-6).to(torch.bfloat16)
+    xf = x.float()
+    pad = torch.zeros((M, 384))
+    pad[:, :K] = xf
+    amax = pad.view(M, 3, 128).abs().amax(-1).clamp(min=1e-4)
+    scale = amax / 448.0
+    q = (pad.view(M, 3, 128) / scale[:, :, None]).view(M, 384)[:, :K].to(torch.float8_e4m3fn)
+    gq, gs = oracle.act_quant(inputs.bits(x))
+    assert np.array_equal(gs, scale.numpy())
+    assert np.array_equal(gq, q.view(torch.uint8).numpy())
+    assert np.all(gq[1, 128:256] == 0)
+    # every block's largest magnitude quantizes to the top code (448) unless the clamp applies
+    big = np.abs(xf.numpy()[0, :128]).argmax()
+    assert gq[0, big] & 0x7F == 0x7E
+
+
+def test_out_proj_fp8_dyn_is_the_product_of_dequantized_operands():
+    """The projection equals a numpy float64 matmul of the two dequantized
+    operands (torch's e4m3 values times their block scales), and a scaled
+    identity weight returns each row's dequantized activations."""
+    M, K, N = 7, 384, 200
+    g = torch.Generator().manual_seed(13)
+    x = torch.randn((M, K), generator=g).to(torch.bfloat16)
+    w8, ws = inputs.out_proj_weight_fp8(N, K, workload=2)
+    y = oracle.out_proj_fp8_dyn(inputs.bits(x), w8.numpy(), ws.numpy())
+    q, sx = oracle.act_quant(inputs.bits(x))
+    xd = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy() * np.repeat(sx, 128, 1)[:, :K]
+    wd = w8.view(torch.float8_e4m3fn).double().numpy() * np.repeat(np.repeat(ws.numpy(), 128, 0), 128, 1)[:N, :K]
+    want = xd @ wd.T
+    assert np.max(np.abs(y - want)) <= 1e-12 * np.max(np.abs(want))
+    # W = 2^-3 I: y[m, n] = dequantized x[m, n] / 8, exactly
+    w8i = np.zeros((K, K), np.uint8)
+    w8i[np.arange(K), np.arange(K)] = 0x38  # 1.0
+    wsi = np.full((3, 3), 0.125, np.float32)
+    yi = oracle.out_proj_fp8_dyn(inputs.bits(x), w8i, wsi)
+    assert np.array_equal(yi, xd / 8)
+
+
 def test_out_proj_fp8_input_recipe():
     """The FP8 weight recipe reproduces the bf16 weight to e4m3 precision
     (relative error below 2^-4 of each block's largest element)."""
