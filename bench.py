@@ -433,6 +433,37 @@ def oproj_fp8_figures(mla, inputs, dev, timer, calls=20):
     return res
 
 
+def oproj_fp8_dyn_figures(mla, inputs, dev, timer, calls=20):
+    """o_proj with FP8 activations and the FP8 checkpoint weight on the FP8
+    matrix cores (x quantized per row and 128-column block, then the e4m3 x
+    e4m3 product with both block scales applied per 128-deep slab), at M = 64
+    and M = 16384: the whole call (both kernels), median time cold and warm;
+    GB/s on x + w8 + scales + y (the algorithmic bytes: the quantized copy of
+    x is an intermediate), TFLOP/s."""
+    import torch
+
+    K, N = 64 * 128, inputs.D_MODEL
+    w8, sc = inputs.out_proj_weight_fp8(N, K, workload=3, device=dev)
+    res = {}
+    for M in (64, 16384):
+        print(f"o_proj fp8 dynamic M={M}", file=sys.stderr, flush=True)
+        x = inputs.normal_bf16((M, K), 90 + M, device=dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(16, mla.mla_out_proj_fp8_dyn_workspace_bytes(M, K, N)),
+                         dtype=torch.uint8, device=dev)
+        f = lambda: mla.mla_out_proj_fp8_dyn(x, w8, sc, y=y, workspace=ws)
+        t = timer.both(f, calls)
+        nb = M * K * 2 + N * K + sc.numel() * 4 + M * N * 2
+        res[f"M{M}"] = {"ms_cold": t["cold"], "ms_warm": t["warm"],
+                        "gbps_cold": nb / t["cold"] / 1e6, "gbps_warm": nb / t["warm"] / 1e6,
+                        "tflops_cold": oproj_flops(M, K, N) / t["cold"] / 1e9,
+                        "tflops_warm": oproj_flops(M, K, N) / t["warm"] / 1e9, "bytes": nb}
+        del x, y, ws
+    del w8, sc
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -601,6 +632,7 @@ def main():
             res["decode_latent"] = decode_latent_figures(mla, inputs, scale, dev)
         res["oproj"] = oproj_figures(mla, inputs, w_o, dev, timer)
         res["oproj_fp8"] = oproj_fp8_figures(mla, inputs, dev, timer)
+        res["oproj_fp8_dyn"] = oproj_fp8_dyn_figures(mla, inputs, dev, timer)
         del timer
         torch.cuda.empty_cache()
 

@@ -299,6 +299,47 @@ int mla_out_proj_fp8(const mla_bf16 *x, const uint8_t *w8, const float *w_scale,
                      int K, int N, void *workspace, size_t workspace_bytes, uint32_t flags,
                      void *stream);
 
+/* FP8 activations, the config's "dynamic" scheme (page "Block input",
+ * config.json quantization_config: fmt e4m3, activation_scheme dynamic).  The
+ * pages give no recipe for the run-time scales; this is the public recipe of
+ * the model family's FP8 format (DeepSeek-V3 technical report, fine-grained
+ * quantization, 1 x 128 activation tiles): per row m and 128-column block b,
+ * scale = max(max |x[m, 128b .. 128b+127]|, 1e-4) / 448 and codes
+ * e4m3(x / scale) (float32, the division correctly rounded, round to nearest
+ * even).
+ *
+ *   x         [M, K] bf16, K a multiple of 128
+ *   x8        [M, K] uint8 e4m3 codes (output)
+ *   x_scaleT  [K/128, mla_act_scale_stride(M)] float scales, transposed
+ *             (output; columns M .. stride-1 are not written)
+ * All device pointers, 16-byte aligned, caller-owned.  Returns MLA_ERR_NULL,
+ * MLA_ERR_DIM (M < 1, K not a multiple of 128, M*K >= 2^31), MLA_ERR_ALIGN,
+ * MLA_ERR_ALIAS (an output overlapping x or the other output) before
+ * enqueueing anything.  mla_out_proj_fp8_dyn runs the same quantizer.
+ * mla_act_scale_stride returns M rounded up to 4 (0 for M out of range).
+ */
+int mla_act_scale_stride(int M);
+
+int mla_act_quant(const mla_bf16 *x, int M, int K, uint8_t *x8, float *x_scaleT, void *stream);
+
+/* o_proj in FP8 throughout: y = dequant(act_quant(x)) · dequant(w8, w_scale)ᵀ,
+ * where a dequantized value is its e4m3 code times its block's scale (x: 1 x
+ * 128 blocks from mla_act_quant, weight: 128 x 128 blocks as the checkpoint
+ * stores them).  The products run on the FP8 matrix cores; each 128-deep slab
+ * of the sum is scaled by its two block scales and accumulated in float32.
+ *
+ *   x, w8, w_scale, y, M, N, flags, stream as for mla_out_proj_fp8 (K a
+ *   multiple of 128, at most 2^31 / 256 - 1)
+ *   workspace >= mla_out_proj_fp8_dyn_workspace_bytes(M, K, N) bytes: the
+ *   quantized activations and their scales (and float32 partials when the
+ *   library splits K for M <= 64)
+ */
+size_t mla_out_proj_fp8_dyn_workspace_bytes(int M, int K, int N);
+
+int mla_out_proj_fp8_dyn(const mla_bf16 *x, const uint8_t *w8, const float *w_scale, void *y,
+                         int M, int K, int N, void *workspace, size_t workspace_bytes,
+                         uint32_t flags, void *stream);
+
 /* ------------------------------------------------------- up-projection --
  * The MLA up-projection in front of the attention: the query from its
  * rank-1536 latent and the nope key and value from the rank-512 latent

@@ -303,3 +303,34 @@ def up(**kw):
 ])
 def test_up_project_rejects(kw, code):
     assert up(**kw) == code
+
+
+def oproj_fp8_dyn(**kw):
+    a = dict(x=A[0], w8=A[1], ws=A[2], y=A[3], M=64, K=8192, N=7168, work=A[4], wbytes=1 << 30,
+             flags=0)
+    a.update(kw)
+    return mla.lib().mla_out_proj_fp8_dyn(a["x"], a["w8"], a["ws"], a["y"], a["M"], a["K"], a["N"],
+                                          a["work"], a["wbytes"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(ws=None), NULL), (dict(y=None), NULL), (dict(flags=4), FLAGS),
+    (dict(M=0), DIM), (dict(K=100), DIM), (dict(K=1 << 24), DIM),
+    (dict(work=None), WORKSPACE), (dict(wbytes=1000), WORKSPACE),
+    (dict(y=ctypes.c_void_p(16 * GB + 64)), ALIAS), (dict(w8=ctypes.c_void_p(2 * 16 * GB + 1)), ALIGN),
+])
+def test_oproj_fp8_dyn_rejects(kw, code):
+    assert oproj_fp8_dyn(**kw) == code
+
+
+def test_act_quant_rejects_and_sizes():
+    lib = mla.lib()
+    assert lib.mla_act_quant(None, 4, 128, A[1], A[2], None) == NULL
+    assert lib.mla_act_quant(A[0], 4, 100, A[1], A[2], None) == DIM
+    assert lib.mla_act_quant(A[0], 0, 128, A[1], A[2], None) == DIM
+    assert mla.mla_act_scale_stride(17) == 20 and mla.mla_act_scale_stride(64) == 64
+    # x8 + transposed scales (+ partials when K is split for M <= 64)
+    ws = mla.mla_out_proj_fp8_dyn_workspace_bytes(16384, 8192, 7168)
+    assert ws == 16384 * 8192 + 64 * 16384 * 4
+    assert mla.mla_out_proj_fp8_dyn_workspace_bytes(64, 8192, 7168) > 64 * 8192 + 64 * 64 * 4
+    assert mla.mla_out_proj_fp8_dyn_workspace_bytes(64, 100, 7168) == 0

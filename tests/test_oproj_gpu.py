@@ -224,3 +224,83 @@ def test_oproj_fp8_large_sampled(gpu_device):
     want = oracle.out_proj_fp8_rows(bits(x), w8.cpu().numpy(), sc.cpu().numpy(), rows)
     got = to_host64(y32[torch.from_numpy(rows).long().to(gpu_device)])
     check_close(got, want, TOL, f"{len(rows)} sampled rows")
+
+
+# ------------------------------------------- FP8 activations (dynamic scheme)
+
+@pytest.mark.parametrize("M,K", [(1, 128), (17, 384), (64, 8192), (300, 1024), (5, 256)])
+def test_act_quant_bit_exact(M, K, gpu_device):
+    """Codes and scales of the GPU quantizer equal the oracle's bit for bit
+    (a zero block, a block below the 1e-4 clamp and a large-magnitude row
+    included)."""
+    say(f"act_quant M={M} K={K}")
+    x = inputs.normal_bf16((M, K), 40 + M)
+    x[0, :128] = 0
+    if M > 1:
+        x[1, -128:] = (x[1, -128:].float() * 1e-6).to(torch.bfloat16)
+    if M > 2:
+        x[2] = (x[2].float() * 300).to(torch.bfloat16)
+    want_q, want_s = oracle.act_quant(bits(x))
+    q, sT = mla.mla_act_quant(x.to(gpu_device))
+    torch.cuda.synchronize()
+    got_s = sT.cpu().numpy()[:, :M].T
+    assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32)), "scales differ"
+    assert np.array_equal(q.cpu().numpy(), want_q), "codes differ"
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (17, 256, 100), (64, 8192, 7168), (130, 1024, 300),
+                                   (300, 384, 129), (1000, 512, 1000), (1, 512, 129), (40, 2048, 1000),
+                                   (64, 1024, 7168), (33, 1024, 500), (64, 2048, 225), (16, 4096, 447),
+                                   (64, 16384, 300), (40, 384, 200), (3, 640, 129), (513, 768, 600)])
+def test_oproj_fp8_dyn_parity(M, K, N, gpu_device):
+    """FP8 activations and weights on the FP8 matrix cores against the
+    oracle's product of the dequantized operands: M <= 64 takes the 256 x 64
+    tile with K split over workgroups, larger M the 256 x 256 tile (ragged
+    against both, N not a multiple of 4)."""
+    say(f"o_proj fp8 dynamic parity M={M} K={K} N={N}")
+    x = inputs.normal_bf16((M, K), 50 + M)
+    w8, sc = inputs.out_proj_weight_fp8(N, K, workload=1)
+    want = oracle.out_proj_fp8_dyn(bits(x), w8.numpy(), sc.numpy())
+    xg, wg, sg = x.to(gpu_device), w8.to(gpu_device), sc.to(gpu_device)
+    y32 = mla.mla_out_proj_fp8_dyn(xg, wg, sg, out_f32=True)
+    y16 = mla.mla_out_proj_fp8_dyn(xg, wg, sg)
+    torch.cuda.synchronize()
+    check_close(to_host64(y32), want, TOL, "float32 output vs oracle")
+    check_bf16_is_rne_of_f32(y16, y32)
+    check_bf16_close(y16, want, "bf16 output vs oracle")
+
+
+@pytest.mark.parametrize("M", [64, 300])
+def test_oproj_fp8_dyn_scaled_identity_exact(M, gpu_device):
+    """W = 1.0 on the diagonal with block scale 1/8: every output is one
+    dequantized activation (code x scale, one float32 rounding) over 8,
+    bit for bit."""
+    K, N = 1024, 600
+    x = inputs.normal_bf16((M, K), 8)
+    w8 = torch.zeros((N, K), dtype=torch.uint8)
+    w8[torch.arange(N), torch.arange(N)] = 0x38
+    sc = torch.full(((N + 127) // 128, K // 128), 0.125, dtype=torch.float32)
+    y = mla.mla_out_proj_fp8_dyn(x.to(gpu_device), w8.to(gpu_device), sc.to(gpu_device), out_f32=True)
+    torch.cuda.synchronize()
+    q, sx = oracle.act_quant(bits(x))
+    qv = torch.from_numpy(q).view(torch.float8_e4m3fn).float().numpy()[:, :N]
+    s_full = np.repeat(sx, 128, axis=1)[:, :N].astype(np.float32)
+    want = (qv * s_full).astype(np.float32) * np.float32(0.125)
+    assert np.array_equal(y.cpu().numpy(), want)
+
+
+def test_oproj_fp8_dyn_large_sampled(gpu_device):
+    """M = 16384, K = 8192, N = 7168 (the prefill projection) on sampled rows:
+    quantization is per row, so the oracle's rows from the sampled x rows are
+    exact."""
+    M, K, N = 16384, 8192, 7168
+    say(f"o_proj fp8 dynamic sampled M={M}")
+    x = inputs.normal_bf16((M, K), 79, device=gpu_device)
+    w8, sc = inputs.out_proj_weight_fp8(N, K, workload=3, device=gpu_device)
+    y32 = mla.mla_out_proj_fp8_dyn(x, w8, sc, out_f32=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 12)]))
+    idx = torch.from_numpy(rows).long().to(gpu_device)
+    want = oracle.out_proj_fp8_dyn(bits(x[idx]), w8.cpu().numpy(), sc.cpu().numpy())
+    check_close(to_host64(y32[idx]), want, TOL, f"{len(rows)} sampled rows")

@@ -88,6 +88,14 @@ def lib():
     L.mla_out_proj_fp8.argtypes = [P, P, P, P, I, I, I, P, Z, U, P]
     L.mla_out_proj_fp8.restype = I
     L.mla_out_proj.restype = I
+    L.mla_act_scale_stride.argtypes = [I]
+    L.mla_act_scale_stride.restype = I
+    L.mla_act_quant.argtypes = [P, I, I, P, P, P]
+    L.mla_act_quant.restype = I
+    L.mla_out_proj_fp8_dyn_workspace_bytes.argtypes = [I, I, I]
+    L.mla_out_proj_fp8_dyn_workspace_bytes.restype = Z
+    L.mla_out_proj_fp8_dyn.argtypes = [P, P, P, P, I, I, I, P, Z, U, P]
+    L.mla_out_proj_fp8_dyn.restype = I
     L.mla_up_project.argtypes = [P, P, P, P, I, I, I, P, P, P, P, U, P]
     L.mla_up_project.restype = I
     _lib = L
@@ -443,6 +451,64 @@ def mla_out_proj_fp8(x, w8, w_scale, *, y=None, out_f32=False, workspace=None, s
                                 ws_bytes, MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
     if rc:
         raise MlaError(rc, "mla_out_proj_fp8")
+    return y
+
+
+def mla_act_scale_stride(M):
+    return lib().mla_act_scale_stride(int(M))
+
+
+def mla_out_proj_fp8_dyn_workspace_bytes(M, K, N):
+    return lib().mla_out_proj_fp8_dyn_workspace_bytes(int(M), int(K), int(N))
+
+
+def mla_act_quant(x, *, x8=None, x_scaleT=None, stream=None):
+    """FP8 activations of x [M,K] bf16 (1 x 128 blocks, dynamic scales):
+    returns (x8 [M,K] uint8 e4m3 codes, x_scaleT [K/128, stride] float32, the
+    scales transposed; columns past M unspecified)."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (M, K), dev)
+    ms = mla_act_scale_stride(M)
+    if x8 is None:
+        x8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if x_scaleT is None:
+        x_scaleT = torch.empty((K // 128, ms), dtype=torch.float32, device=dev)
+    _check(x8, "x8", torch.uint8, (M, K), dev)
+    _check(x_scaleT, "x_scaleT", torch.float32, (K // 128, ms), dev)
+    rc = lib().mla_act_quant(_ptr(x), M, K, _ptr(x8), _ptr(x_scaleT), _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_act_quant")
+    return x8, x_scaleT
+
+
+def mla_out_proj_fp8_dyn(x, w8, w_scale, *, y=None, out_f32=False, workspace=None, stream=None):
+    """y = dequant(act_quant(x)) · dequant(w8, w_scale)ᵀ on the FP8 matrix
+    cores: x [M,K] bf16 (quantized to e4m3 per row and 128 columns inside the
+    call), w8 [N,K] uint8 e4m3, w_scale [ceil(N/128), K/128] float32.
+    Returns y [M,N]."""
+    torch = _torch()
+    if x.dim() != 2 or w8.dim() != 2:
+        raise ValueError("x must be [M, K] and w8 [N, K]")
+    M, K = x.shape
+    N = w8.shape[0]
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (M, K), dev)
+    _check(w8, "w8", torch.uint8, (N, K), dev)
+    _check(w_scale, "w_scale", torch.float32, ((N + 127) // 128, (K + 127) // 128), dev)
+    odt = torch.float32 if out_f32 else torch.bfloat16
+    if y is None:
+        y = torch.empty((M, N), dtype=odt, device=dev)
+    _check(y, "y", odt, (M, N), dev)
+    workspace, ws_bytes = _workspace(workspace, mla_out_proj_fp8_dyn_workspace_bytes(M, K, N), dev)
+    rc = lib().mla_out_proj_fp8_dyn(_ptr(x), _ptr(w8), _ptr(w_scale), _ptr(y), M, K, N,
+                                    _ptr(workspace), ws_bytes, MLA_OUT_F32 if out_f32 else 0,
+                                    _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_out_proj_fp8_dyn")
     return y
 
 

@@ -644,4 +644,93 @@ int mla_out_proj_fp8(const mla_bf16* x, const uint8_t* w8, const float* w_scale,
   return MLA_OK;
 }
 
+// -------------------------------------------------------- FP8 activations
+
+int mla_act_scale_stride(int M) { return M > 0 && M <= kMaxDim ? mla::act_scale_stride(M) : 0; }
+
+int mla_act_quant(const mla_bf16* x, int M, int K, uint8_t* x8, float* x_scaleT, void* stream) {
+  if (!x || !x8 || !x_scaleT) return MLA_ERR_NULL;
+  if (!dims_ok(M, K, 1, 1) || K % 128 != 0 || (long long)M * K > 0x7fffffffLL) return MLA_ERR_DIM;
+  if (!aligned16(x) || !aligned16(x8) || !aligned16(x_scaleT)) return MLA_ERR_ALIGN;
+  const size_t ms = (size_t)mla::act_scale_stride(M);
+  const Range in[] = {{x, (size_t)M * K * 2}};
+  const Range outs[] = {{x8, (size_t)M * K}, {x_scaleT, (size_t)(K / 128) * ms * 4}};
+  if (any_alias(in, 1, outs, 2)) return MLA_ERR_ALIAS;
+  const int dev = check_device();
+  if (dev != MLA_OK) return dev;
+  (void)hipGetLastError();
+  if (mla::launch_act_quant(x, x8, x_scaleT, M, K, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+namespace {
+struct Fp8DynWorkspace {
+  size_t x8_off, xs_off, part_off, total;
+  int splits;
+};
+Fp8DynWorkspace fp8dyn_layout(int M, int K, int N) {
+  Fp8DynWorkspace w;
+  w.splits = mla::oproj_fp8dyn_splits(M, K, N);
+  w.x8_off = 0;
+  w.xs_off = mla::align_up((size_t)M * K, 256);
+  w.part_off = w.xs_off + mla::align_up((size_t)(K / 128) * mla::act_scale_stride(M) * 4, 256);
+  w.total = w.part_off + (w.splits > 1 ? (size_t)w.splits * M * N * 4 : 0);
+  return w;
+}
+bool fp8dyn_dims_ok(int M, int K, int N) {
+  return dims_ok(M, K, N, 1) && K % 128 == 0 && (long long)K * 256 < 0x7fffffffLL &&
+         (long long)M * K <= 0x7fffffffLL && (long long)M * N <= kMaxElems;
+}
+}  // namespace
+
+size_t mla_out_proj_fp8_dyn_workspace_bytes(int M, int K, int N) {
+  if (!fp8dyn_dims_ok(M, K, N)) return 0;
+  return fp8dyn_layout(M, K, N).total;
+}
+
+int mla_out_proj_fp8_dyn(const mla_bf16* x, const uint8_t* w8, const float* w_scale, void* y,
+                         int M, int K, int N, void* workspace, size_t workspace_bytes,
+                         uint32_t flags, void* stream) {
+  if (!x || !w8 || !w_scale || !y) return MLA_ERR_NULL;
+  if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
+  if (!fp8dyn_dims_ok(M, K, N)) return MLA_ERR_DIM;
+  const Fp8DynWorkspace ws = fp8dyn_layout(M, K, N);
+  if (!workspace || workspace_bytes < ws.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w8) || !aligned16(w_scale) || !aligned16(y) ||
+      !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  const size_t out_elt = (flags & MLA_OUT_F32) ? 4 : 2;
+  const size_t nb = (size_t)(N + 127) / 128, kb = (size_t)K / 128;
+  const Range in[] = {{x, (size_t)M * K * 2}, {w8, (size_t)N * K}, {w_scale, nb * kb * 4}};
+  const Range outs[] = {{y, (size_t)M * N * out_elt}, {workspace, ws.total}};
+  if (any_alias(in, 3, outs, 2)) return MLA_ERR_ALIAS;
+  const int dev = check_device();
+  if (dev != MLA_OK) return dev;
+
+  char* wsb = static_cast<char*>(workspace);
+  uint8_t* x8 = reinterpret_cast<uint8_t*>(wsb + ws.x8_off);
+  float* xs = reinterpret_cast<float*>(wsb + ws.xs_off);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (mla::launch_act_quant(x, x8, xs, M, K, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  mla::OprojParams p;
+  p.x = nullptr;
+  p.w = nullptr;
+  p.w8 = w8;
+  p.w_scale = w_scale;
+  p.x8 = x8;
+  p.x_scaleT = xs;
+  p.y = y;
+  p.part = ws.splits > 1 ? reinterpret_cast<float*>(wsb + ws.part_off) : nullptr;
+  p.M = M;
+  p.K = K;
+  p.N = N;
+  p.splits = ws.splits;
+  p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
+  p.group_m = 0;
+  if (mla::launch_oproj_fp8dyn(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
 }  // extern "C"

@@ -137,6 +137,11 @@ struct OprojParams {
   int group_m;        // wide kernel: m-tiles per group of the tile order
   const uint8_t* w8;      // FP8 weight [N][K] (e4m3) instead of w, or null
   const float* w_scale;   // its float32 scales, [ceil(N/128)][ceil(K/128)]
+  // FP8 activations (with w8): x8 [M][K] e4m3 codes and their scales
+  // transposed, x_scaleT [K/128][act_scale_stride(M)] (set by act_quant); x is
+  // then unused.
+  const uint8_t* x8 = nullptr;
+  const float* x_scaleT = nullptr;
   // Head-major split store (hd > 0; splits 1, bf16 weight): row m = b*T + t,
   // column n = h*hd + d goes to y [B][H][T][d0] at d < d0, else to y1
   // [B][H][T][hd-d0] at d - d0 (H = N / hd; hd and d0 multiples of 32).
@@ -146,5 +151,19 @@ struct OprojParams {
 
 int oproj_choose_splits(int M, int K, int N, bool fp8 = false);
 hipError_t launch_oproj(const OprojParams& p, hipStream_t stream);
+
+// Row stride of the transposed activation scales: M rounded up to 4 floats,
+// so every slab's row of scales starts 16-byte aligned.
+constexpr int act_scale_stride(int M) { return (M + 3) & ~3; }
+
+// FP8 activations: x [M][K] bf16 -> x8 [M][K] e4m3 and x_scaleT [K/128][stride]
+// (per row and 128-column block: scale = max(amax, 1e-4) / 448, codes
+// e4m3(x / scale) rounded to nearest even).  K % 128 == 0.
+hipError_t launch_act_quant(const uint16_t* x, uint8_t* x8, float* x_scaleT, int M, int K,
+                            hipStream_t stream);
+// y = (x8, x_scaleT) · (w8, w_scale)ᵀ with FP8 MFMA; splits > 1: float32
+// partials in p.part, then a reduction.
+int oproj_fp8dyn_splits(int M, int K, int N);
+hipError_t launch_oproj_fp8dyn(const OprojParams& p, hipStream_t stream);
 
 }  // namespace mla

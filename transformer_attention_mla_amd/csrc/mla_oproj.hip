@@ -452,6 +452,266 @@ __global__ __launch_bounds__(256) void oproj_reduce_kernel(OprojParams p) {
   }
 }
 
+// ------------------------------------------------------ FP8 activations --
+// Page "Block input", config.json quantization_config: e4m3 with the
+// activation scheme "dynamic".  One 128-column block per 16 lanes (8 values
+// per lane): block maximum by a 16-lane butterfly, scale = max(amax, 1e-4) /
+// 448 and codes e4m3(x / scale), the divisions correctly rounded float32 and
+// v_cvt_pk_fp8_f32 rounding to nearest even.  The scales are stored
+// transposed, [K/128][M], so that one slab's scales for a tile of rows are
+// contiguous (the GEMM copies them into LDS with its tiles), row stride
+// act_scale_stride(M).
+__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x,
+                                                        uint8_t* __restrict__ x8,
+                                                        float* __restrict__ sxT, int M, int K) {
+  const int KB = K / 128;
+  const long g = (long)blockIdx.x * 256 + threadIdx.x;
+  const long blk = g >> 4;  // (m, kb): the 16 lanes of a group share it
+  const int sub = (int)(g & 15);
+  if (blk >= (long)M * KB) return;
+  const int m = (int)(blk / KB), kb = (int)(blk - (long)m * KB);
+  const size_t off = (size_t)m * K + (size_t)kb * 128 + sub * 8;
+  const u32x4 raw = ld_global_16(x + off);
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = bf16lo(raw[e]);
+    v[2 * e + 1] = bf16hi(raw[e]);
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, 16));
+  a = fmaxf(a, 1e-4f);
+  const float sc = a / 448.0f;
+  u32x2 q;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    int w = 0;
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h] / sc, v[4 * h + 1] / sc, w, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h + 2] / sc, v[4 * h + 3] / sc, w, true);
+    q[h] = (uint32_t)w;
+  }
+  *reinterpret_cast<u32x2*>(x8 + off) = q;
+  if (sub == 0) sxT[(size_t)kb * act_scale_stride(M) + m] = sc;
+}
+
+// ------------------------------------------------------------ FP8 x FP8 --
+// Yᵀ = W8·X8ᵀ with v_mfma_f32_32x32x64_f8f6f4 (both operands e4m3).  A k slab
+// is 128 deep -- one 128-byte LDS row per operand row, the same copy plan as
+// the wide bf16 kernel (8 lanes fetch one whole line; chunk slots swizzled by
+// wswz) -- plus the slab's activation scales (1 KiB chunk).  Each 32x32 tile's
+// slab product (two MFMAs) goes to a float32 temporary and is added to the
+// accumulator times w_scale[block of n][slab] · x_scale[m][slab]: the two
+// block scales change with every 128-deep slab, so the sum over k is taken
+// slab by slab in float32 (the order the format implies).  A wave computes
+// WTN x WTM tiles of 32x32; the workgroup WN x WM waves; NSTG LDS stages,
+// the copies of slab kt+NSTG-1 issued once every wave has finished slab kt-1.
+// Both MFMA operands take their 32 bytes per lane of a 64-deep k step from
+// the same byte range of the row, so A and B agree on which k each operand
+// slot holds.
+template <int WN, int WM, int WTN, int WTM, int NSTG>
+__global__ __launch_bounds__(64 * WN * WM) void oproj_fp8_kernel(OprojParams p) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  constexpr int NWAVE = WN * WM;
+  constexpr int BN = WN * WTN * 32, BM = WM * WTM * 32;
+  constexpr int APART = BN * 128, BPART = BM * 128;
+  constexpr int SXOFF = APART + BPART;
+  constexpr int STG = SXOFF + 1024;         // + activation scales (BM floats, padded)
+  constexpr int NCH = STG / 1024;           // 1 KiB copies per slab
+  constexpr int CPW = (NCH + NWAVE - 1) / NWAVE;
+  static_assert(BM <= 256, "one 1 KiB chunk of activation scales per slab");
+  static_assert(WTN * 32 <= 128 && 128 % (WTN * 32) == 0, "a wave's rows lie in one 128-row weight block");
+  static_assert(NSTG * STG <= 160 * 1024, "LDS budget");
+  static_assert((NSTG - 1) * CPW < 64, "vmcnt range");
+  constexpr int NBLK = BN / 128;   // 128-row weight blocks of a tile
+  constexpr int MAXS = 256;        // slabs per split (launch checks)
+  __shared__ __attribute__((aligned(1024))) uint8_t fl[NSTG * STG];
+  __shared__ float wsl[NBLK * MAXS];  // the tile's weight scales, [block][slab]
+
+  const int M = p.M, N = p.N, K = p.K, KB = K / 128;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int ntiles = tiles_m * tiles_n;
+  // grouped tile order dealt to the XCDs as in the wide kernel
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, seq = bid >> 3;
+  const int t = xcd * (ntiles >> 3) + min(xcd, ntiles & 7) + seq;
+  const int gm = p.group_m;
+  const int group = t / (gm * tiles_n);
+  const int first_m = group * gm;
+  const int rows_m = min(gm, tiles_m - first_m);
+  const int within = t - group * gm * tiles_n;
+  const int tm = first_m + within % rows_m;
+  const int tn = within / rows_m;
+  const int n0 = tn * BN, m0 = tm * BM;
+  const int nks = KB / p.splits;  // slabs of this split
+  const int kb0 = blockIdx.y * nks;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, hf = lane >> 5;
+  const int wn = wave % WN, wm = wave / WN;
+
+  // Copy plan: chunk j < APART/1024 holds weight rows 8j..8j+7, then x rows,
+  // then the scales; lane l writes bytes 16l.. of its chunk: row 8j' + l/8,
+  // slot l%8, which holds source chunk slot ^ wswz(row).  Copy i of a wave is
+  // chunk wave + NWAVE*i, so with both operand parts a whole number of
+  // NWAVE-chunk rounds its kind (weight, x or scales) depends on i alone and
+  // is known at compile time.  Copies past the last chunk repeat the scale
+  // chunk (identical bytes).
+  static_assert((APART / 1024) % NWAVE == 0 && (BPART / 1024) % NWAVE == 0, "copy rounds");
+  auto kind_of = [](int i) { return NWAVE * i < APART / 1024 ? 0 : (NWAVE * i < SXOFF / 1024 ? 1 : 2); };
+  uint32_t voff[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int j = wave + NWAVE * i;
+    if (kind_of(i) == 0) {
+      const int row = j * 8 + (lane >> 3);
+      voff[i] = (uint32_t)row * (uint32_t)K + (uint32_t)(((lane & 7) ^ wswz(row)) * 16);
+    } else if (kind_of(i) == 1) {
+      const int row = (j - APART / 1024) * 8 + (lane >> 3);
+      voff[i] = (uint32_t)row * (uint32_t)K + (uint32_t)(((lane & 7) ^ wswz(row)) * 16);
+    } else {
+      voff[i] = (uint32_t)lane * 16u;  // scales of rows m0 + 4 lane ..
+    }
+  }
+  const size_t wbytes = (size_t)(N - n0) * K;
+  const size_t xbytes = (size_t)(M - m0) * K;
+  // scale rows copied: rounded up to 4 so that no 16-byte copy straddles the
+  // extent (the row stride of the transposed scales is M rounded up to 4)
+  const int srows = (min(BM, M - m0) + 3) & ~3;
+
+  auto issue = [&](int stage, int ks) {
+    const int kb = kb0 + ks;
+    const size_t k0 = (size_t)kb * 128;
+    // extents clamped to 31 bits: a tile's rows lie within 256 K < 2^31 bytes
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(p.w8 + (size_t)n0 * K + k0, (uint32_t)min(wbytes - k0, (size_t)0x7fffffff));
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc(p.x8 + (size_t)m0 * K + k0, (uint32_t)min(xbytes - k0, (size_t)0x7fffffff));
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(p.x_scaleT + (size_t)kb * act_scale_stride(M) + m0, (uint32_t)srows * 4u);
+    uint8_t* sb = fl + stage * STG;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int j = min(wave + NWAVE * i, NCH - 1);
+      dma16(kind_of(i) == 0 ? rw : (kind_of(i) == 1 ? rx : rs), sb + j * 1024, voff[i]);
+    }
+  };
+
+  // Fragment (32 bytes) of k step kk for LDS row `row`: chunks 4kk+2hf, +1.
+  auto frag = [&](const uint8_t* part, int row, int kk) {
+    const int sw = wswz(row);
+    const uint8_t* r = part + row * 128;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(r + (((4 * kk + 2 * hf) ^ sw) * 16));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(r + (((4 * kk + 2 * hf + 1) ^ sw) * 16));
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16 acc[WTN][WTM] = {};
+  // The tile's weight scales go to LDS before any copy is issued (a vector
+  // load inside the loop would make the compiler wait for the copies too).
+  // Rows past N use the last block, whose products are zero and never stored.
+  const int NB = (N + 127) >> 7;
+  for (int i = tid; i < NBLK * nks; i += 64 * NWAVE) {
+    const int blk = min((n0 >> 7) + i / nks, NB - 1);
+    wsl[i] = p.w_scale[(size_t)blk * KB + kb0 + i % nks];
+  }
+  const int wblk = (wn * WTN * 32) >> 7;  // this wave's rows lie in one block
+
+#pragma unroll
+  for (int s = 0; s < NSTG - 1; ++s)
+    if (s < nks) issue(s, s);
+  // Tile t = i*WTM + jm of a slab: its two MFMAs go to tq[t&1]; the scale
+  // FMAs of tile t-1 are issued while the matrix core computes tile t (one
+  // temporary would serialize every tile on the MFMA result latency).  The
+  // last tile's FMAs wait for the next slab, where they cover the latency of
+  // its first fragment reads.
+  constexpr int TL = WTN * WTM - 1;
+  f32x16 tq[2];
+  float scp = 0.f;  // scale of the last tile of the previous slab
+  for (int ks = 0; ks < nks; ++ks) {
+    // this wave's copies of slab ks are done (those of ks+1 .. ks+NSTG-2 may
+    // not be; fewer are in flight near the end); after the barrier every
+    // wave's are, and every wave has finished slab ks-1, whose stage the next
+    // copies refill
+    if (ks + NSTG - 2 < nks)
+      wait_vm<(NSTG - 2) * CPW>();
+    else
+      wait_vm<0>();
+    barrier_lds();
+    if (ks + NSTG - 1 < nks) issue((ks + NSTG - 1) % NSTG, ks + NSTG - 1);
+    const uint8_t* sb = fl + (ks % NSTG) * STG;
+    const float swv = wsl[wblk * nks + ks];  // (visible: the barrier above)
+    i32x8 bfr[WTM][2];
+    float sc[WTM];
+#pragma unroll
+    for (int jm = 0; jm < WTM; ++jm) {
+      const int row = wm * (WTM * 32) + jm * 32 + ln;
+      bfr[jm][0] = frag(sb + APART, row, 0);
+      bfr[jm][1] = frag(sb + APART, row, 1);
+      sc[jm] = swv * *reinterpret_cast<const float*>(sb + SXOFF + row * 4);
+    }
+    if (ks > 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        acc[TL / WTM][TL % WTM][r] = fmaf(tq[TL & 1][r], scp, acc[TL / WTM][TL % WTM][r]);
+    }
+#pragma unroll
+    for (int i = 0; i < WTN; ++i) {
+      const int row = wn * (WTN * 32) + i * 32 + ln;
+      const i32x8 a0 = frag(sb, row, 0), a1 = frag(sb, row, 1);
+#pragma unroll
+      for (int jm = 0; jm < WTM; ++jm) {
+        const int t = i * WTM + jm;
+        tq[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bfr[jm][0], f32x16{}, 0, 0, 0, 0, 0, 0);
+        tq[t & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bfr[jm][1], tq[t & 1], 0, 0, 0, 0, 0, 0);
+        if (t > 0) {
+          const int pi = (t - 1) / WTM, pj = (t - 1) % WTM;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[pi][pj][r] = fmaf(tq[(t - 1) & 1][r], sc[pj], acc[pi][pj][r]);
+        }
+      }
+    }
+    scp = sc[TL % WTM];
+  }
+  if (nks > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      acc[TL / WTM][TL % WTM][r] = fmaf(tq[TL & 1][r], scp, acc[TL / WTM][TL % WTM][r]);
+  }
+
+#pragma unroll
+  for (int jm = 0; jm < WTM; ++jm) {
+    const int m = m0 + wm * (WTM * 32) + jm * 32 + ln;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < WTN; ++i)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int n = n0 + wn * (WTN * 32) + i * 32 + gq * 8 + hf * 4;
+        const float v0 = acc[i][jm][gq * 4 + 0], v1 = acc[i][jm][gq * 4 + 1];
+        const float v2 = acc[i][jm][gq * 4 + 2], v3 = acc[i][jm][gq * 4 + 3];
+        if (p.splits > 1) {
+          float* dst = p.part + ((size_t)blockIdx.y * M + m) * N + n;
+          if (n + 3 < N && (N & 3) == 0) {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
+          } else {
+            if (n < N) dst[0] = v0;
+            if (n + 1 < N) dst[1] = v1;
+            if (n + 2 < N) dst[2] = v2;
+            if (n + 3 < N) dst[3] = v3;
+          }
+        } else {
+          store_y4(p, m, n, v0, v1, v2, v3);
+        }
+      }
+  }
+}
+
 }  // namespace
 
 // The wide kernel needs enough 256 x 256 tiles to fill the chip, and 32-bit
@@ -513,6 +773,62 @@ hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
     hipLaunchKernelGGL((oproj_kernel<false, 64, OBK>), grid, dim3(ONT), 0, stream, p);
   else
     hipLaunchKernelGGL((oproj_kernel<false, OBM, OBK>), grid, dim3(ONT), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  const size_t total = (size_t)p.M * p.N;
+  size_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(oproj_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_quant(const uint16_t* x, uint8_t* x8, float* x_scaleT, int M, int K,
+                            hipStream_t stream) {
+  const long threads = (long)M * (K / 128) * 16;
+  const long blocks = (threads + 255) / 256;
+  if (K % 128 != 0 || blocks <= 0 || blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, x8, x_scaleT,
+                     M, K);
+  return hipGetLastError();
+}
+
+// Large M: 256 x 256 tiles, 8 waves of 4 x 2 tiles, two stages.  Small M
+// (M <= 64): 256 (n) x 64 (m) tiles, 8 waves of 2 x 1 tiles, three stages,
+// K split so that the weight stream spreads over the compute units.
+static bool fp8dyn_small(int M) { return M <= 64; }
+
+int oproj_fp8dyn_splits(int M, int K, int N) {
+  if (!fp8dyn_small(M)) return 1;
+  const int tiles = (N + 255) / 256;
+  const int slabs = K / 128;
+  int best = 1;
+  for (int s = 2; s <= slabs / 2; ++s) {
+    if (slabs % s) continue;
+    best = s;
+    if (tiles * s >= 256) break;
+  }
+  return best;
+}
+
+hipError_t launch_oproj_fp8dyn(const OprojParams& p_in, hipStream_t stream) {
+  OprojParams p = p_in;
+  if (!p.w8 || !p.w_scale || !p.x8 || !p.x_scaleT || p.K % 128 != 0 || p.splits < 1 ||
+      (p.K / 128) % p.splits != 0 || p.hd > 0)
+    return hipErrorInvalidConfiguration;
+  if ((long long)p.K * 256 >= 0x7fffffffLL || p.K / 128 / p.splits > 256)
+    return hipErrorInvalidConfiguration;
+  p.group_m = p.group_m > 0 ? p.group_m : WGROUP_M;
+  if (fp8dyn_small(p.M)) {
+    const long tiles = (p.N + 255) / 256;
+    p.group_m = 1;
+    hipLaunchKernelGGL((oproj_fp8_kernel<4, 2, 2, 1, 3>), dim3((unsigned)tiles, (unsigned)p.splits),
+                       dim3(512), 0, stream, p);
+  } else {
+    const long tiles = (long)((p.M + 255) / 256) * ((p.N + 255) / 256);
+    if (tiles > 0x7fffffffL || p.splits != 1) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((oproj_fp8_kernel<2, 4, 4, 2, 2>), dim3((unsigned)tiles, 1), dim3(512), 0,
+                       stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const size_t total = (size_t)p.M * p.N;
