@@ -37,7 +37,8 @@ def oracle_full(d):
 
 
 SHAPES = [(1, 1, 1), (1, 3, 17), (2, 3, 63), (1, 2, 64), (1, 3, 65), (1, 2, 129), (3, 1, 100),
-          (1, 5, 200), (1, 64, 64), (2, 4, 1000), (1, 2, 96), (1, 3, 300)]
+          (1, 5, 200), (1, 64, 64), (2, 4, 1000), (1, 2, 96), (1, 3, 300), (1, 3, 1280),
+          (1, 1, 513)]
 
 
 @pytest.mark.parametrize("B,H,T", SHAPES)
@@ -84,7 +85,7 @@ def test_prefill_workload2_full(gpu_device):
     check_close(to_host64(lse), want_lse, TOL, "lse vs oracle")
 
 
-@pytest.mark.parametrize("B,H,T", [(1, 2, 1), (2, 3, 129), (1, 4, 1000)])
+@pytest.mark.parametrize("B,H,T", [(1, 2, 1), (2, 3, 129), (1, 4, 1000), (1, 64, 1024), (1, 1, 1537)])
 def test_prefill_weights_sum_to_one(B, H, T, gpu_device):
     say(f"prefill V=1 probe B={B} H={H} T={T}")
     d = inputs.prefill_inputs(B, H, T, workload=0)
@@ -95,7 +96,8 @@ def test_prefill_weights_sum_to_one(B, H, T, gpu_device):
     assert err <= SUM_TOL
 
 
-@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 3, 65), (2, 2, 257), (1, 2, 2000)])
+@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 3, 65), (2, 2, 257), (1, 2, 2000), (1, 64, 1024),
+                                   (1, 1, 1537)])
 def test_prefill_count_probe(B, H, T, gpu_device):
     """Zero queries: every visible key has weight exp(0) = 1, so exp(lse)
     must round to t + 1 (bit-exact integer check of mask and tiles)."""
