@@ -35,15 +35,23 @@ CSRC = os.path.join(REPO, "transformer_attention_mla_amd", "csrc")
 # bytes written).  Each figure holds only for the kernel source it was taken on,
 # identified by a hash of its files; after any change the figure is dropped.
 MEASURED_TRAFFIC = {
-    "prefill_kernel": ("ce684b201e3d1a48", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
-                       2068174280, "profiles/prefill_kernel_B4_T4096_H64.txt"),
-    "decode_split_kernel": ("ef9b64db157bd59b", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                            21477507924, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
-    "decode_split_kernel_shared_kpe": ("ef9b64db157bd59b", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                                       17375802638, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
-    "latent_decode_kernel": ("6fceba74ac8b333a", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
-                             657376163, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
+    "prefill_kernel": ("40553ca475cd9844", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
+                       2081852258, "profiles/prefill_kernel_B4_T4096_H64.txt"),
+    "decode_split_kernel": ("270db33e8e45b51e", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                            21477788176, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
+    "decode_split_kernel_shared_kpe": ("270db33e8e45b51e", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                                       17371191268, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
+    "latent_decode_kernel": ("6bc7a642abae5265", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
+                             657384521, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
 }
+# o_proj GEMM kernels at K = 8192, N = 7168 (the split-K reduce kernel, shared
+# by several paths, is left out), M = 16384 and M = 64.
+_OPROJ_SRC = ("6d47f5f393de3e78", ("mla_oproj.hip", "mla_device.h", "mla_internal.h"))
+_OPROJ_PROFILE = "profiles/oproj_kernel_M16384_K8192_N7168_and_M64.txt"
+for _k, _v in {"oproj_bf16_M16384": 3204137041, "oproj_bf16_M64": 140663198,
+               "oproj_fp8_M16384": 5636981161, "oproj_fp8_M64": 81975078,
+               "oproj_fp8_dyn_M16384": 1734009489 + 411088325, "oproj_fp8_dyn_M64": 92915921 + 1655882}.items():
+    MEASURED_TRAFFIC[_k] = _OPROJ_SRC + (_v, _OPROJ_PROFILE)
 
 
 def measured_traffic(kernel):
@@ -80,16 +88,23 @@ class Timer:
     warm: back-to-back calls (inputs and weights may sit in the 256 MB MALL and
     the L2s).  cold: before each timed call, outside the event pair, a 512 MB
     scratch buffer is written, which evicts the MALL and the L2s, so the call
-    reads its inputs and weights from HBM."""
+    reads its inputs and weights from HBM -- and also leaves the caches full of
+    dirty lines, whose write-back the call's reads then pay for.  cold_clean:
+    the same write, then a read of a second 512 MB buffer (a sum), so the
+    caches hold neither the call's inputs nor dirty lines."""
 
     def __init__(self, torch, dev):
         self.torch = torch
         self.scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        self.clean = torch.ones(64 << 20, dtype=torch.float64, device=dev)  # 512 MB
+        self.sink = torch.empty((), dtype=torch.float64, device=dev)
 
-    def flush(self):
+    def flush(self, clean=False):
         self.scratch.fill_(1)
+        if clean:
+            self.torch.sum(self.clean, 0, out=self.sink)
 
-    def median(self, fn, calls, cold=False, untimed=3):
+    def median(self, fn, calls, cold=False, untimed=3, clean=False):
         torch = self.torch
         for _ in range(untimed):
             fn()
@@ -97,7 +112,7 @@ class Timer:
               for _ in range(calls)]
         for a, b in ev:
             if cold:
-                self.flush()
+                self.flush(clean)
             a.record()
             fn()
             b.record()
@@ -106,7 +121,9 @@ class Timer:
         return t[len(t) // 2]
 
     def both(self, fn, calls):
-        return {"cold": self.median(fn, calls, cold=True), "warm": self.median(fn, calls)}
+        return {"cold": self.median(fn, calls, cold=True),
+                "cold_clean": self.median(fn, calls, cold=True, clean=True),
+                "warm": self.median(fn, calls)}
 
 
 def cpu_model():
@@ -240,11 +257,12 @@ def other_configs(mla, inputs, w_o, scale, dev, timer):
         fl_a, fl_o = prefill_flops(B, H, T), oproj_flops(M, K_O, N_O)
         ob = oproj_bytes(M, K_O, N_O)
         out[f"prefill_B{B}_T{T}_H{H}"] = {
-            "attention_ms": ta["cold"], "attention_ms_warm": ta["warm"],
+            "attention_ms": ta["cold"], "attention_ms_cold_clean": ta["cold_clean"],
+            "attention_ms_warm": ta["warm"],
             "attention_tflops": fl_a / ta["cold"] / 1e9,
             "attention_tflops_warm": fl_a / ta["warm"] / 1e9,
             "attention_frac_peak": fl_a / ta["cold"] / 1e9 / PEAK_BF16_TFLOPS,
-            "oproj_ms_cold": to["cold"], "oproj_ms_warm": to["warm"],
+            "oproj_ms_cold": to["cold"], "oproj_ms_cold_clean": to["cold_clean"], "oproj_ms_warm": to["warm"],
             "oproj_tflops_cold": fl_o / to["cold"] / 1e9, "oproj_tflops_warm": fl_o / to["warm"] / 1e9,
             "oproj_gbps_cold": ob / to["cold"] / 1e6, "oproj_gbps_warm": ob / to["warm"] / 1e6,
             "calls": calls, "rope": wl["rope"]}
@@ -281,7 +299,7 @@ def other_configs(mla, inputs, w_o, scale, dev, timer):
     fl = 2.0 * B * T * (1536 * H * 192 + 512 * H * 256)
     nbytes = 2 * (B * T * (1536 + 512) + H * 192 * 1536 + H * 256 * 512 + B * H * T * (128 + 64 + 128 + 128))
     out[f"up_project_B{B}_T{T}_H{H}"] = {
-        "ms_cold": tup["cold"], "ms_warm": tup["warm"], "tflops_cold": fl / tup["cold"] / 1e9,
+        "ms_cold": tup["cold"], "ms_cold_clean": tup["cold_clean"], "ms_warm": tup["warm"], "tflops_cold": fl / tup["cold"] / 1e9,
         "tflops_warm": fl / tup["warm"] / 1e9, "frac_peak_cold": fl / tup["cold"] / 1e9 / PEAK_BF16_TFLOPS,
         "hbm_gbps_cold": nbytes / tup["cold"] / 1e6, "per_call": f"{fl:.4e} flops, {nbytes} bytes"}
     del d, outs
@@ -395,10 +413,11 @@ def oproj_figures(mla, inputs, w_o, dev, timer, calls=20):
                          device=dev)
         t = timer.both(lambda: mla.mla_out_proj(x, w_o, y=y, workspace=ws), calls)
         nb = oproj_bytes(M, K, N)
-        res[f"M{M}"] = {"ms_cold": t["cold"], "ms_warm": t["warm"],
+        res[f"M{M}"] = {"ms_cold": t["cold"], "ms_cold_clean": t["cold_clean"], "ms_warm": t["warm"],
                         "gbps_cold": nb / t["cold"] / 1e6, "gbps_warm": nb / t["warm"] / 1e6,
                         "tflops_cold": oproj_flops(M, K, N) / t["cold"] / 1e9,
-                        "tflops_warm": oproj_flops(M, K, N) / t["warm"] / 1e9, "bytes": nb}
+                        "tflops_warm": oproj_flops(M, K, N) / t["warm"] / 1e9, "bytes": nb,
+                        "traffic": measured_traffic(f"oproj_bf16_M{M}") if N == 7168 and K == 8192 else None}
         del x, y, ws
     torch.cuda.empty_cache()
     return res
@@ -423,10 +442,11 @@ def oproj_fp8_figures(mla, inputs, dev, timer, calls=20):
         f = lambda: mla.mla_out_proj_fp8(x, w8, sc, y=y, workspace=ws)
         t = timer.both(f, calls)
         nb = M * K * 2 + N * K + sc.numel() * 4 + M * N * 2
-        res[f"M{M}"] = {"ms_cold": t["cold"], "ms_warm": t["warm"],
+        res[f"M{M}"] = {"ms_cold": t["cold"], "ms_cold_clean": t["cold_clean"], "ms_warm": t["warm"],
                         "gbps_cold": nb / t["cold"] / 1e6, "gbps_warm": nb / t["warm"] / 1e6,
                         "tflops_cold": oproj_flops(M, K, N) / t["cold"] / 1e9,
-                        "tflops_warm": oproj_flops(M, K, N) / t["warm"] / 1e9, "bytes": nb}
+                        "tflops_warm": oproj_flops(M, K, N) / t["warm"] / 1e9, "bytes": nb,
+                        "traffic": measured_traffic(f"oproj_fp8_M{M}")}
         del x, y, ws
     del w8, sc
     torch.cuda.empty_cache()
@@ -454,10 +474,13 @@ def oproj_fp8_dyn_figures(mla, inputs, dev, timer, calls=20):
         f = lambda: mla.mla_out_proj_fp8_dyn(x, w8, sc, y=y, workspace=ws)
         t = timer.both(f, calls)
         nb = M * K * 2 + N * K + sc.numel() * 4 + M * N * 2
-        res[f"M{M}"] = {"ms_cold": t["cold"], "ms_warm": t["warm"],
+        res[f"M{M}"] = {"ms_cold": t["cold"], "ms_cold_clean": t["cold_clean"], "ms_warm": t["warm"],
                         "gbps_cold": nb / t["cold"] / 1e6, "gbps_warm": nb / t["warm"] / 1e6,
                         "tflops_cold": oproj_flops(M, K, N) / t["cold"] / 1e9,
-                        "tflops_warm": oproj_flops(M, K, N) / t["warm"] / 1e9, "bytes": nb}
+                        "tflops_warm": oproj_flops(M, K, N) / t["warm"] / 1e9, "bytes": nb,
+                        "traffic": measured_traffic(f"oproj_fp8_dyn_M{M}"),
+                        "traffic_note": "quantization kernel + GEMM kernel per call (the split-K "
+                                        "reduce at M = 64 not included)"}
         del x, y, ws
     del w8, sc
     torch.cuda.empty_cache()
