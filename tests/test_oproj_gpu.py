@@ -248,6 +248,38 @@ def test_act_quant_bit_exact(M, K, gpu_device):
     assert np.array_equal(q.cpu().numpy(), want_q), "codes differ"
 
 
+def test_act_quant_rounding_midpoints(gpu_device):
+    """Blocks whose quotient x / scale lands exactly on e4m3 rounding midpoints
+    (ties go to the even code) or one float32 step beside them, with scales
+    whose reciprocal is inexact (block maxima 3*448, 5*448, 7*448 * 2^k): the
+    codes must still equal those of the correctly rounded division."""
+    import itertools
+    say("act_quant midpoints")
+    mids = []
+    for e in range(-9, 9):  # normal and subnormal e4m3 midpoints below 448
+        for m in range(16):
+            val = (16 + m + 0.5) * 2.0 ** (e - 4) if e >= -6 else (m + 0.5) * 2.0 ** -9
+            if val < 448:
+                mids.append(val)
+    rows = []
+    for f, k in itertools.product((3.0, 5.0, 7.0), (-3, 0, 2)):
+        sc = f * 2.0 ** k
+        amax = 448.0 * sc
+        for chunk in range(0, len(mids), 127):
+            vals = [amax] + [sgn * mq * sc for mq, sgn in zip(mids[chunk:chunk + 127],
+                                                               itertools.cycle((1.0, -1.0)))]
+            vals += [0.0] * (128 - len(vals))
+            rows.append(vals)
+    x = torch.tensor(rows, dtype=torch.float32).to(torch.bfloat16)
+    # keep only blocks whose maximum survived bf16 rounding exactly
+    x = x[x.float().abs().amax(1) == torch.tensor([r[0] for r in rows])]
+    want_q, want_s = oracle.act_quant(bits(x))
+    q, sT = mla.mla_act_quant(x.to(gpu_device))
+    torch.cuda.synchronize()
+    assert np.array_equal(sT.cpu().numpy()[:, :x.shape[0]].T.view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), want_q), "codes differ next to rounding midpoints"
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 128, 1), (17, 256, 100), (64, 8192, 7168), (130, 1024, 300),
                                    (300, 384, 129), (1000, 512, 1000), (1, 512, 129), (40, 2048, 1000),
                                    (64, 1024, 7168), (33, 1024, 500), (64, 2048, 225), (16, 4096, 447),
