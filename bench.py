@@ -46,11 +46,11 @@ MEASURED_TRAFFIC = {
 }
 # o_proj GEMM kernels at K = 8192, N = 7168 (the split-K reduce kernel, shared
 # by several paths, is left out), M = 16384 and M = 64.
-_OPROJ_SRC = ("6d47f5f393de3e78", ("mla_oproj.hip", "mla_device.h", "mla_internal.h"))
+_OPROJ_SRC = ("de39e05a992f0e75", ("mla_oproj.hip", "mla_device.h", "mla_internal.h"))
 _OPROJ_PROFILE = "profiles/oproj_kernel_M16384_K8192_N7168_and_M64.txt"
-for _k, _v in {"oproj_bf16_M16384": 3204137041, "oproj_bf16_M64": 140663198,
-               "oproj_fp8_M16384": 5636981161, "oproj_fp8_M64": 81975078,
-               "oproj_fp8_dyn_M16384": 1734009489 + 411088325, "oproj_fp8_dyn_M64": 92915921 + 1655882}.items():
+for _k, _v in {"oproj_bf16_M16384": 3214556055, "oproj_bf16_M64": 140651610,
+               "oproj_fp8_M16384": 5539089235, "oproj_fp8_M64": 81975202,
+               "oproj_fp8_dyn_M16384": 1733771394 + 411087907, "oproj_fp8_dyn_M64": 70562862 + 1655850}.items():
     MEASURED_TRAFFIC[_k] = _OPROJ_SRC + (_v, _OPROJ_PROFILE)
 
 

@@ -286,7 +286,7 @@ def test_act_quant_rounding_midpoints(gpu_device):
                                    (64, 16384, 300), (40, 384, 200), (3, 640, 129), (513, 768, 600)])
 def test_oproj_fp8_dyn_parity(M, K, N, gpu_device):
     """FP8 activations and weights on the FP8 matrix cores against the
-    oracle's product of the dequantized operands: M <= 64 takes the 256 x 64
+    oracle's product of the dequantized operands: M <= 64 takes the 128 x 64
     tile with K split over workgroups, larger M the 256 x 256 tile (ragged
     against both, N not a multiple of 4)."""
     say(f"o_proj fp8 dynamic parity M={M} K={K} N={N}")
