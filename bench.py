@@ -427,8 +427,9 @@ def oproj_figures(mla, inputs, w_o, dev, timer, calls=20):
 
 def oproj_fp8_figures(mla, inputs, dev, timer, calls=20):
     """o_proj with the FP8 checkpoint weight ([7168, 8192] e4m3 + float32 block
-    scales, dequantized to bf16 as it is loaded), at M = 64 (decode) and M =
-    16384 (prefill): median time cold and warm, GB/s on x + w8 + scales + y,
+    scales; at M = 64 (decode) dequantized to bf16 as it is loaded, at M =
+    16384 (prefill) dequantized once per call into the workspace before the
+    bf16 product): median time cold and warm, GB/s on x + w8 + scales + y,
     TFLOP/s."""
     import torch
 

@@ -289,7 +289,13 @@ int mla_out_proj(const mla_bf16 *x, const mla_bf16 *w_o, void *y, int M, int K, 
  *   w8       [N, K]                       uint8  e4m3 (OCP "fn": bias 7, no
  *                                                infinities, 0x7f/0xff NaN)
  *   w_scale  [ceil(N/128), K/128]         float  block scales, row-major
- *   workspace >= mla_out_proj_fp8_workspace_bytes(M, K, N) bytes
+ *   workspace >= mla_out_proj_fp8_workspace_bytes(M, K, N) bytes.  At
+ *            decode sizes it holds the float32 partials of split K; when
+ *            y spans at least 256 tiles of 256 x 256 (M = 16384, N = 7168
+ *            among them) it holds the whole dequantized weight, N*K*2
+ *            bytes: the weight is converted once per call and the product
+ *            then runs as mla_out_proj's, with identical results.  The
+ *            workspace must not overlap x, w8, w_scale or y.
  *   (x, y, M, K, N, flags, stream and the errors as for mla_out_proj; w8 or
  *   w_scale NULL is MLA_ERR_NULL, misaligned MLA_ERR_ALIGN)
  */

@@ -260,8 +260,10 @@ def oproj8(**kw):
     (dict(flags=8), FLAGS),
     (dict(M=0), DIM), (dict(K=100), DIM),
     (dict(M=64), WORKSPACE),
-    (dict(s=ctypes.c_void_p(3 * 16 * GB + 4)), ALIGN),
-    (dict(y=ctypes.c_void_p(3 * 16 * GB + 16)), ALIAS),  # y over the scales
+    (dict(M=1000, s=ctypes.c_void_p(3 * 16 * GB + 4)), ALIGN),
+    (dict(M=1000, y=ctypes.c_void_p(3 * 16 * GB + 16)), ALIAS),  # y over the scales
+    (dict(ws=A[4], ws_bytes=7168 * 8192 * 2 - 1), WORKSPACE),  # wide: room for the bf16 weight
+    (dict(ws=ctypes.c_void_p(1 * 16 * GB + 64), ws_bytes=1 << 30), ALIAS),  # workspace over w8
 ])
 def test_oproj_fp8_rejects(kw, code):
     assert oproj8(**kw) == code
@@ -269,7 +271,9 @@ def test_oproj_fp8_rejects(kw, code):
 
 def test_oproj_fp8_workspace():
     assert mla.mla_out_proj_fp8_workspace_bytes(64, 8192, 7168) > 0      # split K
-    assert mla.mla_out_proj_fp8_workspace_bytes(16384, 8192, 7168) == 0  # enough tiles
+    # enough 256 x 256 tiles: the bf16 weight is formed once in the workspace
+    assert mla.mla_out_proj_fp8_workspace_bytes(16384, 8192, 7168) == 7168 * 8192 * 2
+    assert mla.mla_out_proj_fp8_workspace_bytes(1000, 8192, 7168) == 0  # small-tile kernel, no split
     assert mla.mla_out_proj_fp8_workspace_bytes(64, 100, 7168) == 0
 
 

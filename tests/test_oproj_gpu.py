@@ -211,6 +211,22 @@ def test_oproj_fp8_dequant_exact(M, gpu_device):
     assert torch.equal(y2.cpu(), want)
 
 
+@pytest.mark.parametrize("M,K,N", [(4352, 1024, 4096), (4100, 512, 4000)])
+def test_oproj_fp8_wide_equals_bf16_on_dequantized_weight(M, K, N, gpu_device):
+    """Enough 256 x 256 tiles: the FP8 weight is dequantized once (value x
+    block scale in float32, rounded to bf16) and the wide bf16 kernel runs, so
+    the output must equal the bf16 projection with the oracle's dequantized
+    weight bit for bit (ragged N against the tile and against 128 included)."""
+    say(f"o_proj fp8 wide vs bf16 on the dequantized weight M={M} K={K} N={N}")
+    x = inputs.normal_bf16((M, K), 31, device=gpu_device)
+    w8, sc = inputs.out_proj_weight_fp8(N, K, workload=1)
+    wd = torch.from_numpy(oracle.dequant_fp8(w8.numpy(), sc.numpy()).view(np.int16)).view(torch.bfloat16)
+    y8 = mla.mla_out_proj_fp8(x, w8.to(gpu_device), sc.to(gpu_device), out_f32=True)
+    yb = mla.mla_out_proj(x, wd.to(gpu_device), out_f32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y8, yb)
+
+
 def test_oproj_fp8_large_sampled(gpu_device):
     """M = 16384, K = 8192, N = 7168 (the prefill projection) on sampled rows."""
     M, K, N = 16384, 8192, 7168

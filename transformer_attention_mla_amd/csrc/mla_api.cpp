@@ -603,6 +603,7 @@ int mla_up_project(const mla_bf16* q_lat, const mla_bf16* ckv, const mla_bf16* w
 
 size_t mla_out_proj_fp8_workspace_bytes(int M, int K, int N) {
   if (!dims_ok(M, K, N, 1) || K % 128 != 0) return 0;
+  if (mla::oproj_fp8_wide(M, K, N)) return mla::align_up((size_t)N * K * 2, 256);
   return oproj_ws_bytes(M, N, mla::oproj_choose_splits(M, K, N, true));
 }
 
@@ -612,8 +613,9 @@ int mla_out_proj_fp8(const mla_bf16* x, const uint8_t* w8, const float* w_scale,
   if (!x || !w8 || !w_scale || !y) return MLA_ERR_NULL;
   if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
   if (!dims_ok(M, K, N, 1) || K % 128 != 0 || (long long)M * N > kMaxElems) return MLA_ERR_DIM;
-  const int splits = mla::oproj_choose_splits(M, K, N, true);
-  const size_t need = oproj_ws_bytes(M, N, splits);
+  const bool wide = mla::oproj_fp8_wide(M, K, N);
+  const int splits = wide ? 1 : mla::oproj_choose_splits(M, K, N, true);
+  const size_t need = wide ? mla::align_up((size_t)N * K * 2, 256) : oproj_ws_bytes(M, N, splits);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(w8) || !aligned16(w_scale) || !aligned16(y) ||
       !aligned16(workspace))
@@ -626,21 +628,31 @@ int mla_out_proj_fp8(const mla_bf16* x, const uint8_t* w8, const float* w_scale,
   const int dev = check_device();
   if (dev != MLA_OK) return dev;
 
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
   mla::OprojParams p;
   p.x = x;
   p.w = nullptr;
   p.w8 = w8;
   p.w_scale = w_scale;
   p.y = y;
-  p.part = static_cast<float*>(need ? workspace : nullptr);
+  p.part = static_cast<float*>(need && !wide ? workspace : nullptr);
+  if (wide) {
+    // the bf16 weight the small-tile kernel would form in its load path,
+    // formed once, then the wide bf16 kernel
+    uint16_t* wbf = static_cast<uint16_t*>(workspace);
+    if (mla::launch_dequant_fp8(w8, w_scale, wbf, N, K, s) != hipSuccess) return MLA_ERR_LAUNCH;
+    p.w = wbf;
+    p.w8 = nullptr;
+    p.w_scale = nullptr;
+  }
   p.M = M;
   p.K = K;
   p.N = N;
   p.splits = splits;
   p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
   p.group_m = 0;
-  (void)hipGetLastError();
-  if (mla::launch_oproj(p, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_LAUNCH;
+  if (mla::launch_oproj(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
   return MLA_OK;
 }
 

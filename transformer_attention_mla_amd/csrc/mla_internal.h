@@ -150,6 +150,11 @@ struct OprojParams {
 };
 
 int oproj_choose_splits(int M, int K, int N, bool fp8 = false);
+// FP8 weight at large M: dequantize it once (bf16 [N][K] into the workspace)
+// and run the wide bf16 kernel when this holds.
+bool oproj_fp8_wide(int M, int K, int N);
+hipError_t launch_dequant_fp8(const uint8_t* w8, const float* w_scale, uint16_t* w, int N, int K,
+                              hipStream_t stream);
 hipError_t launch_oproj(const OprojParams& p, hipStream_t stream);
 
 // Row stride of the transposed activation scales: M rounded up to 4 floats,

@@ -452,6 +452,21 @@ __global__ __launch_bounds__(256) void oproj_reduce_kernel(OprojParams p) {
   }
 }
 
+// FP8 weight -> bf16 weight (the same arithmetic as dequant8 in the load
+// path of the small-tile kernel), 8 values per thread: used at large M, where
+// the weight is dequantized once into the workspace and the wide bf16 kernel
+// (which copies raw bytes into LDS and cannot dequantize) does the product.
+__global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint8_t* __restrict__ w8,
+                                                          const float* __restrict__ w_scale,
+                                                          uint16_t* __restrict__ w, int N, int K) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;  // 8-value group
+  if (i >= (long)N * K / 8) return;
+  const long e = i * 8;
+  const int n = (int)(e / K), k = (int)(e - (long)n * K);
+  const float sc = w_scale[(size_t)(n >> 7) * ((K + 127) / 128) + (k >> 7)];
+  *reinterpret_cast<u32x4*>(w + e) = dequant8(ld_global_8(w8 + e), sc);
+}
+
 // ------------------------------------------------------ FP8 activations --
 // Page "Block input", config.json quantization_config: e4m3 with the
 // activation scheme "dynamic".  One 128-column block per 16 lanes (8 values
@@ -779,6 +794,18 @@ hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
   size_t blocks = (total + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(oproj_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+bool oproj_fp8_wide(int M, int K, int N) { return oproj_use_wide(M, K, N) && K % 8 == 0; }
+
+hipError_t launch_dequant_fp8(const uint8_t* w8, const float* w_scale, uint16_t* w, int N, int K,
+                              hipStream_t stream) {
+  const long groups = (long)N * K / 8;
+  const long blocks = (groups + 255) / 256;
+  if (K % 8 != 0 || blocks <= 0 || blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(dequant_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w8, w_scale, w,
+                     N, K);
   return hipGetLastError();
 }
 
