@@ -18,6 +18,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -80,6 +81,25 @@ def measured_copy_gbps(torch, dev, reps=5):
         best = min(best, e0.elapsed_time(e1))
     del src, dst
     return 2.0 * (1 << 30) / (best * 1e-3) / 1e9
+
+
+def measured_mfma_tflops(mla, torch, dev, kind=0, reps=5):
+    """Matrix-core rate this GPU sustains with every compute unit busy (the
+    library's probe: MFMA chains on register operands, no memory traffic;
+    kind 0 bf16, kind 1 e4m3), median of a few launches of about 5 ms each."""
+    iters = 32768 if kind == 0 else 16384
+    out = torch.empty(mla.MLA_MFMA_PROBE_OUT, dtype=torch.float32, device=dev)
+    mla.mla_mfma_probe(iters, kind, out=out)
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mla.mla_mfma_probe(iters, kind, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del out
+    return mla.mla_mfma_probe_flops(iters, kind) / (statistics.median(times) * 1e-3) / 1e12
 
 
 class Timer:
@@ -614,11 +634,16 @@ def main():
             "oproj_ms": avg["prefill_oproj"], "oproj_tflops": fo / to / 1e12,
             "oproj_frac_peak": fo / to / 1e12 / PEAK_BF16_TFLOPS,
             "attention_plus_oproj_tflops": (fa + fo) / (ta + to) / 1e12}
+        mfma_tf = measured_mfma_tflops(mla, torch, dev, kind=0)
+        res["measured_mfma_tflops"] = {"bf16": mfma_tf, "fp8_e4m3": measured_mfma_tflops(mla, torch, dev, kind=1)}
+        res["prefill"]["exp_count"] = B * H * T * (T + 1) // 2
         res["roofline"] = {"bound": "mfma", "achieved": fa / ta / 1e12, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": fa / ta / 1e12 / PEAK_BF16_TFLOPS,
                            "traffic": measured_traffic("prefill_kernel"),
                            "kernel": "prefill_kernel (+ rope_prep_kernel)",
-                           "per_launch": f"{fa:.4e} causal flops"}
+                           "per_launch": f"{fa:.4e} causal flops",
+                           "measured_mfma_tflops": mfma_tf,
+                           "frac_of_measured_mfma": fa / ta / 1e12 / mfma_tf}
         parts.append(f"prefill B={B} T={T} H={H} causal + o_proj [{B * T}x{K_O}]x[{K_O}x{N_O}]")
         cfg.update({"prefill_batch": B, "prefill_seq_len": T})
     if do_d:

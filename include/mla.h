@@ -376,6 +376,29 @@ int mla_up_project(const mla_bf16 *q_lat, const mla_bf16 *ckv, const mla_bf16 *w
                    const mla_bf16 *w_kv_b, int B, int T, int H, void *q_nope, void *q_pe,
                    void *k_nope, void *v, uint32_t flags, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement helper (not a step of the attention path): the rate the matrix
+ * cores of this GPU sustain with every compute unit busy, clock and power
+ * limits included -- the measured figures beside which the published peaks
+ * and the kernels' rates are read.  One launch of 512 workgroups of 4 waves
+ * (two waves per SIMD), each wave running `iters` rounds of four independent
+ * MFMA chains on register operands, with no memory traffic in the loop:
+ * kind 0 v_mfma_f32_32x32x16_bf16 (the attention and bf16 GEMM products),
+ * kind 1 v_mfma_f32_32x32x64_f8f6f4 on e4m3 operands (the FP8 o_proj).  It
+ * performs mla_mfma_probe_flops(iters, kind) floating-point operations (0
+ * when iters or kind is out of range).
+ *
+ *   out    device, float32, MLA_MFMA_PROBE_OUT elements, 16-byte aligned,
+ *          caller-owned; receives per-thread sums of the products
+ *   iters  1 .. 2^24, kind 0 or 1 (else MLA_ERR_DIM)
+ *
+ * Errors: out NULL MLA_ERR_NULL, misaligned MLA_ERR_ALIGN, not gfx950
+ * MLA_ERR_DEVICE.  Asynchronous on `stream`; time it with events on it.
+ */
+#define MLA_MFMA_PROBE_OUT (512 * 256)
+double mla_mfma_probe_flops(int iters, int kind);
+int mla_mfma_probe(float *out, int iters, int kind, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

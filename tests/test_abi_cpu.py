@@ -34,6 +34,22 @@ def test_header_symbols_exported():
         assert hasattr(lib, n), n
 
 
+def test_mfma_probe_rejects_and_counts():
+    L = mla.lib()
+    assert mla.mla_mfma_probe_flops(1, 0) == 512 * 4 * 4 * 2 * 32 * 32 * 16
+    assert mla.mla_mfma_probe_flops(1, 1) == 512 * 4 * 4 * 2 * 32 * 32 * 64
+    assert mla.mla_mfma_probe_flops(1000, 0) == 1000 * mla.mla_mfma_probe_flops(1, 0)
+    assert mla.mla_mfma_probe_flops(0, 0) == 0.0
+    assert mla.mla_mfma_probe_flops((1 << 24) + 1, 0) == 0.0
+    assert mla.mla_mfma_probe_flops(1, 2) == 0.0
+    assert L.mla_mfma_probe(None, 10, 0, None) == NULL
+    assert L.mla_mfma_probe(A[0], 0, 0, None) == DIM
+    assert L.mla_mfma_probe(A[0], (1 << 24) + 1, 0, None) == DIM
+    assert L.mla_mfma_probe(A[0], 10, -1, None) == DIM
+    assert L.mla_mfma_probe(A[0], 10, 2, None) == DIM
+    assert L.mla_mfma_probe(ctypes.c_void_p(16 * GB + 4), 10, 0, None) == ALIGN
+
+
 def test_version_and_strings():
     assert mla.mla_abi_version() == 1
     for code in range(10):

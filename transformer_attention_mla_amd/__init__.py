@@ -98,6 +98,10 @@ def lib():
     L.mla_out_proj_fp8_dyn.restype = I
     L.mla_up_project.argtypes = [P, P, P, P, I, I, I, P, P, P, P, U, P]
     L.mla_up_project.restype = I
+    L.mla_mfma_probe_flops.argtypes = [I, I]
+    L.mla_mfma_probe_flops.restype = ctypes.c_double
+    L.mla_mfma_probe.argtypes = [P, I, I, P]
+    L.mla_mfma_probe.restype = I
     _lib = L
     return L
 
@@ -580,3 +584,26 @@ def mla_attend_prefill_chunk(q_nope, q_pe, k_nope_cache, kpe_cache, v_cache, R, 
     if rc:
         raise MlaError(rc, "mla_attend_prefill_chunk")
     return out, lse
+
+
+MLA_MFMA_PROBE_OUT = 512 * 256
+
+
+def mla_mfma_probe_flops(iters: int, kind: int = 0) -> float:
+    return lib().mla_mfma_probe_flops(int(iters), int(kind))
+
+
+def mla_mfma_probe(iters, kind=0, *, out=None, device=None, stream=None):
+    """One launch of the matrix-core rate probe (a measurement helper, not a
+    step of the path): mla_mfma_probe_flops(iters, kind) flops of MFMA chains
+    on every compute unit, kind 0 bf16 32x32x16, kind 1 e4m3 32x32x64.
+    Returns the out buffer (float32 per-thread sums of the products)."""
+    torch = _torch()
+    dev = out.device if out is not None else torch.device(device or "cuda:0")
+    if out is None:
+        out = torch.empty(MLA_MFMA_PROBE_OUT, dtype=torch.float32, device=dev)
+    _check(out, "out", torch.float32, (MLA_MFMA_PROBE_OUT,), dev)
+    rc = lib().mla_mfma_probe(_ptr(out), int(iters), int(kind), _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_mfma_probe")
+    return out

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libmla.so")
 
 SOURCES = ["mla_api.cpp", "mla_rope.hip", "mla_prefill.hip", "mla_decode.hip", "mla_oproj.hip",
-           "mla_latent.hip"]
+           "mla_latent.hip", "mla_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

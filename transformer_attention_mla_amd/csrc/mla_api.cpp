@@ -15,6 +15,7 @@
 
 #include "mla.h"
 #include "mla_internal.h"
+#include "mla_probe.h"
 
 namespace {
 
@@ -746,3 +747,22 @@ int mla_out_proj_fp8_dyn(const mla_bf16* x, const uint8_t* w8, const float* w_sc
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------ matrix-core probe
+double mla_mfma_probe_flops(int iters, int kind) {
+  if (iters < 1 || iters > (1 << 24) || kind < 0 || kind > 1) return 0.0;
+  return (double)mla::kProbeBlocks * (mla::kProbeThreads / 64) * mla::kProbeChains * (double)iters *
+         mla::kProbeFlopsPerMfma[kind];
+}
+
+int mla_mfma_probe(float* out, int iters, int kind, void* stream) {
+  if (!out) return MLA_ERR_NULL;
+  if (iters < 1 || iters > (1 << 24) || kind < 0 || kind > 1) return MLA_ERR_DIM;
+  if (!aligned16(out)) return MLA_ERR_ALIGN;
+  const int dev = check_device();
+  if (dev != MLA_OK) return dev;
+  (void)hipGetLastError();
+  if (mla::launch_mfma_probe(out, iters, kind, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
