@@ -326,6 +326,51 @@ def other_configs(mla, inputs, w_o, scale, dev, timer):
         "hbm_gbps_cold": nbytes / tup["cold"] / 1e6, "per_call": f"{fl:.4e} flops, {nbytes} bytes"}
     del d, outs
     torch.cuda.empty_cache()
+    # Attention feeding the FP8 o_proj at B=4, T=4096, 64 heads: the bf16
+    # output quantized by a separate pass (mla_attend_prefill, then
+    # mla_out_proj_fp8_dyn), against the output quantized in the attention's
+    # epilogue (mla_attend_prefill_fp8, then mla_out_proj_fp8_q).
+    B, H, T = 4, 64, 4096
+    M, K_O = B * T, H * 128
+    print(f"other config: attention -> FP8 o_proj (B={B} T={T})", file=sys.stderr, flush=True)
+    d = inputs.prefill_inputs(B, H, T, workload=3, device=dev)
+    w8, sc = inputs.out_proj_weight_fp8(inputs.D_MODEL, K_O, workload=3, device=dev)
+    N_O = w8.shape[0]
+    ws = torch.empty(mla.mla_prefill_workspace_bytes(B, H, T), dtype=torch.uint8, device=dev)
+    o16 = torch.empty((B, T, K_O), dtype=torch.bfloat16, device=dev)
+    o8 = torch.empty((B, T, K_O), dtype=torch.uint8, device=dev)
+    osT = torch.empty((H, mla.mla_act_scale_stride(M)), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N_O), dtype=torch.bfloat16, device=dev)
+    ws_d = torch.empty(max(16, mla.mla_out_proj_fp8_dyn_workspace_bytes(M, K_O, N_O)), dtype=torch.uint8,
+                       device=dev)
+    args = (d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], d["R"], scale)
+    fa16 = lambda: mla.mla_attend_prefill(*args, out=o16, workspace=ws)
+    fdyn = lambda: mla.mla_out_proj_fp8_dyn(o16.view(M, K_O), w8, sc, y=y, workspace=ws_d)
+    fa8 = lambda: mla.mla_attend_prefill_fp8(*args, out8=o8, out_scaleT=osT, workspace=ws)
+    fq = lambda: mla.mla_out_proj_fp8_q(o8.view(M, K_O), osT, w8, sc, y=y)
+    # the four calls interleaved, 10 rounds after 3 untimed ones; median per call
+    fns = (fa16, fdyn, fa8, fq)
+    for _ in range(3):
+        for f in fns:
+            f()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(10)]
+    for row in ev:
+        for (a, b), f in zip(row, fns):
+            a.record()
+            f()
+            b.record()
+    torch.cuda.synchronize()
+    t16, tdyn, t8, tq = (statistics.median(row[i][0].elapsed_time(row[i][1]) for row in ev)
+                         for i in range(len(fns)))
+    fl_a, fl_o = prefill_flops(B, H, T), oproj_flops(M, K_O, N_O)
+    out[f"attention_to_fp8_oproj_B{B}_T{T}_H{H}"] = {
+        "separate_quantization_ms": {"attention": t16, "oproj_fp8_dyn": tdyn, "total": t16 + tdyn},
+        "quantized_in_epilogue_ms": {"attention_fp8_out": t8, "oproj_fp8_q": tq, "total": t8 + tq},
+        "total_tflops": {"separate": (fl_a + fl_o) / (t16 + tdyn) / 1e9,
+                         "in_epilogue": (fl_a + fl_o) / (t8 + tq) / 1e9}}
+    del d, w8, sc, ws, o16, o8, osT, y, ws_d
+    torch.cuda.empty_cache()
     return out
 
 

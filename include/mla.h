@@ -111,6 +111,33 @@ int mla_attend_prefill(const mla_bf16 *q_nope, const mla_bf16 *q_pe, const mla_b
                        size_t workspace_bytes, void *out, float *lse, uint32_t flags,
                        void *stream);
 
+/* mla_attend_prefill with the output already quantized for the FP8 o_proj
+ * (page "Block input", config.json quantization_config: e4m3, activation
+ * scheme "dynamic"): the kernel rounds each output to bf16, as
+ * mla_attend_prefill stores it, and quantizes it in its epilogue exactly as
+ * mla_act_quant would quantize that bf16 output -- head h's 128 values of
+ * row b*T + t are one 128-column block of the o_proj input, so the block
+ * maximum is taken across the lanes that hold them.  The separate
+ * quantization pass (a read of the bf16 output, a write of the codes) is
+ * thereby folded into the attention's own store.
+ *
+ *   out8        [B, T, H*128] uint8 e4m3 codes: the [M = B*T, K = H*128]
+ *               input of mla_out_proj_fp8_q
+ *   out_scaleT  [H, mla_act_scale_stride(B*T)] float32 scales (row m of
+ *               block h at h * stride + m; columns B*T .. stride-1 are not
+ *               written)
+ *   lse         as for mla_attend_prefill (optional)
+ * Other arguments and the errors as for mla_attend_prefill; out8 or
+ * out_scaleT NULL is MLA_ERR_NULL, any flag bit MLA_ERR_FLAGS, B*T >= 2^31
+ * MLA_ERR_DIM, an output overlapping an input or another output
+ * MLA_ERR_ALIAS.
+ */
+int mla_attend_prefill_fp8(const mla_bf16 *q_nope, const mla_bf16 *q_pe, const mla_bf16 *k_nope,
+                           const mla_bf16 *k_pe, const mla_bf16 *v, const float *R, int r_rows,
+                           float softmax_scale, int B, int H, int T, void *workspace,
+                           size_t workspace_bytes, uint8_t *out8, float *out_scaleT, float *lse,
+                           uint32_t flags, void *stream);
+
 /* Allocation-free variant of mla_attend_prefill, for callers that cannot
  * allocate device memory or pass a workspace: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
@@ -345,6 +372,25 @@ size_t mla_out_proj_fp8_dyn_workspace_bytes(int M, int K, int N);
 int mla_out_proj_fp8_dyn(const mla_bf16 *x, const uint8_t *w8, const float *w_scale, void *y,
                          int M, int K, int N, void *workspace, size_t workspace_bytes,
                          uint32_t flags, void *stream);
+
+/* The product of mla_out_proj_fp8_dyn on activations already quantized (by
+ * mla_act_quant, or by mla_attend_prefill_fp8 in its epilogue): y =
+ * dequant(x8, x_scaleT) · dequant(w8, w_scale)ᵀ, the same kernels and results
+ * as mla_out_proj_fp8_dyn on the input those codes came from.
+ *
+ *   x8        [M, K] uint8 e4m3 codes, K a multiple of 128
+ *   x_scaleT  [K/128, mla_act_scale_stride(M)] float32 scales, transposed
+ *   w8, w_scale, y, M, N, flags, stream as for mla_out_proj_fp8_dyn
+ *   workspace >= mla_out_proj_fp8_q_workspace_bytes(M, K, N) bytes (float32
+ *             partials when the library splits K for M <= 64; 0 otherwise,
+ *             and then workspace may be NULL)
+ * Errors as for mla_out_proj_fp8_dyn.
+ */
+size_t mla_out_proj_fp8_q_workspace_bytes(int M, int K, int N);
+
+int mla_out_proj_fp8_q(const uint8_t *x8, const float *x_scaleT, const uint8_t *w8,
+                       const float *w_scale, void *y, int M, int K, int N, void *workspace,
+                       size_t workspace_bytes, uint32_t flags, void *stream);
 
 /* ------------------------------------------------------- up-projection --
  * The MLA up-projection in front of the attention: the query from its

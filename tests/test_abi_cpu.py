@@ -354,3 +354,58 @@ def test_act_quant_rejects_and_sizes():
     assert ws == 16384 * 8192 + 64 * 16384 * 4
     assert mla.mla_out_proj_fp8_dyn_workspace_bytes(64, 8192, 7168) > 64 * 8192 + 64 * 64 * 4
     assert mla.mla_out_proj_fp8_dyn_workspace_bytes(64, 100, 7168) == 0
+
+
+def prefill_fp8(**kw):
+    a = dict(q_nope=A[0], q_pe=A[1], k_nope=A[2], k_pe=A[3], v=A[4], R=A[5], r_rows=64,
+             scale=0.07, B=1, H=2, T=64, ws=A[6], ws_bytes=1 << 20, out8=A[7], sT=A[8], lse=None,
+             flags=0)
+    a.update(kw)
+    return mla.lib().mla_attend_prefill_fp8(a["q_nope"], a["q_pe"], a["k_nope"], a["k_pe"], a["v"],
+                                            a["R"], a["r_rows"], a["scale"], a["B"], a["H"], a["T"],
+                                            a["ws"], a["ws_bytes"], a["out8"], a["sT"], a["lse"],
+                                            a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out8=None), NULL), (dict(sT=None), NULL), (dict(q_pe=None), NULL),
+    (dict(flags=1), FLAGS),  # no float32 variant of an FP8 output
+    (dict(T=0), DIM), (dict(T=65), DIM),  # T beyond the angle table
+    (dict(scale=-1.0), SCALE),
+    (dict(ws_bytes=100), WORKSPACE),
+    (dict(out8=ctypes.c_void_p(8 * 16 * GB + 4)), ALIGN),
+    (dict(sT=ctypes.c_void_p(9 * 16 * GB + 8)), ALIGN),
+    (dict(sT=ctypes.c_void_p(1 * 16 * GB + 64)), ALIAS),  # scales over q_nope
+    (dict(sT=ctypes.c_void_p(8 * 16 * GB + 1024)), ALIAS),  # scales over the codes
+    (dict(lse=ctypes.c_void_p(9 * 16 * GB)), ALIAS),  # lse over the scales
+])
+def test_prefill_fp8_rejects(kw, code):
+    assert prefill_fp8(**kw) == code
+
+
+def oproj8q(**kw):
+    a = dict(x8=A[0], xs=A[1], w8=A[2], s=A[3], y=A[4], M=16384, K=8192, N=7168, ws=None, ws_bytes=0,
+             flags=0)
+    a.update(kw)
+    return mla.lib().mla_out_proj_fp8_q(a["x8"], a["xs"], a["w8"], a["s"], a["y"], a["M"], a["K"],
+                                        a["N"], a["ws"], a["ws_bytes"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x8=None), NULL), (dict(xs=None), NULL), (dict(w8=None), NULL), (dict(y=None), NULL),
+    (dict(flags=2), FLAGS),
+    (dict(M=0), DIM), (dict(K=100), DIM),
+    (dict(M=64), WORKSPACE),  # K split: float32 partials
+    (dict(x8=ctypes.c_void_p(1 * 16 * GB + 4)), ALIGN),
+    (dict(y=ctypes.c_void_p(3 * 16 * GB + 16)), ALIAS),  # y over w8
+    (dict(y=ctypes.c_void_p(2 * 16 * GB)), ALIAS),  # y over the activation scales
+])
+def test_oproj_fp8_q_rejects(kw, code):
+    assert oproj8q(**kw) == code
+
+
+def test_oproj_fp8_q_workspace():
+    assert mla.mla_out_proj_fp8_q_workspace_bytes(16384, 8192, 7168) == 0
+    # 4 K splits at M = 64: float32 partials only (no room for codes or scales)
+    assert mla.mla_out_proj_fp8_q_workspace_bytes(64, 8192, 7168) == 4 * 64 * 7168 * 4
+    assert mla.mla_out_proj_fp8_q_workspace_bytes(64, 100, 7168) == 0

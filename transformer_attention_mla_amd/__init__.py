@@ -98,6 +98,12 @@ def lib():
     L.mla_out_proj_fp8_dyn.restype = I
     L.mla_up_project.argtypes = [P, P, P, P, I, I, I, P, P, P, P, U, P]
     L.mla_up_project.restype = I
+    L.mla_attend_prefill_fp8.argtypes = [P, P, P, P, P, P, I, F, I, I, I, P, Z, P, P, P, U, P]
+    L.mla_attend_prefill_fp8.restype = I
+    L.mla_out_proj_fp8_q_workspace_bytes.argtypes = [I, I, I]
+    L.mla_out_proj_fp8_q_workspace_bytes.restype = Z
+    L.mla_out_proj_fp8_q.argtypes = [P, P, P, P, P, I, I, I, P, Z, U, P]
+    L.mla_out_proj_fp8_q.restype = I
     L.mla_mfma_probe_flops.argtypes = [I, I]
     L.mla_mfma_probe_flops.restype = ctypes.c_double
     L.mla_mfma_probe.argtypes = [P, I, I, P]
@@ -221,6 +227,48 @@ def mla_attend_prefill(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, out=N
     if rc:
         raise MlaError(rc, "mla_attend_prefill")
     return out, lse
+
+
+def mla_attend_prefill_fp8(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, out8=None,
+                           out_scaleT=None, lse=None, want_lse=False, workspace=None, stream=None):
+    """Causal prefill attention with its output quantized for the FP8 o_proj
+    in the epilogue (the codes and scales mla_act_quant gives for the bf16
+    output).  Shapes as for mla_attend_prefill.  Returns (out8 [B,T,H*128]
+    uint8 e4m3, out_scaleT [H, mla_act_scale_stride(B*T)] float32, lse or
+    None)."""
+    torch = _torch()
+    if q_nope.dim() != 4:
+        raise ValueError("q_nope must be [B, H, T, 128]")
+    B, H, T, _ = q_nope.shape
+    dev = q_nope.device
+    bf = torch.bfloat16
+    _check(q_nope, "q_nope", bf, (B, H, T, NOPE), dev)
+    _check(q_pe, "q_pe", bf, (B, H, T, ROPE), dev)
+    _check(k_nope, "k_nope", bf, (B, H, T, NOPE), dev)
+    _check(k_pe, "k_pe", bf, (B, 1, T, ROPE), dev)
+    _check(v, "v", bf, (B, H, T, VDIM), dev)
+    if R.dim() != 2:
+        raise ValueError("R must be [r_rows, 32]")
+    _check(R, "R", torch.float32, (R.shape[0], PAIRS), dev)
+    ms = mla_act_scale_stride(B * T)
+    if out8 is None:
+        out8 = torch.empty((B, T, H * VDIM), dtype=torch.uint8, device=dev)
+    if out_scaleT is None:
+        out_scaleT = torch.empty((H, ms), dtype=torch.float32, device=dev)
+    _check(out8, "out8", torch.uint8, (B, T, H * VDIM), dev)
+    _check(out_scaleT, "out_scaleT", torch.float32, (H, ms), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H, T), dev)
+    workspace, ws_bytes = _workspace(workspace, mla_prefill_workspace_bytes(B, H, T), dev)
+    rc = lib().mla_attend_prefill_fp8(_ptr(q_nope), _ptr(q_pe), _ptr(k_nope), _ptr(k_pe), _ptr(v),
+                                      _ptr(R), R.shape[0], float(softmax_scale), B, H, T,
+                                      _ptr(workspace), ws_bytes, _ptr(out8), _ptr(out_scaleT),
+                                      _ptr(lse), 0, _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_attend_prefill_fp8")
+    return out8, out_scaleT, lse
 
 
 def mla_attend_prefill_noalloc(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, out=None,
@@ -513,6 +561,39 @@ def mla_out_proj_fp8_dyn(x, w8, w_scale, *, y=None, out_f32=False, workspace=Non
                                     _stream_handle(stream, dev))
     if rc:
         raise MlaError(rc, "mla_out_proj_fp8_dyn")
+    return y
+
+
+def mla_out_proj_fp8_q_workspace_bytes(M: int, K: int, N: int) -> int:
+    return lib().mla_out_proj_fp8_q_workspace_bytes(M, K, N)
+
+
+def mla_out_proj_fp8_q(x8, x_scaleT, w8, w_scale, *, y=None, out_f32=False, workspace=None,
+                       stream=None):
+    """The FP8 product on activations already quantized: x8 [M,K] uint8
+    e4m3, x_scaleT [K/128, mla_act_scale_stride(M)] float32 (from
+    mla_act_quant or mla_attend_prefill_fp8), w8 [N,K] uint8 e4m3, w_scale
+    [ceil(N/128), K/128] float32.  Returns y [M,N]."""
+    torch = _torch()
+    if x8.dim() != 2 or w8.dim() != 2:
+        raise ValueError("x8 must be [M, K] and w8 [N, K]")
+    M, K = x8.shape
+    N = w8.shape[0]
+    dev = x8.device
+    _check(x8, "x8", torch.uint8, (M, K), dev)
+    _check(x_scaleT, "x_scaleT", torch.float32, (K // 128, mla_act_scale_stride(M)), dev)
+    _check(w8, "w8", torch.uint8, (N, K), dev)
+    _check(w_scale, "w_scale", torch.float32, ((N + 127) // 128, (K + 127) // 128), dev)
+    odt = torch.float32 if out_f32 else torch.bfloat16
+    if y is None:
+        y = torch.empty((M, N), dtype=odt, device=dev)
+    _check(y, "y", odt, (M, N), dev)
+    workspace, ws_bytes = _workspace(workspace, mla_out_proj_fp8_q_workspace_bytes(M, K, N), dev)
+    rc = lib().mla_out_proj_fp8_q(_ptr(x8), _ptr(x_scaleT), _ptr(w8), _ptr(w_scale), _ptr(y), M, K,
+                                  N, _ptr(workspace), ws_bytes, MLA_OUT_F32 if out_f32 else 0,
+                                  _stream_handle(stream, dev))
+    if rc:
+        raise MlaError(rc, "mla_out_proj_fp8_q")
     return y
 
 

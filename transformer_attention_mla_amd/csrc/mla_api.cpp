@@ -120,31 +120,38 @@ namespace {
 // Shared by mla_attend_prefill and mla_attend_prefill_noalloc.  `scratch` is
 // null for the caller-workspace entry point; otherwise it resolves the static
 // buffer once the arguments are validated (it needs the current device).
+// With out8 set (FP8 output), `out` is unused and out_sT receives the scales.
 int attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16* k_nope,
                    const mla_bf16* k_pe, const mla_bf16* v, const float* R, int r_rows,
                    float softmax_scale, int B, int H, int T, void* workspace,
                    size_t workspace_bytes, void* out, float* lse, uint32_t flags, void* stream,
-                   void* (*scratch)(int* status)) {
-  if (!q_nope || !q_pe || !k_nope || !k_pe || !v || !R || !out) return MLA_ERR_NULL;
-  if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
+                   void* (*scratch)(int* status), uint8_t* out8 = nullptr,
+                   float* out_sT = nullptr) {
+  const bool fp8 = out8 != nullptr || out_sT != nullptr;
+  if (!q_nope || !q_pe || !k_nope || !k_pe || !v || !R || (!fp8 && !out) || (fp8 && (!out8 || !out_sT)))
+    return MLA_ERR_NULL;
+  if (flags & ~(fp8 ? 0u : MLA_OUT_F32)) return MLA_ERR_FLAGS;
   if (!dims_ok(B, H, T, kQK) || r_rows <= 0 || r_rows > kMaxDim || T > r_rows ||
       (size_t)H * T * 256 > 0xffffffffu)
     return MLA_ERR_DIM;
+  if (fp8 && (long long)B * T > 0x7ffffff0LL) return MLA_ERR_DIM;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_SCALE;
   const mla::PrefillWorkspace ws = mla::prefill_workspace_layout(B, T);
   if (!scratch && !workspace) return MLA_ERR_WORKSPACE;
   if (workspace_bytes < ws.total) return MLA_ERR_WORKSPACE;
   if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(k_nope) || !aligned16(k_pe) ||
-      !aligned16(v) || !aligned16(R) || !aligned16(out) || !aligned16(lse) || !aligned16(workspace))
+      !aligned16(v) || !aligned16(R) || !aligned16(out) || !aligned16(lse) || !aligned16(workspace) ||
+      !aligned16(out8) || !aligned16(out_sT))
     return MLA_ERR_ALIGN;
   const size_t bht = (size_t)B * H * T;
   const size_t out_elt = (flags & MLA_OUT_F32) ? 4 : 2;
   const Range in[] = {{q_nope, bht * kNope * 2}, {q_pe, bht * kRope * 2}, {k_nope, bht * kNope * 2},
                       {k_pe, (size_t)B * T * kRope * 2}, {v, bht * kV * 2},
                       {R, (size_t)r_rows * mla::kPairs * 4}};
-  const Range outs[] = {{out, bht * kV * out_elt}, {lse, lse ? bht * 4 : 0},
-                        {workspace, scratch ? 0 : ws.total}};
-  if (any_alias(in, 6, outs, 3)) return MLA_ERR_ALIAS;
+  const Range outs[] = {{fp8 ? nullptr : out, bht * kV * out_elt}, {lse, lse ? bht * 4 : 0},
+                        {workspace, scratch ? 0 : ws.total}, {out8, fp8 ? bht * kV : 0},
+                        {out_sT, fp8 ? (size_t)H * mla::act_scale_stride(B * T) * 4 : 0}};
+  if (any_alias(in, 6, outs, 5)) return MLA_ERR_ALIAS;
   const int dev = check_device();
   if (dev != MLA_OK) return dev;
   if (scratch) {
@@ -162,7 +169,9 @@ int attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16*
   p.R = R;
   p.cs = reinterpret_cast<float2*>(static_cast<char*>(workspace) + ws.cs_off);
   p.kpe_rot = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + ws.kpe_off);
-  p.out = out;
+  p.out = fp8 ? nullptr : out;
+  p.out8 = out8;
+  p.out_sT = out_sT;
   p.lse = lse;
   p.B = B;
   p.H = H;
@@ -227,6 +236,16 @@ int mla_attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_b
                        void* stream) {
   return attend_prefill(q_nope, q_pe, k_nope, k_pe, v, R, r_rows, softmax_scale, B, H, T,
                         workspace, workspace_bytes, out, lse, flags, stream, nullptr);
+}
+
+int mla_attend_prefill_fp8(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16* k_nope,
+                           const mla_bf16* k_pe, const mla_bf16* v, const float* R, int r_rows,
+                           float softmax_scale, int B, int H, int T, void* workspace,
+                           size_t workspace_bytes, uint8_t* out8, float* out_scaleT, float* lse,
+                           uint32_t flags, void* stream) {
+  return attend_prefill(q_nope, q_pe, k_nope, k_pe, v, R, r_rows, softmax_scale, B, H, T,
+                        workspace, workspace_bytes, nullptr, lse, flags, stream, nullptr, out8,
+                        out_scaleT);
 }
 
 int mla_attend_prefill_noalloc(const mla_bf16* q_nope, const mla_bf16* q_pe,
@@ -696,6 +715,52 @@ bool fp8dyn_dims_ok(int M, int K, int N) {
          (long long)M * K <= 0x7fffffffLL && (long long)M * N <= kMaxElems;
 }
 }  // namespace
+
+size_t mla_out_proj_fp8_q_workspace_bytes(int M, int K, int N) {
+  if (!fp8dyn_dims_ok(M, K, N)) return 0;
+  const Fp8DynWorkspace ws = fp8dyn_layout(M, K, N);
+  return ws.total - ws.part_off;
+}
+
+int mla_out_proj_fp8_q(const uint8_t* x8, const float* x_scaleT, const uint8_t* w8,
+                       const float* w_scale, void* y, int M, int K, int N, void* workspace,
+                       size_t workspace_bytes, uint32_t flags, void* stream) {
+  if (!x8 || !x_scaleT || !w8 || !w_scale || !y) return MLA_ERR_NULL;
+  if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
+  if (!fp8dyn_dims_ok(M, K, N)) return MLA_ERR_DIM;
+  const Fp8DynWorkspace ws = fp8dyn_layout(M, K, N);
+  const size_t need = ws.total - ws.part_off;  // the split partials only
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(x8) || !aligned16(x_scaleT) || !aligned16(w8) || !aligned16(w_scale) ||
+      !aligned16(y) || !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  const size_t out_elt = (flags & MLA_OUT_F32) ? 4 : 2;
+  const size_t nb = (size_t)(N + 127) / 128, kb = (size_t)K / 128;
+  const Range in[] = {{x8, (size_t)M * K}, {x_scaleT, kb * mla::act_scale_stride(M) * 4},
+                      {w8, (size_t)N * K}, {w_scale, nb * kb * 4}};
+  const Range outs[] = {{y, (size_t)M * N * out_elt}, {need ? workspace : nullptr, need}};
+  if (any_alias(in, 4, outs, 2)) return MLA_ERR_ALIAS;
+  const int dev = check_device();
+  if (dev != MLA_OK) return dev;
+  (void)hipGetLastError();
+  mla::OprojParams p;
+  p.x = nullptr;
+  p.w = nullptr;
+  p.w8 = w8;
+  p.w_scale = w_scale;
+  p.x8 = x8;
+  p.x_scaleT = x_scaleT;
+  p.y = y;
+  p.part = ws.splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  p.M = M;
+  p.K = K;
+  p.N = N;
+  p.splits = ws.splits;
+  p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
+  p.group_m = 0;
+  if (mla::launch_oproj_fp8dyn(p, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
 
 size_t mla_out_proj_fp8_dyn_workspace_bytes(int M, int K, int N) {
   if (!fp8dyn_dims_ok(M, K, N)) return 0;

@@ -53,6 +53,12 @@ struct PrefillParams {
   float scale_log2;    // softmax_scale * log2(e)
   int out_f32;
   int paired;          // set by launch_prefill: 1 = a workgroup takes query tiles i and NQ-1-i
+  // FP8 output instead of `out` (when out8 is set): the bf16-rounded outputs
+  // quantized as launch_act_quant quantizes the o_proj input, one 128-column
+  // block per (row b*T + t, head): codes out8 [B*T][H*128] e4m3, scales
+  // out_sT [H][act_scale_stride(B*T)].
+  uint8_t* out8 = nullptr;
+  float* out_sT = nullptr;
 };
 
 hipError_t launch_rope_prep(const PrefillParams& p, hipStream_t stream);

@@ -401,7 +401,42 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     barrier_lds();  // every wave is done with the stages before the next pass refills them
 
     // ---- epilogue
-    if (head_ok) {
+    if (head_ok && p.out8) {
+      // FP8 output: the bf16-rounded outputs of this query and head (64 per
+      // lane, the other 64 in lane ^ 32) are one 128-column block of the
+      // o_proj input; scale = max(block amax, 1e-4) / 448, codes e4m3(x /
+      // scale) with the divisions correctly rounded -- the arithmetic of the
+      // activation quantizer, so the codes equal its codes of the bf16 output.
+      const float l_tot = sum_halves(l_run);
+      const float inv = 1.0f / l_tot;
+      float amax = 0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          acc[db][r] = (float)f32_to_bf16(acc[db][r] * inv);
+          amax = fmaxf(amax, fabsf(acc[db][r]));
+        }
+      const float sc = fmaxf(max_halves(amax), 1e-4f) / 448.0f;
+      if (myq < T) {
+        const size_t row = (size_t)b * T + myq;
+        uint8_t* dst = p.out8 + row * ((size_t)H * kV) + (size_t)head * kV;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            int w = 0;
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(acc[db][gq * 4 + 0] / sc, acc[db][gq * 4 + 1] / sc, w, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(acc[db][gq * 4 + 2] / sc, acc[db][gq * 4 + 3] / sc, w, true);
+            *reinterpret_cast<uint32_t*>(dst + db * 32 + gq * 8 + hf * 4) = (uint32_t)w;
+          }
+        if (hf == 0) {
+          p.out_sT[(size_t)head * act_scale_stride(p.B * T) + row] = sc;
+          if (p.lse)
+            p.lse[((size_t)b * H + head) * T + myq] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+        }
+      }
+    } else if (head_ok) {
       const float l_tot = sum_halves(l_run);
       const float inv = 1.0f / l_tot;
       if (myq < T) {
