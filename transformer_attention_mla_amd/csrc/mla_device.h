@@ -39,6 +39,12 @@ __device__ __forceinline__ u32x2 ld_global_8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }
 
+// A 16-byte load of data read once per call (a cache or weight stream), with
+// the non-temporal policy so the stream does not displace reusable lines.
+__device__ __forceinline__ u32x4 ld_stream_16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
 
@@ -87,6 +93,17 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wav
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory", "m0");
+}
+
+// dma16 with the non-temporal policy, for bytes read once per call.
+__device__ __forceinline__ void dma16_stream(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wave_base, uint32_t voff) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen nt lds"
       :
       : "s"(lds), "v"(voff), "s"(r)
       : "memory", "m0");

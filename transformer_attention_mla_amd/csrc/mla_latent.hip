@@ -185,10 +185,10 @@ void latent_decode_kernel(LatentParams p) {
 #pragma unroll
     for (int u = 0; u < L_CPW; ++u) {
       const int j = wave * L_CPW + u;
-      if (j < LBK)
-        dma16(live ? crs : none, st + j * 1024, voff[u] + k0 * L_CROW);
+      if (j < LBK)  // every cached byte is read once per call: non-temporal
+        dma16_stream(live ? crs : none, st + j * 1024, voff[u] + k0 * L_CROW);
       else
-        dma16(live ? prs : none, st + j * 1024, voff[u] + k0 * L_PROW);
+        dma16_stream(live ? prs : none, st + j * 1024, voff[u] + k0 * L_PROW);
     }
   };
 
