@@ -36,22 +36,22 @@ CSRC = os.path.join(REPO, "transformer_attention_mla_amd", "csrc")
 # bytes written).  Each figure holds only for the kernel source it was taken on,
 # identified by a hash of its files; after any change the figure is dropped.
 MEASURED_TRAFFIC = {
-    "prefill_kernel": ("13791f12995d4d8b", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
-                       2095935536, "profiles/prefill_kernel_B4_T4096_H64.txt"),
-    "decode_split_kernel": ("41aa6342ec469a2b", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                            21477800703, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
-    "decode_split_kernel_shared_kpe": ("41aa6342ec469a2b", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                                       17496553619, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
-    "latent_decode_kernel": ("c7f899a345bd8ced", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
-                             657383382, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
+    "prefill_kernel": ("fb5263fb670dac4e", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
+                       2086889126, "profiles/prefill_kernel_B4_T4096_H64.txt"),
+    "decode_split_kernel": ("e278ec5917a24807", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                            21477791650, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
+    "decode_split_kernel_shared_kpe": ("e278ec5917a24807", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                                       17249596128, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
+    "latent_decode_kernel": ("9e75355e82fb7a23", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
+                             657392443, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
 }
 # o_proj GEMM kernels at K = 8192, N = 7168 (the split-K reduce kernel, shared
 # by several paths, is left out), M = 16384 and M = 64.
-_OPROJ_SRC = ("b3041477f2ce2071", ("mla_oproj.hip", "mla_device.h", "mla_internal.h"))
+_OPROJ_SRC = ("9ecfb224453d64ca", ("mla_oproj.hip", "mla_device.h", "mla_internal.h"))
 _OPROJ_PROFILE = "profiles/oproj_kernel_M16384_K8192_N7168_and_M64.txt"
-for _k, _v in {"oproj_bf16_M16384": 3213942016, "oproj_bf16_M64": 140821713,
-               "oproj_fp8_M16384": 176252083 + 3198226859, "oproj_fp8_M64": 81983364,
-               "oproj_fp8_dyn_M16384": 1733958354 + 411083829, "oproj_fp8_dyn_M64": 70548531 + 1651754}.items():
+for _k, _v in {"oproj_bf16_M16384": 3204922652, "oproj_bf16_M64": 140689375,
+               "oproj_fp8_M16384": 176252098 + 3197935840, "oproj_fp8_M64": 81984166,
+               "oproj_fp8_dyn_M16384": 1733861476 + 411083815, "oproj_fp8_dyn_M64": 70548528 + 1651754}.items():
     MEASURED_TRAFFIC[_k] = _OPROJ_SRC + (_v, _OPROJ_PROFILE)
 
 
