@@ -403,6 +403,47 @@ __global__ __launch_bounds__(WNT) void oproj_wide_kernel(OprojParams p) {
     mma(f1);
   }
 
+  // bf16 output: the tile goes through LDS (both stages are free now, 256
+  // rows x 512 B = 128 KiB), so that each global store writes whole 128-byte
+  // lines of a row -- a lane's own results are 8-byte pieces of 32 different
+  // rows, which the memory system absorbs far more slowly (the stores then
+  // cost a fifth of the time at K = 1536 and almost half at K = 512).
+  // Row r keeps its 16-byte chunk c at c ^ (r % 32).
+  if (!p.out_f32 && (p.hd > 0 || (N & 7) == 0)) {
+    barrier_lds();  // every wave has read its last fragments
+#pragma unroll
+    for (int jm = 0; jm < WTM; ++jm) {
+      const int r = wm * (WTM * 32) + jm * 32 + ln;
+#pragma unroll
+      for (int i = 0; i < WTN; ++i)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int c = wn * (WTN * 4) + i * 4 + gq;
+          *reinterpret_cast<u32x2*>(wlds + r * 512 + ((c ^ (r & 31)) * 16) + hf * 8) =
+              u32x2{pack_bf16x2(acc[i][jm][gq * 4 + 0], acc[i][jm][gq * 4 + 1]),
+                    pack_bf16x2(acc[i][jm][gq * 4 + 2], acc[i][jm][gq * 4 + 3])};
+        }
+    }
+    barrier_lds();
+    const int c = lane & 31;  // chunk: columns n0 + 8c .. +7
+    const int n = n0 + c * 8;
+    SplitCol sc;
+    if (p.hd > 0 && n < N) sc = split_col(p, n0 + (c >> 2) * 32);
+#pragma unroll 4
+    for (int rr = 0; rr < WBM / (2 * WNW); ++rr) {
+      const int r = (rr * WNW + wave) * 2 + (lane >> 5);
+      const int m = m0 + r;
+      if (m >= M || n >= N) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(wlds + r * 512 + ((c ^ (r & 31)) * 16));
+      if (p.hd > 0) {
+        const size_t off = (split_row(p, m) + sc.head_off) * sc.width + sc.d + (c & 3) * 8;
+        *reinterpret_cast<u32x4*>(static_cast<__bf16*>(sc.base) + off) = v;
+      } else {
+        *reinterpret_cast<u32x4*>(static_cast<__bf16*>(p.y) + (size_t)m * N + n) = v;
+      }
+    }
+    return;
+  }
   if (p.hd > 0) {
 #pragma unroll
     for (int jm = 0; jm < WTM; ++jm) {
