@@ -740,6 +740,39 @@ __global__ __launch_bounds__(64 * WN * WM) void oproj_fp8_kernel(OprojParams p) 
       acc[TL / WTM][TL % WTM][r] = fmaf(tq[TL & 1][r], scp, acc[TL / WTM][TL % WTM][r]);
   }
 
+  // bf16 output of the 256 x 256 tile: staged through the free LDS stages
+  // and stored as whole lines, as in the wide bf16 kernel.
+  if constexpr (BN == 256 && BM * BN * 2 <= NSTG * STG) {
+    if (p.splits == 1 && !p.out_f32 && (N & 7) == 0) {
+      barrier_lds();  // every wave has read its last fragments
+#pragma unroll
+      for (int jm = 0; jm < WTM; ++jm) {
+        const int r = wm * (WTM * 32) + jm * 32 + ln;
+#pragma unroll
+        for (int i = 0; i < WTN; ++i)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int c = wn * (WTN * 4) + i * 4 + gq;
+            *reinterpret_cast<u32x2*>(fl + r * 512 + ((c ^ (r & 31)) * 16) + hf * 8) =
+                u32x2{pack_bf16x2(acc[i][jm][gq * 4 + 0], acc[i][jm][gq * 4 + 1]),
+                      pack_bf16x2(acc[i][jm][gq * 4 + 2], acc[i][jm][gq * 4 + 3])};
+          }
+      }
+      barrier_lds();
+      const int c = lane & 31;
+      const int n = n0 + c * 8;
+#pragma unroll 4
+      for (int rr = 0; rr < BM / (2 * NWAVE); ++rr) {
+        const int r = (rr * NWAVE + wave) * 2 + (lane >> 5);
+        const int m = m0 + r;
+        if (m >= M || n >= N) continue;
+        *reinterpret_cast<u32x4*>(static_cast<__bf16*>(p.y) + (size_t)m * N + n) =
+            *reinterpret_cast<const u32x4*>(fl + r * 512 + ((c ^ (r & 31)) * 16));
+      }
+      return;
+    }
+  }
+
 #pragma unroll
   for (int jm = 0; jm < WTM; ++jm) {
     const int m = m0 + wm * (WTM * 32) + jm * 32 + ln;

@@ -89,6 +89,7 @@ constexpr int NCW = 2;                         // waves that copy
 constexpr int DPW = (NCHUNK + NCW - 1) / NCW;  // 11 copies per copying wave per tile
 static_assert(STAGE % 1024 == 0 && KPOFF % 1024 == 0 && VOFF % 1024 == 0, "chunk layout");
 static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS budget");
+static_assert(BQ * kV * 2 <= NSTAGE * STAGE, "the staged output tile fits the stages");
 static_assert((NSTAGE - 2) * DPW < 64, "vmcnt range");
 static_assert(NCHUNK - NCW >= CKP, "spare copies repeat V chunks");
 
@@ -436,6 +437,37 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
             p.lse[((size_t)b * H + head) * T + myq] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
         }
       }
+    } else if (head_ok && !p.out_f32) {
+      // bf16 output: the workgroup's 256 query rows x 256 B go through LDS
+      // (free: every wave is past its last tile) so that each global store
+      // writes whole lines of a row; a lane's own results are 8-byte pieces
+      // of 32 rows.  Row q keeps its 16-byte chunk c at c ^ (q mod 16).
+      const float l_tot = sum_halves(l_run);
+      const float inv = 1.0f / l_tot;
+      const int q = qb * 32 + ln;  // tile-local row
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int c = db * 4 + gq;
+          *reinterpret_cast<u32x2*>(lds + q * 256 + ((c ^ (q & 15)) * 16) + hf * 8) =
+              u32x2{pack_bf16x2(acc[db][gq * 4 + 0] * inv, acc[db][gq * 4 + 1] * inv),
+                    pack_bf16x2(acc[db][gq * 4 + 2] * inv, acc[db][gq * 4 + 3] * inv)};
+        }
+      if (p.lse && hf == 0 && myq < T)
+        p.lse[((size_t)b * H + head) * T + myq] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+      barrier_lds();
+      const int c = lane & 15;
+#pragma unroll
+      for (int rr = 0; rr < BQ / (4 * NW); ++rr) {
+        const int r = (rr * NW + wave) * 4 + (lane >> 4);
+        const int t = qt * BQ + r;
+        if (t >= T) continue;
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + ((size_t)b * T + t) * ((size_t)H * kV) +
+                                  (size_t)head * kV + c * 8) =
+            *reinterpret_cast<const u32x4*>(lds + r * 256 + ((c ^ (r & 15)) * 16));
+      }
+      barrier_lds();  // every wave has read the staged rows before the next pass's copies
     } else if (head_ok) {
       const float l_tot = sum_halves(l_run);
       const float inv = 1.0f / l_tot;
