@@ -36,8 +36,8 @@ CSRC = os.path.join(REPO, "transformer_attention_mla_amd", "csrc")
 # bytes written).  Each figure holds only for the kernel source it was taken on,
 # identified by a hash of its files; after any change the figure is dropped.
 MEASURED_TRAFFIC = {
-    "prefill_kernel": ("fb5263fb670dac4e", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
-                       2086889126, "profiles/prefill_kernel_B4_T4096_H64.txt"),
+    "prefill_kernel": ("d5d172b645c359f7", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
+                       2006234015, "profiles/prefill_kernel_B4_T4096_H64.txt"),
     "decode_split_kernel": ("e278ec5917a24807", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
                             21477791650, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
     "decode_split_kernel_shared_kpe": ("e278ec5917a24807", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
@@ -47,11 +47,11 @@ MEASURED_TRAFFIC = {
 }
 # o_proj GEMM kernels at K = 8192, N = 7168 (the split-K reduce kernel, shared
 # by several paths, is left out), M = 16384 and M = 64.
-_OPROJ_SRC = ("9ecfb224453d64ca", ("mla_oproj.hip", "mla_device.h", "mla_internal.h"))
+_OPROJ_SRC = ("497701d27461a358", ("mla_oproj.hip", "mla_device.h", "mla_internal.h"))
 _OPROJ_PROFILE = "profiles/oproj_kernel_M16384_K8192_N7168_and_M64.txt"
-for _k, _v in {"oproj_bf16_M16384": 3204922652, "oproj_bf16_M64": 140689375,
-               "oproj_fp8_M16384": 176252098 + 3197935840, "oproj_fp8_M64": 81984166,
-               "oproj_fp8_dyn_M16384": 1733861476 + 411083815, "oproj_fp8_dyn_M64": 70548528 + 1651754}.items():
+for _k, _v in {"oproj_bf16_M16384": 3190233034, "oproj_bf16_M64": 140681548,
+               "oproj_fp8_M16384": 176252088 + 3190278405, "oproj_fp8_M64": 81979959,
+               "oproj_fp8_dyn_M16384": 1728980824 + 411087930, "oproj_fp8_dyn_M64": 70557747 + 1655850}.items():
     MEASURED_TRAFFIC[_k] = _OPROJ_SRC + (_v, _OPROJ_PROFILE)
 
 
