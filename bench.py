@@ -36,22 +36,22 @@ CSRC = os.path.join(REPO, "transformer_attention_mla_amd", "csrc")
 # bytes written).  Each figure holds only for the kernel source it was taken on,
 # identified by a hash of its files; after any change the figure is dropped.
 MEASURED_TRAFFIC = {
-    "prefill_kernel": ("d5d172b645c359f7", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
-                       2006234015, "profiles/prefill_kernel_B4_T4096_H64.txt"),
-    "decode_split_kernel": ("e278ec5917a24807", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                            21477791650, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
-    "decode_split_kernel_shared_kpe": ("e278ec5917a24807", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                                       17249596128, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
-    "latent_decode_kernel": ("9e75355e82fb7a23", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
-                             657392443, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
+    "prefill_kernel": ("2478cc0ad31a8ba1", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
+                       1988590260, "profiles/prefill_kernel_B4_T4096_H64.txt"),
+    "decode_split_kernel": ("6931c1b00c67b632", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                            21477808333, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
+    "decode_split_kernel_shared_kpe": ("6931c1b00c67b632", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                                       17249618665, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
+    "latent_decode_kernel": ("772ba3d56ca0bcba", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
+                             657396962, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
 }
 # o_proj GEMM kernels at K = 8192, N = 7168 (the split-K reduce kernel, shared
 # by several paths, is left out), M = 16384 and M = 64.
-_OPROJ_SRC = ("497701d27461a358", ("mla_oproj.hip", "mla_device.h", "mla_internal.h"))
+_OPROJ_SRC = ("e93ba6a7920a2f97", ("mla_oproj.hip", "mla_device.h", "mla_internal.h"))
 _OPROJ_PROFILE = "profiles/oproj_kernel_M16384_K8192_N7168_and_M64.txt"
-for _k, _v in {"oproj_bf16_M16384": 3190233034, "oproj_bf16_M64": 140681548,
-               "oproj_fp8_M16384": 176252088 + 3190278405, "oproj_fp8_M64": 81979959,
-               "oproj_fp8_dyn_M16384": 1728980824 + 411087930, "oproj_fp8_dyn_M64": 70557747 + 1655850}.items():
+for _k, _v in {"oproj_bf16_M16384": 3201583158, "oproj_bf16_M64": 140670153,
+               "oproj_fp8_M16384": 176245012 + 3195933014, "oproj_fp8_M64": 81988834,
+               "oproj_fp8_dyn_M16384": 1728855613 + 411088300, "oproj_fp8_dyn_M64": 70562988 + 1655852}.items():
     MEASURED_TRAFFIC[_k] = _OPROJ_SRC + (_v, _OPROJ_PROFILE)
 
 
@@ -264,6 +264,7 @@ def other_configs(mla, inputs, w_o, scale, dev, timer):
         B, H, T = wl["B"], wl["H"], wl["T"]
         print(f"other config: workload {w} (B={B} T={T})", file=sys.stderr, flush=True)
         d = inputs.prefill_inputs(B, H, T, workload=w, device=dev)
+        d["v"] = inputs.to_v_blocked(d["v"])  # the layout mla_up_project writes with MLA_V_BLOCKED
         o = torch.empty((B, T, H * 128), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(mla.mla_prefill_workspace_bytes(B, H, T), dtype=torch.uint8, device=dev)
         M, K_O, N_O = B * T, H * 128, w_o.shape[0]
@@ -271,7 +272,7 @@ def other_configs(mla, inputs, w_o, scale, dev, timer):
         ws_o = torch.empty(max(16, mla.mla_out_proj_workspace_bytes(M, K_O, N_O)), dtype=torch.uint8,
                            device=dev)
         fa = lambda: mla.mla_attend_prefill(d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"],
-                                            d["R"], scale, out=o, workspace=ws)
+                                            d["R"], scale, out=o, workspace=ws, v_blocked=True)
         fo = lambda: mla.mla_out_proj(o.view(M, K_O), w_o, y=y, workspace=ws_o)
 
         calls = 200 if T <= 1024 else 10
@@ -315,8 +316,10 @@ def other_configs(mla, inputs, w_o, scale, dev, timer):
     B, T, H = 4, 4096, 64
     print(f"other config: up-projection (B={B} T={T})", file=sys.stderr, flush=True)
     d = inputs.up_project_inputs(B, T, H, workload=3, device=dev)
-    outs = [torch.empty((B, H, T, w), dtype=torch.bfloat16, device=dev) for w in (128, 64, 128, 128)]
-    fup = lambda: mla.mla_up_project(d["q_lat"], d["ckv"], d["w_q_b"], d["w_kv_b"], outs=outs)
+    outs = [torch.empty((B, H, T, w), dtype=torch.bfloat16, device=dev) for w in (128, 64, 128)]
+    outs.append(torch.empty((B, H, (T + 15) // 16, 128, 16), dtype=torch.bfloat16, device=dev))
+    fup = lambda: mla.mla_up_project(d["q_lat"], d["ckv"], d["w_q_b"], d["w_kv_b"], outs=outs,
+                                     v_blocked=True)
     tup = timer.both(fup, 10)
     fl = 2.0 * B * T * (1536 * H * 192 + 512 * H * 256)
     nbytes = 2 * (B * T * (1536 + 512) + H * 192 * 1536 + H * 256 * 512 + B * H * T * (128 + 64 + 128 + 128))
@@ -343,10 +346,11 @@ def other_configs(mla, inputs, w_o, scale, dev, timer):
     y = torch.empty((M, N_O), dtype=torch.bfloat16, device=dev)
     ws_d = torch.empty(max(16, mla.mla_out_proj_fp8_dyn_workspace_bytes(M, K_O, N_O)), dtype=torch.uint8,
                        device=dev)
-    args = (d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], d["R"], scale)
-    fa16 = lambda: mla.mla_attend_prefill(*args, out=o16, workspace=ws)
+    args = (d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], inputs.to_v_blocked(d["v"]), d["R"], scale)
+    fa16 = lambda: mla.mla_attend_prefill(*args, out=o16, workspace=ws, v_blocked=True)
     fdyn = lambda: mla.mla_out_proj_fp8_dyn(o16.view(M, K_O), w8, sc, y=y, workspace=ws_d)
-    fa8 = lambda: mla.mla_attend_prefill_fp8(*args, out8=o8, out_scaleT=osT, workspace=ws)
+    fa8 = lambda: mla.mla_attend_prefill_fp8(*args, out8=o8, out_scaleT=osT, workspace=ws,
+                                             v_blocked=True)
     fq = lambda: mla.mla_out_proj_fp8_q(o8.view(M, K_O), osT, w8, sc, y=y)
     # the four calls interleaved, 10 rounds after 3 untimed ones; median per call
     fns = (fa16, fdyn, fa8, fq)
@@ -596,6 +600,9 @@ def main():
     w_o = inputs.out_proj_weight(N_O, K_O, workload=3, device=dev)
     if do_p:
         d = inputs.prefill_inputs(B, H, T, workload=3, device=dev)
+        # values key-blocked, as mla_up_project writes them with MLA_V_BLOCKED (the
+        # oracle leg below takes the same values in [B, H, T, 128])
+        v_blk = inputs.to_v_blocked(d["v"])
         attn_out = torch.empty((B, T, H * 128), dtype=torch.bfloat16, device=dev)
         y_p = torch.empty((B * T, N_O), dtype=torch.bfloat16, device=dev)
         ws_p = torch.empty(mla.mla_prefill_workspace_bytes(B, H, T), dtype=torch.uint8, device=dev)
@@ -629,8 +636,8 @@ def main():
                 ev[name][i][1].record()
         if do_p:
             timed("prefill_attention", lambda: mla.mla_attend_prefill(
-                d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], d["v"], d["R"], scale,
-                out=attn_out, workspace=ws_p))
+                d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], v_blk, d["R"], scale,
+                out=attn_out, workspace=ws_p, v_blocked=True))
             timed("prefill_oproj", lambda: mla.mla_out_proj(
                 attn_out.view(B * T, K_O), w_o, y=y_p, workspace=ws_op))
         if do_d:
@@ -690,7 +697,8 @@ def main():
                            "measured_mfma_tflops": mfma_tf,
                            "frac_of_measured_mfma": fa / ta / 1e12 / mfma_tf}
         parts.append(f"prefill B={B} T={T} H={H} causal + o_proj [{B * T}x{K_O}]x[{K_O}x{N_O}]")
-        cfg.update({"prefill_batch": B, "prefill_seq_len": T})
+        cfg.update({"prefill_batch": B, "prefill_seq_len": T,
+                    "prefill_v_layout": "key-blocked [B,H,T/16,128,16] (MLA_V_BLOCKED)"})
     if do_d:
         bd = decode_bytes(Bd, Hd, L)
         td = avg["decode_attention"] / 1e3

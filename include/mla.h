@@ -74,6 +74,21 @@ typedef enum {
  * round-to-nearest-even of its float32 twin. */
 #define MLA_OUT_F32 0x1u
 
+/* flags bit for mla_attend_prefill (and its _fp8 and _noalloc forms) and
+ * mla_up_project: `v` is held key-blocked instead of [B, H, T, 128]:
+ *
+ *   v  [B, H, NB, 128, 16] bf16, NB = ceil(T/16); value feature d of position
+ *      t at element ((b*H + h)*NB + t/16)*2048 + d*16 + t%16
+ *
+ * i.e. each block of 16 consecutive positions is stored feature by feature.
+ * The value product takes 8 consecutive keys of one feature per lane, which
+ * in this layout are 16 contiguous bytes; from the natural layout the
+ * attention kernel transposes them on every LDS read.  The slots of
+ * positions T .. NB*16-1 in the last block of each head never reach a result
+ * (any contents, NaN included) and mla_up_project leaves them unwritten.
+ * Everything else (the results bit for bit included) is as without the bit. */
+#define MLA_V_BLOCKED 0x2u
+
 /* Version of this ABI (MLA_ABI_VERSION). */
 int mla_abi_version(void);
 
@@ -88,17 +103,20 @@ const char *mla_status_string(int status);
  *   q_pe    [B, H, T, 64]  bf16   rotary query part, NOT yet rotated
  *   k_nope  [B, H, T, 128] bf16   non-rotated key part
  *   k_pe    [B, 1, T, 64]  bf16   rotary key part, NOT yet rotated, shared by all heads
- *   v       [B, H, T, 128] bf16   values
+ *   v       [B, H, T, 128] bf16   values (key-blocked with MLA_V_BLOCKED)
  *   R       [r_rows, 32]   float  angle table in radians, row t = position t; T <= r_rows
  *   softmax_scale                 score multiplier (Kimi K2: 192^-0.5), finite and > 0
  *   workspace                     device scratch of >= mla_prefill_workspace_bytes(B,H,T)
- *                                 bytes (cos/sin table and the rotated shared key)
+ *                                 bytes (cos/sin table, the rotated shared key and,
+ *                                 when T % 16 != 0, a zero-padded copy of each
+ *                                 head's last key-blocked value tile)
  *   out     [B, T, H*128]  bf16, or float32 with MLA_OUT_F32; element
  *                          [b][t][h*128+d] is head h's output (head-major flatten)
  *   lse     [B, H, T] float natural-log sum of exp of the scaled, masked scores
  *                     per row, or NULL
  *
  * Row t of head h is softmax_j≤t(scale·(q_nope·k_noperᵀ + rot(q_pe)·rot(k_pe)ᵀ))·V.
+ * flags: MLA_OUT_F32, MLA_V_BLOCKED (others MLA_ERR_FLAGS).
  * B, H, T >= 1 with any tails.  The softmax is evaluated online in float32 in
  * base 2; the weights that multiply V are rounded to bf16 and the row sum is
  * accumulated from those same rounded weights.
@@ -128,7 +146,8 @@ int mla_attend_prefill(const mla_bf16 *q_nope, const mla_bf16 *q_pe, const mla_b
  *               written)
  *   lse         as for mla_attend_prefill (optional)
  * Other arguments and the errors as for mla_attend_prefill; out8 or
- * out_scaleT NULL is MLA_ERR_NULL, any flag bit MLA_ERR_FLAGS, B*T >= 2^31
+ * out_scaleT NULL is MLA_ERR_NULL, a flag bit other than MLA_V_BLOCKED
+ * MLA_ERR_FLAGS, B*T >= 2^31
  * MLA_ERR_DIM, an output overlapping an input or another output
  * MLA_ERR_ALIAS.
  */
@@ -143,10 +162,11 @@ int mla_attend_prefill_fp8(const mla_bf16 *q_nope, const mla_bf16 *q_pe, const m
  * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
  * computation and results (bit for bit) as mla_attend_prefill, without
  * `workspace` / `workspace_bytes`: the cos/sin table and the rotated shared key
- * go to a static buffer of MLA_PREFILL_NOALLOC_SCRATCH_BYTES that each GPU
- * holds for the life of the process.  The call needs
- * mla_prefill_workspace_bytes(B, H, T) = T·256 + B·T·128 bytes (each part
- * rounded up to 256); sizes beyond MLA_PREFILL_NOALLOC_SCRATCH_BYTES (16 MiB:
+ * (and, when T % 16 != 0, the zero-padded last value tile of each head) go to
+ * a static buffer of MLA_PREFILL_NOALLOC_SCRATCH_BYTES that each GPU holds for
+ * the life of the process.  The call needs mla_prefill_workspace_bytes(B, H, T)
+ * = T·256 + B·T·128 (+ B·H·8192 when T % 16 != 0) bytes (each part rounded up
+ * to 256); sizes beyond MLA_PREFILL_NOALLOC_SCRATCH_BYTES (16 MiB:
  * e.g. B·T up to 98,304 positions at T = 16384, 129,024 at T = 1024) return
  * MLA_ERR_WORKSPACE before anything is enqueued.  No device memory is
  * allocated or freed by this call.  Every call on one GPU uses that GPU's
@@ -410,7 +430,9 @@ int mla_out_proj_fp8_q(const uint8_t *x8, const float *x_scaleT, const uint8_t *
  *                                rows h*256+128 .. +127: its value
  *   q_nope  [B, H, T, 128], q_pe [B, H, T, 64] (unrotated: the rotary step is
  *   the attention's), k_nope [B, H, T, 128], v [B, H, T, 128]: outputs in the
- *   layouts mla_attend_prefill takes; bf16, or float32 with MLA_OUT_F32.
+ *   layouts mla_attend_prefill takes; bf16, or float32 with MLA_OUT_F32; v
+ *   key-blocked ([B, H, ceil(T/16), 128, 16], the slots past T unwritten)
+ *   with MLA_V_BLOCKED.
  *
  * Float32 accumulation over the latent, one rounding per output.  No
  * workspace.  Errors: a NULL pointer MLA_ERR_NULL; B, T, H < 1 or too large

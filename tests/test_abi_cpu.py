@@ -135,7 +135,7 @@ def oproj(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q_nope=None), NULL), (dict(k_pe=None), NULL), (dict(R=None), NULL), (dict(out=None), NULL),
-    (dict(flags=2), FLAGS),
+    (dict(flags=4), FLAGS), (dict(flags=6), FLAGS),
     (dict(B=0), DIM), (dict(H=-1), DIM), (dict(T=0), DIM), (dict(T=65), DIM), (dict(r_rows=0), DIM),
     (dict(scale=0.0), SCALE), (dict(scale=-1.0), SCALE), (dict(scale=float("nan")), SCALE),
     (dict(scale=float("inf")), SCALE),
@@ -144,6 +144,9 @@ def oproj(**kw):
     (dict(out=ctypes.c_void_p(1 * 16 * GB + 4096)), ALIAS),     # out inside q_nope
     (dict(ws=A[7]), ALIAS),                                   # workspace == out
     (dict(lse=ctypes.c_void_p(7 * 16 * GB + 1024)), ALIAS),    # lse inside workspace
+    # key-blocked v spans whole 16-key blocks: at T = 63 it reaches 256 B past the
+    # [B, H, T, 128] extent, into `out`
+    (dict(T=63, flags=2, v=ctypes.c_void_p(8 * 16 * GB - 2 * 63 * 256 - 256)), ALIAS),
 ])
 def test_prefill_rejects(kw, code):
     assert prefill(**kw) == code
@@ -161,7 +164,7 @@ def prefill_noalloc(**kw):
 # Every case fails validation: B * T beyond the static buffer (16 MiB holds
 # T*256 + B*T*128 bytes) is MLA_ERR_WORKSPACE, before any device call.
 @pytest.mark.parametrize("kw,code", [
-    (dict(q_nope=None), NULL), (dict(out=None), NULL), (dict(flags=2), FLAGS),
+    (dict(q_nope=None), NULL), (dict(out=None), NULL), (dict(flags=4), FLAGS),
     (dict(T=0), DIM), (dict(scale=0.0), SCALE),
     (dict(B=7, T=16384), WORKSPACE), (dict(B=1, T=65536), WORKSPACE),
     (dict(B=127, T=1024), WORKSPACE),
@@ -176,6 +179,15 @@ def test_prefill_noalloc_limit_matches_workspace_formula():
     limit = 16 << 20
     assert mla.mla_prefill_workspace_bytes(6, 1, 16384) <= limit < mla.mla_prefill_workspace_bytes(7, 1, 16384)
     assert mla.mla_prefill_workspace_bytes(126, 1, 1024) <= limit < mla.mla_prefill_workspace_bytes(127, 1, 1024)
+
+
+def test_prefill_workspace_value_tail():
+    # T % 16 != 0: one zero-padded key-blocked value tile (8 KiB) per (b, h)
+    base = lambda B, T: -(-T * 32 * 8 // 256) * 256 + -(-B * T * 64 * 2 // 256) * 256
+    assert mla.mla_prefill_workspace_bytes(2, 3, 1008) == base(2, 1008)
+    assert mla.mla_prefill_workspace_bytes(2, 3, 1000) == base(2, 1000) + 2 * 3 * 8192
+    assert mla.mla_prefill_workspace_bytes(2, 3, 1001) == base(2, 1001) + 2 * 3 * 8192
+    assert mla.mla_prefill_workspace_bytes(4, 64, 4095) == base(4, 4095) + 4 * 64 * 8192
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -320,6 +332,10 @@ def up(**kw):
     (dict(kn=ctypes.c_void_p(1 * 16 * GB + 64)), ALIAS),   # k_nope over q_lat
     (dict(v=ctypes.c_void_p(4 * 16 * GB + 256)), ALIAS),   # v over w_kv_b
     (dict(v=ctypes.c_void_p(5 * 16 * GB + 256)), ALIAS),   # v over q_nope
+    # key-blocked v (whole 16-position blocks) at T = 4095 reaches into q_nope,
+    # which the [B, H, T, 128] extent ends 4 KiB short of
+    (dict(T=4095, flags=2, v=ctypes.c_void_p(5 * 16 * GB - 4 * 64 * 4095 * 256 - 4096)), ALIAS),
+    (dict(flags=6), FLAGS),
 ])
 def test_up_project_rejects(kw, code):
     assert up(**kw) == code
@@ -370,6 +386,7 @@ def prefill_fp8(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(out8=None), NULL), (dict(sT=None), NULL), (dict(q_pe=None), NULL),
     (dict(flags=1), FLAGS),  # no float32 variant of an FP8 output
+    (dict(flags=3), FLAGS), (dict(flags=4), FLAGS),
     (dict(T=0), DIM), (dict(T=65), DIM),  # T beyond the angle table
     (dict(scale=-1.0), SCALE),
     (dict(ws_bytes=100), WORKSPACE),

@@ -26,6 +26,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 
 MLA_OUT_F32 = 0x1
+MLA_V_BLOCKED = 0x2  # v key-blocked: [B, H, ceil(T/16), 128, 16]
 NOPE, ROPE, VDIM, PAIRS = 128, 64, 128, 32
 LATENT = 512  # kv_lora_rank
 Q_RANK = 1536  # q_lora_rank
@@ -191,11 +192,17 @@ def _ptr(t):
 
 # ------------------------------------------------------------------ calls
 
+def _v_shape(B, H, T, v_blocked):
+    return (B, H, (T + 15) // 16, VDIM, 16) if v_blocked else (B, H, T, VDIM)
+
+
 def mla_attend_prefill(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, out=None, lse=None,
-                       want_lse=False, out_f32=False, workspace=None, stream=None):
+                       want_lse=False, out_f32=False, v_blocked=False, workspace=None,
+                       stream=None):
     """Causal prefill attention.  Shapes: q_nope/k_nope/v [B,H,T,128] bf16,
     q_pe [B,H,T,64] bf16 (unrotated), k_pe [B,1,T,64] bf16 (unrotated, shared
-    by heads), R [r_rows,32] float32 (angles, r_rows >= T).  Returns
+    by heads), R [r_rows,32] float32 (angles, r_rows >= T); with v_blocked, v
+    is key-blocked [B,H,ceil(T/16),128,16] (MLA_V_BLOCKED).  Returns
     (out [B,T,H*128] bf16 or float32, lse [B,H,T] float32 or None)."""
     torch = _torch()
     if q_nope.dim() != 4:
@@ -207,7 +214,7 @@ def mla_attend_prefill(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, out=N
     _check(q_pe, "q_pe", bf, (B, H, T, ROPE), dev)
     _check(k_nope, "k_nope", bf, (B, H, T, NOPE), dev)
     _check(k_pe, "k_pe", bf, (B, 1, T, ROPE), dev)
-    _check(v, "v", bf, (B, H, T, VDIM), dev)
+    _check(v, "v", bf, _v_shape(B, H, T, v_blocked), dev)
     if R.dim() != 2:
         raise ValueError("R must be [r_rows, 32]")
     _check(R, "R", torch.float32, (R.shape[0], PAIRS), dev)
@@ -220,17 +227,19 @@ def mla_attend_prefill(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, out=N
     if lse is not None:
         _check(lse, "lse", torch.float32, (B, H, T), dev)
     workspace, ws_bytes = _workspace(workspace, mla_prefill_workspace_bytes(B, H, T), dev)
+    flags = (MLA_OUT_F32 if out_f32 else 0) | (MLA_V_BLOCKED if v_blocked else 0)
     rc = lib().mla_attend_prefill(_ptr(q_nope), _ptr(q_pe), _ptr(k_nope), _ptr(k_pe), _ptr(v),
                                   _ptr(R), R.shape[0], float(softmax_scale), B, H, T,
                                   _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
-                                  MLA_OUT_F32 if out_f32 else 0, _stream_handle(stream, dev))
+                                  flags, _stream_handle(stream, dev))
     if rc:
         raise MlaError(rc, "mla_attend_prefill")
     return out, lse
 
 
 def mla_attend_prefill_fp8(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, out8=None,
-                           out_scaleT=None, lse=None, want_lse=False, workspace=None, stream=None):
+                           out_scaleT=None, lse=None, want_lse=False, v_blocked=False,
+                           workspace=None, stream=None):
     """Causal prefill attention with its output quantized for the FP8 o_proj
     in the epilogue (the codes and scales mla_act_quant gives for the bf16
     output).  Shapes as for mla_attend_prefill.  Returns (out8 [B,T,H*128]
@@ -246,7 +255,7 @@ def mla_attend_prefill_fp8(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, o
     _check(q_pe, "q_pe", bf, (B, H, T, ROPE), dev)
     _check(k_nope, "k_nope", bf, (B, H, T, NOPE), dev)
     _check(k_pe, "k_pe", bf, (B, 1, T, ROPE), dev)
-    _check(v, "v", bf, (B, H, T, VDIM), dev)
+    _check(v, "v", bf, _v_shape(B, H, T, v_blocked), dev)
     if R.dim() != 2:
         raise ValueError("R must be [r_rows, 32]")
     _check(R, "R", torch.float32, (R.shape[0], PAIRS), dev)
@@ -265,14 +274,16 @@ def mla_attend_prefill_fp8(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, o
     rc = lib().mla_attend_prefill_fp8(_ptr(q_nope), _ptr(q_pe), _ptr(k_nope), _ptr(k_pe), _ptr(v),
                                       _ptr(R), R.shape[0], float(softmax_scale), B, H, T,
                                       _ptr(workspace), ws_bytes, _ptr(out8), _ptr(out_scaleT),
-                                      _ptr(lse), 0, _stream_handle(stream, dev))
+                                      _ptr(lse), MLA_V_BLOCKED if v_blocked else 0,
+                                      _stream_handle(stream, dev))
     if rc:
         raise MlaError(rc, "mla_attend_prefill_fp8")
     return out8, out_scaleT, lse
 
 
 def mla_attend_prefill_noalloc(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, *, out=None,
-                               lse=None, want_lse=False, out_f32=False, stream=None):
+                               lse=None, want_lse=False, out_f32=False, v_blocked=False,
+                               stream=None):
     """mla_attend_prefill without a workspace argument: the library's static
     per-device buffer (MLA_PREFILL_NOALLOC_SCRATCH_BYTES) holds the cos/sin
     table and the rotated shared key.  Same shapes and results; calls that
@@ -288,7 +299,7 @@ def mla_attend_prefill_noalloc(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, 
     _check(q_pe, "q_pe", bf, (B, H, T, ROPE), dev)
     _check(k_nope, "k_nope", bf, (B, H, T, NOPE), dev)
     _check(k_pe, "k_pe", bf, (B, 1, T, ROPE), dev)
-    _check(v, "v", bf, (B, H, T, VDIM), dev)
+    _check(v, "v", bf, _v_shape(B, H, T, v_blocked), dev)
     if R.dim() != 2:
         raise ValueError("R must be [r_rows, 32]")
     _check(R, "R", torch.float32, (R.shape[0], PAIRS), dev)
@@ -300,9 +311,10 @@ def mla_attend_prefill_noalloc(q_nope, q_pe, k_nope, k_pe, v, R, softmax_scale, 
         lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
     if lse is not None:
         _check(lse, "lse", torch.float32, (B, H, T), dev)
+    flags = (MLA_OUT_F32 if out_f32 else 0) | (MLA_V_BLOCKED if v_blocked else 0)
     rc = lib().mla_attend_prefill_noalloc(_ptr(q_nope), _ptr(q_pe), _ptr(k_nope), _ptr(k_pe),
                                           _ptr(v), _ptr(R), R.shape[0], float(softmax_scale), B, H,
-                                          T, _ptr(out), _ptr(lse), MLA_OUT_F32 if out_f32 else 0,
+                                          T, _ptr(out), _ptr(lse), flags,
                                           _stream_handle(stream, dev))
     if rc:
         raise MlaError(rc, "mla_attend_prefill_noalloc")
@@ -453,11 +465,13 @@ def mla_out_proj(x, w_o, *, y=None, out_f32=False, workspace=None, stream=None):
     return y
 
 
-def mla_up_project(q_lat, ckv, w_q_b, w_kv_b, *, outs=None, out_f32=False, stream=None):
+def mla_up_project(q_lat, ckv, w_q_b, w_kv_b, *, outs=None, out_f32=False, v_blocked=False,
+                   stream=None):
     """The MLA up-projection: q_lat [B,T,1536] and ckv [B,T,512] bf16, w_q_b
     [H*192,1536] and w_kv_b [H*256,512] bf16.  Returns (q_nope [B,H,T,128],
     q_pe [B,H,T,64] unrotated, k_nope [B,H,T,128], v [B,H,T,128]), bf16 or
-    float32; ``outs`` may hold the four output tensors."""
+    float32; with v_blocked, v is key-blocked [B,H,ceil(T/16),128,16] (the
+    slots past T unwritten).  ``outs`` may hold the four output tensors."""
     torch = _torch()
     if q_lat.dim() != 3 or w_q_b.dim() != 2:
         raise ValueError("q_lat must be [B, T, 1536] and w_q_b [H*192, 1536]")
@@ -469,13 +483,14 @@ def mla_up_project(q_lat, ckv, w_q_b, w_kv_b, *, outs=None, out_f32=False, strea
     _check(w_q_b, "w_q_b", torch.bfloat16, (H * (NOPE + ROPE), Q_RANK), dev)
     _check(w_kv_b, "w_kv_b", torch.bfloat16, (H * (NOPE + VDIM), LATENT), dev)
     odt = torch.float32 if out_f32 else torch.bfloat16
-    shapes = [(B, H, T, NOPE), (B, H, T, ROPE), (B, H, T, NOPE), (B, H, T, VDIM)]
+    shapes = [(B, H, T, NOPE), (B, H, T, ROPE), (B, H, T, NOPE), _v_shape(B, H, T, v_blocked)]
     if outs is None:
         outs = [torch.empty(sh, dtype=odt, device=dev) for sh in shapes]
     for t, sh, name in zip(outs, shapes, ("q_nope", "q_pe", "k_nope", "v")):
         _check(t, name, odt, sh, dev)
     rc = lib().mla_up_project(_ptr(q_lat), _ptr(ckv), _ptr(w_q_b), _ptr(w_kv_b), B, T, H,
-                              *[_ptr(t) for t in outs], MLA_OUT_F32 if out_f32 else 0,
+                              *[_ptr(t) for t in outs],
+                              (MLA_OUT_F32 if out_f32 else 0) | (MLA_V_BLOCKED if v_blocked else 0),
                               _stream_handle(stream, dev))
     if rc:
         raise MlaError(rc, "mla_up_project")

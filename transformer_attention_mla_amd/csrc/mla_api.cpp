@@ -110,7 +110,7 @@ const char* mla_status_string(int status) {
 
 size_t mla_prefill_workspace_bytes(int B, int H, int T) {
   if (!dims_ok(B, H, T, kQK)) return 0;
-  return mla::prefill_workspace_layout(B, T).total;
+  return mla::prefill_workspace_layout(B, H, T).total;
 }
 
 }  // extern "C"
@@ -130,13 +130,14 @@ int attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16*
   const bool fp8 = out8 != nullptr || out_sT != nullptr;
   if (!q_nope || !q_pe || !k_nope || !k_pe || !v || !R || (!fp8 && !out) || (fp8 && (!out8 || !out_sT)))
     return MLA_ERR_NULL;
-  if (flags & ~(fp8 ? 0u : MLA_OUT_F32)) return MLA_ERR_FLAGS;
+  if (flags & ~(MLA_V_BLOCKED | (fp8 ? 0u : MLA_OUT_F32))) return MLA_ERR_FLAGS;
+  const bool vblk = (flags & MLA_V_BLOCKED) != 0;
   if (!dims_ok(B, H, T, kQK) || r_rows <= 0 || r_rows > kMaxDim || T > r_rows ||
       (size_t)H * T * 256 > 0xffffffffu)
     return MLA_ERR_DIM;
   if (fp8 && (long long)B * T > 0x7ffffff0LL) return MLA_ERR_DIM;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_SCALE;
-  const mla::PrefillWorkspace ws = mla::prefill_workspace_layout(B, T);
+  const mla::PrefillWorkspace ws = mla::prefill_workspace_layout(B, H, T);
   if (!scratch && !workspace) return MLA_ERR_WORKSPACE;
   if (workspace_bytes < ws.total) return MLA_ERR_WORKSPACE;
   if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(k_nope) || !aligned16(k_pe) ||
@@ -144,9 +145,10 @@ int attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16*
       !aligned16(out8) || !aligned16(out_sT))
     return MLA_ERR_ALIGN;
   const size_t bht = (size_t)B * H * T;
+  const size_t v_rows = vblk ? (size_t)B * H * ((T + 15) / 16 * 16) : bht;
   const size_t out_elt = (flags & MLA_OUT_F32) ? 4 : 2;
   const Range in[] = {{q_nope, bht * kNope * 2}, {q_pe, bht * kRope * 2}, {k_nope, bht * kNope * 2},
-                      {k_pe, (size_t)B * T * kRope * 2}, {v, bht * kV * 2},
+                      {k_pe, (size_t)B * T * kRope * 2}, {v, v_rows * kV * 2},
                       {R, (size_t)r_rows * mla::kPairs * 4}};
   const Range outs[] = {{fp8 ? nullptr : out, bht * kV * out_elt}, {lse, lse ? bht * 4 : 0},
                         {workspace, scratch ? 0 : ws.total}, {out8, fp8 ? bht * kV : 0},
@@ -180,9 +182,13 @@ int attend_prefill(const mla_bf16* q_nope, const mla_bf16* q_pe, const mla_bf16*
   p.LK = T;
   p.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
   p.out_f32 = (flags & MLA_OUT_F32) ? 1 : 0;
+  p.v_blocked = vblk ? 1 : 0;
+  if (vblk && ws.vtail_bytes)
+    p.v_tail = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + ws.vtail_off);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
   if (mla::launch_rope_prep(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  if (p.v_tail && mla::launch_v_tail(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
   if (mla::launch_prefill(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
   return MLA_OK;
 }
@@ -567,7 +573,8 @@ int mla_up_project(const mla_bf16* q_lat, const mla_bf16* ckv, const mla_bf16* w
                    const mla_bf16* w_kv_b, int B, int T, int H, void* q_nope, void* q_pe,
                    void* k_nope, void* v, uint32_t flags, void* stream) {
   if (!q_lat || !ckv || !w_q_b || !w_kv_b || !q_nope || !q_pe || !k_nope || !v) return MLA_ERR_NULL;
-  if (flags & ~MLA_OUT_F32) return MLA_ERR_FLAGS;
+  if (flags & ~(MLA_OUT_F32 | MLA_V_BLOCKED)) return MLA_ERR_FLAGS;
+  const bool vblk = (flags & MLA_V_BLOCKED) != 0;
   if (!dims_ok(B, T, H, mla::kQK + kV) || (long long)B * T > 0x7fffffffLL ||
       (long long)H * (kNope + kV) > 0x7fffffffLL)
     return MLA_ERR_DIM;
@@ -575,6 +582,7 @@ int mla_up_project(const mla_bf16* q_lat, const mla_bf16* ckv, const mla_bf16* w
       !aligned16(q_nope) || !aligned16(q_pe) || !aligned16(k_nope) || !aligned16(v))
     return MLA_ERR_ALIGN;
   const size_t M = (size_t)B * T, rows = (size_t)B * H * T;
+  const size_t v_rows = vblk ? (size_t)B * H * ((T + 15) / 16 * 16) : rows;
   const size_t elt = (flags & MLA_OUT_F32) ? 4 : 2;
   const Range in[] = {{q_lat, M * mla::kQRank * 2},
                       {ckv, M * mla::kLatent * 2},
@@ -583,7 +591,7 @@ int mla_up_project(const mla_bf16* q_lat, const mla_bf16* ckv, const mla_bf16* w
   const Range outs[] = {{q_nope, rows * kNope * elt},
                         {q_pe, rows * kRope * elt},
                         {k_nope, rows * kNope * elt},
-                        {v, rows * kV * elt}};
+                        {v, v_rows * kV * elt}};
   if (any_alias(in, 4, outs, 4)) return MLA_ERR_ALIAS;
   const int dev = check_device();
   if (dev != MLA_OK) return dev;
@@ -617,6 +625,7 @@ int mla_up_project(const mla_bf16* q_lat, const mla_bf16* ckv, const mla_bf16* w
   p.hd = kNope + kV;
   p.y = k_nope;
   p.y1 = v;
+  p.y1_blocked = vblk ? 1 : 0;
   if (mla::launch_oproj(p, s) != hipSuccess) return MLA_ERR_LAUNCH;
   return MLA_OK;
 }

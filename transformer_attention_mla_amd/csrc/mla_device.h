@@ -46,6 +46,14 @@ __device__ __forceinline__ u32x4 ld_stream_16(const void* p) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16), per 16-lane group: each
+// lane addresses 8 bytes (four 16-bit elements); lane i receives element i%4
+// of the pieces that lanes i/4, i/4+4, i/4+8 and i/4+12 address, in that order.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 ds_read_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
 __device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
 
 // D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulate.

@@ -23,16 +23,24 @@ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct PrefillWorkspace {
   size_t cs_off, cs_bytes;    // float2 [T][32]: (cos, sin) of R[t][i]
   size_t kpe_off, kpe_bytes;  // bf16 [B][T][64]: rotated shared key
+  // When T % 16 != 0: bf16 [B][H][2][128][16], per head the key-blocked value
+  // tile (blocks 2*((T-1)/32) and the next) with the slots of positions T..
+  // zeroed, read instead of v's own last tile (used with key-blocked v only).
+  size_t vtail_off, vtail_bytes;
   size_t total;
 };
 
-inline PrefillWorkspace prefill_workspace_layout(int B, int T) {
+constexpr int kVTileElems = 2 * 16 * 128;  // one 32-key tile of key-blocked V
+
+inline PrefillWorkspace prefill_workspace_layout(int B, int H, int T) {
   PrefillWorkspace w;
   w.cs_off = 0;
   w.cs_bytes = align_up((size_t)T * kPairs * 8, 256);
   w.kpe_off = w.cs_off + w.cs_bytes;
   w.kpe_bytes = align_up((size_t)B * T * kRope * 2, 256);
-  w.total = w.kpe_off + w.kpe_bytes;
+  w.vtail_off = w.kpe_off + w.kpe_bytes;
+  w.vtail_bytes = (T % 16) ? align_up((size_t)B * H * kVTileElems * 2, 256) : 0;
+  w.total = w.vtail_off + w.vtail_bytes;
   return w;
 }
 
@@ -59,9 +67,18 @@ struct PrefillParams {
   // out_sT [H][act_scale_stride(B*T)].
   uint8_t* out8 = nullptr;
   float* out_sT = nullptr;
+  // V key-blocked (plain prefill only: past = 0, LK = T): v [B][H][ceil(T/16)][128][16],
+  // element (b, h, t, d) at ((b*H + h)*ceil(T/16) + t/16)*2048 + d*16 + t%16.
+  int v_blocked = 0;
+  // With v_blocked and T % 16 != 0: per head the last key tile of v with its
+  // slots past T zeroed ([B][H][kVTileElems], workspace; written by
+  // launch_v_tail), which the kernel reads in place of that tile.
+  uint16_t* v_tail = nullptr;
 };
 
 hipError_t launch_rope_prep(const PrefillParams& p, hipStream_t stream);
+// p.v_tail from p.v (key-blocked; p.T % 16 != 0).
+hipError_t launch_v_tail(const PrefillParams& p, hipStream_t stream);
 
 // Rotary table and rotated shared key at positions r_off + t, t < T: cs[t]
 // (when cs is set) and dst[b][dst_off + t] (rows of dst_rows) from k_pe[b][t]
@@ -153,6 +170,10 @@ struct OprojParams {
   // [B][H][T][hd-d0] at d - d0 (H = N / hd; hd and d0 multiples of 32).
   int hd = 0, d0 = 0, T = 0;
   void* y1 = nullptr;
+  // y1 key-blocked (hd > 0): column h*hd + d (d >= d0) of row b*T + t goes to
+  // y1 [B][H][ceil(T/16)][hd-d0][16] at ((b*H + h)*ceil(T/16) + t/16)*16*(hd-d0)
+  // + (d-d0)*16 + t%16.
+  int y1_blocked = 0;
 };
 
 int oproj_choose_splits(int M, int K, int N, bool fp8 = false);

@@ -96,6 +96,8 @@ struct SplitCol {
   void* base;       // y or y1
   size_t head_off;  // h*T rows
   int width, d;     // the part's row width and the block's first feature in it
+  int h;            // head
+  bool blk;         // the key-blocked second part
 };
 __device__ __forceinline__ size_t split_row(const OprojParams& p, int m) {
   const int b = m / p.T;
@@ -105,11 +107,29 @@ __device__ __forceinline__ SplitCol split_col(const OprojParams& p, int nb) {
   const int h = nb / p.hd, d = nb - h * p.hd;
   const bool first = d < p.d0;
   return SplitCol{first ? p.y : p.y1, (size_t)h * p.T, first ? p.d0 : p.hd - p.d0,
-                  first ? d : d - p.d0};
+                  first ? d : d - p.d0, h, !first && p.y1_blocked};
 }
-// Features c.d + dn .. +3 of the block for the row at split_row r.
-__device__ __forceinline__ void store_split4(const OprojParams& p, const SplitCol& c, size_t r, int dn,
-                                             float v0, float v1, float v2, float v3) {
+// Element offset of feature d of head h, row m = b*T + t, in the key-blocked part.
+__device__ __forceinline__ size_t blocked_off(const OprojParams& p, int m, int h, int d) {
+  const int b = m / p.T, t = m - b * p.T;
+  const int H = p.N / p.hd, NB = (p.T + 15) >> 4, w = p.hd - p.d0;
+  return ((size_t)(b * H + h) * NB + (t >> 4)) * (16 * w) + d * 16 + (t & 15);
+}
+// Features c.d + dn .. +3 of the block for row m (at split_row r).
+__device__ __forceinline__ void store_split4(const OprojParams& p, const SplitCol& c, size_t r, int m,
+                                             int dn, float v0, float v1, float v2, float v3) {
+  if (c.blk) {
+    const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const size_t off = blocked_off(p, m, c.h, c.d + dn + e);
+      if (p.out_f32)
+        static_cast<float*>(c.base)[off] = v[e];
+      else
+        static_cast<__bf16*>(c.base)[off] = f32_to_bf16(v[e]);
+    }
+    return;
+  }
   const size_t off = (r + c.head_off) * c.width + c.d + dn;
   if (p.out_f32)
     *reinterpret_cast<f32x4*>(static_cast<float*>(c.base) + off) = f32x4{v0, v1, v2, v3};
@@ -226,7 +246,7 @@ __global__ __launch_bounds__(ONT) void oproj_kernel(OprojParams p) {
         const SplitCol c = split_col(p, nb);
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq)
-          store_split4(p, c, r, gq * 8 + hf * 4, acc[i][jm][gq * 4 + 0], acc[i][jm][gq * 4 + 1],
+          store_split4(p, c, r, m, gq * 8 + hf * 4, acc[i][jm][gq * 4 + 0], acc[i][jm][gq * 4 + 1],
                        acc[i][jm][gq * 4 + 2], acc[i][jm][gq * 4 + 3]);
       }
     }
@@ -425,6 +445,62 @@ __global__ __launch_bounds__(WNT) void oproj_wide_kernel(OprojParams p) {
         }
     }
     barrier_lds();
+    if (p.y1_blocked) {
+      // The tile is one head (hd = 256, d0 = 128): chunks 0..15 are its first
+      // part, stored as row pieces, four rows per wave instruction; the second
+      // part goes key-blocked, each wave instruction writing one 16-row block
+      // of 32 features (1 KiB), a lane's 8 rows of one feature gathered by
+      // two transposing LDS reads (lane i of a 16-lane group receives element
+      // i%4 of the 8-byte pieces that lanes i/4, i/4+4, i/4+8, i/4+12 address).
+      const int h = n0 / p.hd;
+      {
+        const int c = lane & 15;
+        const SplitCol sc = split_col(p, n0 + (c >> 2) * 32);
+#pragma unroll 4
+        for (int rr = 0; rr < WBM / (4 * WNW); ++rr) {
+          const int r = (rr * WNW + wave) * 4 + (lane >> 4);
+          const int m = m0 + r;
+          if (m >= M) continue;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(wlds + r * 512 + ((c ^ (r & 31)) * 16));
+          const size_t off = (split_row(p, m) + sc.head_off) * sc.width + sc.d + (c & 3) * 8;
+          *reinterpret_cast<u32x4*>(static_cast<__bf16*>(sc.base) + off) = v;
+        }
+      }
+      uint16_t* y1 = static_cast<uint16_t*>(p.y1);
+      if ((p.T & 15) == 0) {  // every 16-row block lies in one sequence (M % 16 == 0 too)
+        const int g = lane >> 4, i = lane & 15, half = g >> 1, q = i & 3;
+        const int H = N / p.hd, NB = p.T >> 4;
+#pragma unroll 2
+        for (int it = 0; it < (WBM / 16) * 4 / WNW; ++it) {
+          const int w = it * WNW + wave;
+          const int j = w >> 2, fg = w & 3;  // 16-row block, 32-feature group
+          const int m = m0 + j * 16;
+          if (m >= M) continue;
+          const int b = m / p.T, t = m - b * p.T;
+          // as a source, lane (g, i) addresses features 16(g&1) + 4q .. +3 of the
+          // group in row i/4 (+4) of the block's half `half`
+          const int cc = 16 + fg * 4 + 2 * (g & 1) + (q >> 1);
+          const int rA = j * 16 + half * 8 + (i >> 2), rB = rA + 4;
+          const s16x4 lo = ds_read_tr(wlds + rA * 512 + ((cc ^ (rA & 31)) * 16) + (q & 1) * 8);
+          const s16x4 hi = ds_read_tr(wlds + rB * 512 + ((cc ^ (rB & 31)) * 16) + (q & 1) * 8);
+          const int d = fg * 32 + 16 * (g & 1) + i;  // received: feature d, rows half*8 .. +7
+          *reinterpret_cast<u32x4*>(y1 + ((size_t)(b * H + h) * NB + (t >> 4)) * 2048 + d * 16 + half * 8) =
+              __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      } else {  // a 16-row block may span two sequences: element stores
+        const int c = 16 + (lane & 15);
+        for (int rr = 0; rr < WBM / (4 * WNW); ++rr) {
+          const int r = (rr * WNW + wave) * 4 + (lane >> 4);
+          const int m = m0 + r;
+          if (m >= M) continue;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(wlds + r * 512 + ((c ^ (r & 31)) * 16));
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            y1[blocked_off(p, m, h, (c - 16) * 8 + e)] = (uint16_t)(v[e >> 1] >> ((e & 1) * 16));
+        }
+      }
+      return;
+    }
     const int c = lane & 31;  // chunk: columns n0 + 8c .. +7
     const int n = n0 + c * 8;
     SplitCol sc;
@@ -457,7 +533,7 @@ __global__ __launch_bounds__(WNT) void oproj_wide_kernel(OprojParams p) {
         const SplitCol c = split_col(p, nb);
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq)
-          store_split4(p, c, r, gq * 8 + hf * 4, acc[i][jm][gq * 4 + 0], acc[i][jm][gq * 4 + 1],
+          store_split4(p, c, r, m, gq * 8 + hf * 4, acc[i][jm][gq * 4 + 0], acc[i][jm][gq * 4 + 1],
                        acc[i][jm][gq * 4 + 2], acc[i][jm][gq * 4 + 3]);
       }
     }
@@ -840,6 +916,7 @@ hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
                    p.hd % 32 != 0 || p.d0 % 32 != 0 || p.d0 <= 0 || p.d0 >= p.hd || !p.y1))
     return hipErrorInvalidConfiguration;
   if (!p.w8 && p.splits == 1 && oproj_use_wide(p.M, p.K, p.N)) {
+    if (p.y1_blocked && (p.hd != WBN || p.d0 != WBN / 2)) return hipErrorInvalidConfiguration;
     const long wide_tiles = (long)((p.M + WBM - 1) / WBM) * ((p.N + WBN - 1) / WBN);
     if (wide_tiles > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (p.group_m <= 0) p.group_m = WGROUP_M;

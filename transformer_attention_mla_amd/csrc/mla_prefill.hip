@@ -43,8 +43,12 @@
 //   * Key rows are stored in LDS in the order the A lanes read them, chosen so
 //     that the Sᵀ accumulator registers are directly the B-operand layout of
 //     Pᵀ in Oᵀ += Vᵀ·Pᵀ (no data movement between the two products).
-//   * Vᵀ fragments come from V's natural [key][dim] layout with the gfx950
-//     transposing LDS read ds_read_b64_tr_b16.
+//   * Vᵀ fragments (8 consecutive keys of one feature per lane) come from V's
+//     natural [key][dim] layout with the gfx950 transposing LDS read
+//     ds_read_b64_tr_b16, or, when V is given key-blocked (16-key blocks
+//     stored feature by feature), with one plain 16-byte read each: the
+//     transposing read moves about 90 B per clock per compute unit against
+//     about 236 for ds_read_b128.
 //   * Online softmax in base 2, softmax_scale·log2(e) folded into one FMA.  The
 //     reference maximum is only raised when a tile's maximum exceeds it by
 //     more than 8 (weights then stay <= 2^8); the result is the same softmax.
@@ -109,13 +113,11 @@ __device__ __forceinline__ int kpswz(int R) { return (R ^ (R >> 3)) & 7; }
 
 __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ s16x4 ds_read_tr(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-}
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
+// VB: V key-blocked, [B][H][ceil(LK/16)][128][16] (past = 0 only).
+template <bool VB>
 __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -185,20 +187,35 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
       const int c = (s % 8) ^ kpswz(R);
       v = (uint32_t)(akey(R) * 128 + c * 16);
       kind[i] = 1;
-    } else {
+    } else if (!VB) {
       const int s = (j - CKP) * 64 + lane;  // slot in the V region (16 per row)
       const int row = s / 16;
       const int c = (s % 16) ^ ((row & 3) << 2);
       v = (uint32_t)row * 256u + c * 16;
+      kind[i] = 2;
+    } else {
+      // Key-blocked V: the tile is two 4 KiB blocks [128 features][16 keys];
+      // feature d's 32-byte row keeps its key halves swapped when d & 8, so
+      // that 16 lanes reading 16 consecutive features hit 64 distinct banks.
+      const int s = (j - CKP) * 64 + lane;
+      const int blk = s >> 8, d = (s >> 1) & 127, half = (s & 1) ^ ((d >> 3) & 1);
+      v = (uint32_t)(blk * 4096 + d * 32 + half * 16);
       kind[i] = 2;
     }
     voff[i] = v;
   }
   const int headc = head_ok ? head : H - 1;
   const uint16_t* khead = p.k_nope + ((size_t)b * H + headc) * LK * kNope;
-  const uint16_t* vhead = p.v + ((size_t)b * H + headc) * LK * kV;
+  const int LKV = VB ? (LK + 15) / 16 * 16 : LK;  // V rows per head (whole blocks when blocked)
+  const uint16_t* vhead = p.v + ((size_t)b * H + headc) * LKV * kV;
   const uint16_t* pseq = p.kpe_rot + (size_t)b * LK * kRope;
   const uint32_t nvis = (uint32_t)(past + p.T);  // rows 0 .. past+T-1 hold data
+  // Blocked V: the extent covers whole 16-key blocks.  When the last block is
+  // partial, its slots past the data may hold any bits, so the tile holding
+  // it is read from the zero-padded copy in the workspace instead.
+  const uint32_t nvis_v = VB ? (nvis + 15u) / 16u * 16u : nvis;
+  const int kt_tail = (VB && (nvis & 15u)) ? (int)((nvis - 1) / BK) : -1;
+  const uint16_t* vtail = VB && p.v_tail ? p.v_tail + ((size_t)b * H + headc) * kVTileElems : nullptr;
 
   // Copies of one tile: descriptors whose base advances with the tile, and the
   // stage they fill.  Past the last tile the descriptors are empty (nothing is
@@ -215,7 +232,9 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     // live tiles start below kend <= nvis, so the extents are positive
     c.rK = make_rsrc(khead + (size_t)k0 * kNope, live ? (nvis - k0) * 256u : 0u);
     c.rP = make_rsrc(pseq + (size_t)k0 * kRope, live ? (nvis - k0) * 128u : 0u);
-    c.rV = make_rsrc(vhead + (size_t)k0 * kV, live ? (nvis - k0) * 256u : 0u);
+    const bool tail = live && kt == kt_tail;
+    c.rV = make_rsrc(tail ? vtail : vhead + (size_t)k0 * kV,
+                     tail ? (uint32_t)kVTileElems * 2u : live ? (nvis_v - k0) * 256u : 0u);
     c.buf = buf;
     return c;
   };
@@ -257,6 +276,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   for (int db = 0; db < 4; ++db)
     v_lane[db] = VOFF + g * V_HEAD + v_row * V_ROW +
                  (((db ^ (s16 >> 2)) * 4 + (q16 & 1) * 2 + ((s16 & 3) >> 1)) * 16) + (s16 & 1) * 8;
+  // blocked V: lane (ln, hf) reads feature db*32 + ln, keys c*16 + hf*8 .. +7
+  const int vb_lane = VOFF + ln * 32 + ((hf ^ ((ln >> 3) & 1)) * 16);  // + c*4096 + db*1024
 
   const float cl2 = p.scale_log2;
   const uint32_t ones = 0x3f803f80u;  // bf16 pair (1, 1)
@@ -304,6 +325,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     // waiting for those does not wait for the copies (the previous pass ended
     // with all waves past their last LDS read and no copy outstanding)
     auto stage = [&](int kt) { return lds + (kt % NSTAGE) * STAGE; };
+
 #pragma unroll
     for (int st = 0; st < NSTAGE - 1; ++st) copy_all(plan(stage(st), st, nkt));
 
@@ -361,14 +383,22 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
         pf[c] = as_bf16x8(w);
       }
       bf16x8 vf[4][2];
+      if constexpr (VB) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint8_t* vr = buf + v_lane[db];
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const s16x4 lo = ds_read_tr(vr + c * 16 * V_ROW);
-          const s16x4 hi = ds_read_tr(vr + c * 16 * V_ROW + 4 * V_ROW);
-          vf[db][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          for (int c = 0; c < 2; ++c)
+            vf[db][c] = *reinterpret_cast<const bf16x8*>(buf + vb_lane + c * 4096 + db * 1024);
+      } else {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const uint8_t* vr = buf + v_lane[db];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const s16x4 lo = ds_read_tr(vr + c * 16 * V_ROW);
+            const s16x4 hi = ds_read_tr(vr + c * 16 * V_ROW + 4 * V_ROW);
+            vf[db][c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -506,7 +536,12 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   q.paired = paired_blocks >= 2 * kComputeUnits ? 1 : 0;
   const long blocks = (long)p.B * HG * (q.paired ? (NQ + 1) / 2 : NQ);
   if (blocks <= 0 || blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, q);
+  if (p.v_blocked) {
+    if (p.past != 0 || p.LK != p.T || (p.T % 16 != 0 && !p.v_tail)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)blocks), dim3(NT), 0, stream, q);
+  } else {
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, stream, q);
+  }
   return hipGetLastError();
 }
 

@@ -75,6 +75,31 @@ hipError_t launch_rope_prep(const PrefillParams& p, hipStream_t stream) {
   return launch_rope(p.R, p.past, p.k_pe, p.cs, p.kpe_rot, p.LK, 0, p.B, p.T, stream);
 }
 
+// The last key tile of key-blocked V per head, its slots of positions T..
+// zeroed (the caller's padding may hold any bits): 8 KiB per (b, h), one
+// 16-byte piece (8 positions of one feature) per thread.
+__global__ __launch_bounds__(512) void v_tail_kernel(const uint16_t* __restrict__ v,
+                                                     uint16_t* __restrict__ tail, int T) {
+  const int bh = blockIdx.x, u = threadIdx.x;  // u = blk*256 + d*2 + half
+  const int NB = (T + 15) >> 4;
+  const int gb = 2 * ((T - 1) / 32) + (u >> 8);  // global block
+  const int key = gb * 16 + (u & 1) * 8;
+  u32x4 x = {0, 0, 0, 0};
+  if (gb < NB) x = *reinterpret_cast<const u32x4*>(v + ((size_t)bh * NB + gb) * 2048 + (u & 255) * 8);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    x[e] &= (key + 2 * e < T ? 0xffffu : 0u) | (key + 2 * e + 1 < T ? 0xffff0000u : 0u);
+  *reinterpret_cast<u32x4*>(tail + (size_t)bh * kVTileElems + u * 8) = x;
+}
+
+hipError_t launch_v_tail(const PrefillParams& p, hipStream_t stream) {
+  const long blocks = (long)p.B * p.H;
+  if (!p.v_blocked || !p.v_tail || p.T % 16 == 0 || blocks > 0x7fffffffL)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(v_tail_kernel, dim3((unsigned)blocks), dim3(512), 0, stream, p.v, p.v_tail, p.T);
+  return hipGetLastError();
+}
+
 hipError_t launch_append_rows(const uint16_t* src, uint16_t* dst, int BH, int T, int dst_rows,
                               int dst_off, hipStream_t stream) {
   const long n = (long)BH * T * 16;

@@ -228,3 +228,23 @@ def bits(t) -> np.ndarray:
     import torch
 
     return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def to_v_blocked(v, fill: float = 0.0):
+    """The key-blocked value layout (flag MLA_V_BLOCKED): v [B, H, T, 128] ->
+    [B, H, ceil(T/16), 128, 16], the 16 positions of a block stored feature
+    by feature; the slots past T hold ``fill``.  A copy in a new layout, no
+    arithmetic."""
+    import torch
+
+    B, H, T, D = v.shape
+    nb = (T + 15) // 16
+    padded = torch.full((B, H, nb * 16, D), fill, dtype=v.dtype, device=v.device)
+    padded[:, :, :T] = v
+    return padded.view(B, H, nb, 16, D).transpose(3, 4).contiguous()
+
+
+def from_v_blocked(vb, T: int):
+    """Inverse of to_v_blocked: [B, H, NB, 128, 16] -> [B, H, T, 128]."""
+    B, H, nb, D, _ = vb.shape
+    return vb.transpose(3, 4).reshape(B, H, nb * 16, D)[:, :, :T].contiguous()
