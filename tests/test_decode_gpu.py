@@ -178,3 +178,38 @@ def test_decode_shared_kpe_full_size_sampled(gpu_device):
             sb(d["v_cache"], b), d["R"].cpu().numpy(), q_pos, SCALE, np.array([[0, h]], np.int32))
         check_close(to_host64(o32[b, h * 128:(h + 1) * 128]), want[0], TOL, f"b={b} h={h}")
         check_close(to_host64(lse[b, h:h + 1]), wl, TOL, f"b={b} h={h} lse")
+
+
+@pytest.mark.parametrize("kind", ["rising", "falling", "spikes"])
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_decode_score_extremes(kind, splits, gpu_device):
+    """Scores that rise or fall along the cache (steps of ~0.3 nats per key:
+    the running maximum moves all the time, or the first key dominates and the
+    rest underflow), or random scores with a large bump on every 37th key; the
+    cached keys' rotary part is zero so the scores are q_nope·k_nope alone."""
+    B, H, L = 2, 3, 1500
+    say(f"decode score extremes {kind} splits={splits}")
+    d = inputs.decode_inputs(B, H, L, q_pos=L)
+    j = torch.arange(L, dtype=torch.float32).view(1, 1, L, 1)
+    k = d["k_cache"].float()
+    k[..., 128:] = 0
+    if kind == "rising":
+        d["q_nope"] = torch.ones_like(d["q_nope"])
+        k[..., :128] = 0.035 * j
+    elif kind == "falling":
+        d["q_nope"] = torch.ones_like(d["q_nope"])
+        k[..., :128] = 0.035 * (L - j)
+    else:
+        k[:, :, ::37, :128] += 4.0
+        d["q_nope"] = (d["q_nope"].float().abs() + 0.5).to(torch.bfloat16)
+    d["k_cache"] = k.to(torch.bfloat16)
+    want, want_lse = oracle_full(d)
+    out32, lse = run(d, gpu_device, num_splits=splits, out_f32=True, want_lse=True)
+    assert torch.isfinite(out32).all() and torch.isfinite(lse).all()
+    check_close(to_host64(out32), want, TOL, f"{kind}: float32 output vs oracle")
+    check_close(to_host64(lse), want_lse, TOL, f"{kind}: lse vs oracle")
+    d["v_cache"] = torch.ones_like(d["v_cache"])
+    ones, _ = run(d, gpu_device, num_splits=splits, out_f32=True)
+    err = (ones.double() - 1).abs().max().item()
+    say(f"  {kind}: V = 1 max |out - 1| {err:.2e}")
+    assert err <= SUM_TOL

@@ -231,3 +231,46 @@ def test_prefill_large_workloads_sampled(workload, gpu_device):
         g16 = out16[b, torch.from_numpy(rows).long().to(gpu_device), h * 128:(h + 1) * 128]
         check_bf16_close(g16, o, f"b={b} h={h} bf16")
     say(f"  worst {worst:.3e}")
+
+
+def _scored_inputs(T, kind, H=2):
+    """Inputs whose scores rise (every 32-key tile lifts the running maximum by
+    ~14 in log2 units, more than the lazy-rescale threshold of 8), fall (the
+    first key dominates and later weights underflow), or carry spikes (random
+    scores with a large bump on every 37th key): the rescale path and the
+    underflow of weights, which N(0, 1) inputs barely reach.  The rotary part
+    is zero so that the scores are q_nope·k_nope alone."""
+    d = inputs.prefill_inputs(1, H, T, workload=0)
+    j = torch.arange(T, dtype=torch.float32).view(1, 1, T, 1)
+    c = 0.035
+    if kind == "rising":
+        d["q_nope"] = torch.ones_like(d["q_nope"])
+        d["k_nope"] = (c * j).expand(1, H, T, 128).to(torch.bfloat16)
+    elif kind == "falling":
+        d["q_nope"] = torch.ones_like(d["q_nope"])
+        d["k_nope"] = (c * (T - j)).expand(1, H, T, 128).to(torch.bfloat16)
+    else:
+        k = d["k_nope"].float()
+        k[:, :, ::37] += 4.0
+        d["k_nope"] = k.to(torch.bfloat16)
+        d["q_nope"] = (d["q_nope"].float().abs() + 0.5).to(torch.bfloat16)
+    d["q_pe"] = torch.zeros_like(d["q_pe"])
+    return d
+
+
+@pytest.mark.parametrize("kind", ["rising", "falling", "spikes"])
+@pytest.mark.parametrize("T", [600, 1000])
+def test_prefill_score_extremes(kind, T, gpu_device):
+    say(f"prefill score extremes {kind} T={T}")
+    d = _scored_inputs(T, kind)
+    want, want_lse = oracle_full(d)
+    out32, lse = run(d, gpu_device, out_f32=True, want_lse=True)
+    assert torch.isfinite(out32).all() and torch.isfinite(lse).all()
+    check_close(to_host64(out32), want, TOL, f"{kind}: float32 output vs oracle")
+    check_close(to_host64(lse), want_lse, TOL, f"{kind}: lse vs oracle")
+    # V = 1: whatever the rescaling, the weights that multiply V sum to the normaliser
+    d["v"] = torch.ones_like(d["v"])
+    ones, _ = run(d, gpu_device, out_f32=True)
+    err = (ones - 1).abs().max().item()
+    say(f"  {kind}: V = 1 max |out - 1| {err:.2e}")
+    assert err <= SUM_TOL
