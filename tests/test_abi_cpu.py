@@ -426,3 +426,13 @@ def test_oproj_fp8_q_workspace():
     # 4 K splits at M = 64: float32 partials only (no room for codes or scales)
     assert mla.mla_out_proj_fp8_q_workspace_bytes(64, 8192, 7168) == 4 * 64 * 7168 * 4
     assert mla.mla_out_proj_fp8_q_workspace_bytes(64, 100, 7168) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No fallback: without the built library every entry point raises."""
+    monkeypatch.setattr(mla, "_lib", None)
+    monkeypatch.setattr(mla, "LIB_PATH", "/nonexistent/libmla.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        mla.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        mla.mla_prefill_workspace_bytes(1, 1, 1)
