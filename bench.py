@@ -102,6 +102,53 @@ def measured_mfma_tflops(mla, torch, dev, kind=0, reps=5):
     return mla.mla_mfma_probe_flops(iters, kind) / (statistics.median(times) * 1e-3) / 1e12
 
 
+def clock_under_load(fn, torch, seconds=2.5):
+    """Graphics clock of the GPU while `fn` (one call of a kernel path) runs back
+    to back for about `seconds`: `amd-smi metric -c` sampled from a thread, the
+    median over samples of each XCD's current clock.  None when amd-smi is not
+    available or reports no clock."""
+    import json
+    import shutil
+    import subprocess
+    import threading
+
+    smi = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if smi is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([smi, "metric", "-g", "0", "-c", "--json"], capture_output=True,
+                                   text=True, timeout=30)
+                clk = json.loads(r.stdout)["gpu_data"][0]["clock"]
+                xcd = [v["clk"]["value"] for k, v in sorted(clk.items()) if k.startswith("gfx_")]
+                if xcd and all(isinstance(x, (int, float)) for x in xcd):
+                    samples.append(xcd)
+            except Exception:
+                return
+
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds or (not samples and time.perf_counter() - t0 < 4 * seconds):
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=60)
+    if len(samples) < 2:
+        return None
+    samples = samples[1:]  # the first sample may straddle the start of the load
+    per_xcd = [statistics.median(col) for col in zip(*samples)]
+    return {"mhz_median": statistics.median(per_xcd), "mhz_per_xcd": per_xcd, "samples": len(samples),
+            "source": "amd-smi metric -c (current gfx clock per XCD), sampled while the call repeats"}
+
+
 class Timer:
     """Median call time with HIP events on the current stream, warm and cold.
 
@@ -571,6 +618,9 @@ def main():
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the extra figures: prefill at T=64, 1024 and 16384, and decode "
                          "with the shared-rotary cache layout")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the graphics clock (amd-smi) under the prefill and the probe "
+                         "(--no-other-configs skips it as well)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, run a plain streaming kernel over 1 GiB (read 1 GiB, "
                          "write 1 GiB) three times, to scale hardware byte counters")
@@ -688,6 +738,14 @@ def main():
             "attention_plus_oproj_tflops": (fa + fo) / (ta + to) / 1e12}
         mfma_tf = measured_mfma_tflops(mla, torch, dev, kind=0)
         res["measured_mfma_tflops"] = {"bf16": mfma_tf, "fp8_e4m3": measured_mfma_tflops(mla, torch, dev, kind=1)}
+        if not (args.no_clock or args.no_other_configs):  # the profiled runs leave it out too
+            probe_out = torch.empty(mla.MLA_MFMA_PROBE_OUT, dtype=torch.float32, device=dev)
+            res["clock_under_load"] = {
+                "prefill_attention": clock_under_load(lambda: mla.mla_attend_prefill(
+                    d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], v_blk, d["R"], scale,
+                    out=attn_out, workspace=ws_p, v_blocked=True), torch),
+                "mfma_probe_bf16": clock_under_load(lambda: mla.mla_mfma_probe(32768, 0, out=probe_out), torch)}
+            del probe_out
         res["prefill"]["exp_count"] = B * H * T * (T + 1) // 2
         res["roofline"] = {"bound": "mfma", "achieved": fa / ta / 1e12, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": fa / ta / 1e12 / PEAK_BF16_TFLOPS,
