@@ -86,8 +86,10 @@ def measured_copy_gbps(torch, dev, reps=5):
 def measured_mfma_tflops(mla, torch, dev, kind=0, reps=5):
     """Matrix-core rate this GPU sustains with every compute unit busy (the
     library's probe: MFMA chains on register operands, no memory traffic;
-    kind 0 bf16, kind 1 e4m3), median of a few launches of about 5 ms each."""
-    iters = 32768 if kind == 0 else 16384
+    kind 0 bf16, kind 1 e4m3 on fixed operands, kinds 2 and 3 the same on
+    random operands that change with every instruction), median of a few
+    launches of about 5 ms each."""
+    iters = 32768 if kind in (0, 2) else 16384
     out = torch.empty(mla.MLA_MFMA_PROBE_OUT, dtype=torch.float32, device=dev)
     mla.mla_mfma_probe(iters, kind, out=out)
     times = []
@@ -736,15 +738,21 @@ def main():
             "oproj_ms": avg["prefill_oproj"], "oproj_tflops": fo / to / 1e12,
             "oproj_frac_peak": fo / to / 1e12 / PEAK_BF16_TFLOPS,
             "attention_plus_oproj_tflops": (fa + fo) / (ta + to) / 1e12}
-        mfma_tf = measured_mfma_tflops(mla, torch, dev, kind=0)
-        res["measured_mfma_tflops"] = {"bf16": mfma_tf, "fp8_e4m3": measured_mfma_tflops(mla, torch, dev, kind=1)}
+        mfma_fixed = measured_mfma_tflops(mla, torch, dev, kind=0)
+        mfma_tf = measured_mfma_tflops(mla, torch, dev, kind=2)
+        res["measured_mfma_tflops"] = {
+            "bf16_random_operands": mfma_tf, "bf16": mfma_fixed,
+            "fp8_e4m3_random_operands": measured_mfma_tflops(mla, torch, dev, kind=3),
+            "fp8_e4m3": measured_mfma_tflops(mla, torch, dev, kind=1)}
         if not (args.no_clock or args.no_other_configs):  # the profiled runs leave it out too
             probe_out = torch.empty(mla.MLA_MFMA_PROBE_OUT, dtype=torch.float32, device=dev)
             res["clock_under_load"] = {
                 "prefill_attention": clock_under_load(lambda: mla.mla_attend_prefill(
                     d["q_nope"], d["q_pe"], d["k_nope"], d["k_pe"], v_blk, d["R"], scale,
                     out=attn_out, workspace=ws_p, v_blocked=True), torch),
-                "mfma_probe_bf16": clock_under_load(lambda: mla.mla_mfma_probe(32768, 0, out=probe_out), torch)}
+                "mfma_probe_bf16": clock_under_load(lambda: mla.mla_mfma_probe(32768, 0, out=probe_out), torch),
+                "mfma_probe_bf16_random_operands": clock_under_load(
+                    lambda: mla.mla_mfma_probe(32768, 2, out=probe_out), torch)}
             del probe_out
         res["prefill"]["exp_count"] = B * H * T * (T + 1) // 2
         res["roofline"] = {"bound": "mfma", "achieved": fa / ta / 1e12, "peak": PEAK_BF16_TFLOPS,
@@ -753,7 +761,9 @@ def main():
                            "kernel": "prefill_kernel (+ rope_prep_kernel)",
                            "per_launch": f"{fa:.4e} causal flops",
                            "measured_mfma_tflops": mfma_tf,
-                           "frac_of_measured_mfma": fa / ta / 1e12 / mfma_tf}
+                           "measured_mfma_operands": "random, changing with every instruction (probe kind 2)",
+                           "frac_of_measured_mfma": fa / ta / 1e12 / mfma_tf,
+                           "measured_mfma_tflops_fixed_operands": mfma_fixed}
         parts.append(f"prefill B={B} T={T} H={H} causal + o_proj [{B * T}x{K_O}]x[{K_O}x{N_O}]")
         cfg.update({"prefill_batch": B, "prefill_seq_len": T,
                     "prefill_v_layout": "key-blocked [B,H,T/16,128,16] (MLA_V_BLOCKED)"})

@@ -452,13 +452,25 @@ int mla_up_project(const mla_bf16 *q_lat, const mla_bf16 *ckv, const mla_bf16 *w
  * (two waves per SIMD), each wave running `iters` rounds of four independent
  * MFMA chains on register operands, with no memory traffic in the loop:
  * kind 0 v_mfma_f32_32x32x16_bf16 (the attention and bf16 GEMM products),
- * kind 1 v_mfma_f32_32x32x64_f8f6f4 on e4m3 operands (the FP8 o_proj).  It
- * performs mla_mfma_probe_flops(iters, kind) floating-point operations (0
- * when iters or kind is out of range).
+ * kind 1 v_mfma_f32_32x32x64_f8f6f4 on e4m3 operands (the FP8 o_proj), each
+ * on operands that stay the same from one instruction to the next; kinds 2
+ * (bf16) and 3 (e4m3) cycle every chain through eight random operand sets,
+ * so the matrix cores switch bits as on real data -- the switching power
+ * then lowers the clock the chip holds, and these are the rates to read a
+ * kernel on random inputs against.  Operand sets: xorshift32 (shifts 13, 17,
+ * 5) seeded with 0x9e3779b9 * (thread + 1) xor iters, for each set and
+ * element one draw for A then one for B (four per 4-byte group for e4m3):
+ * bf16 A = ±(1 + (h & 0xffff)·2^-16), B = ±(0.5 + (h & 0xffff)·2^-17), the
+ * sign from bit 16, rounded to nearest even; e4m3 byte = bit 7 of h>>7 (sign)
+ * | (5 + (h>>3) mod 5) << 3 | (h & 7); chain c at step v (iteration 8j + v)
+ * multiplies A set (v + c) mod 8 by B set (v + 3c) mod 8.  It performs
+ * mla_mfma_probe_flops(iters, kind) floating-point operations (0 when iters
+ * or kind is out of range).
  *
  *   out    device, float32, MLA_MFMA_PROBE_OUT elements, 16-byte aligned,
  *          caller-owned; receives per-thread sums of the products
- *   iters  1 .. 2^24, kind 0 or 1 (else MLA_ERR_DIM)
+ *   iters  1 .. 2^24 (a multiple of 8 for kinds 2 and 3), kind 0 .. 3 (else
+ *          MLA_ERR_DIM)
  *
  * Errors: out NULL MLA_ERR_NULL, misaligned MLA_ERR_ALIGN, not gfx950
  * MLA_ERR_DEVICE.  Asynchronous on `stream`; time it with events on it.

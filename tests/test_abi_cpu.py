@@ -41,12 +41,17 @@ def test_mfma_probe_rejects_and_counts():
     assert mla.mla_mfma_probe_flops(1000, 0) == 1000 * mla.mla_mfma_probe_flops(1, 0)
     assert mla.mla_mfma_probe_flops(0, 0) == 0.0
     assert mla.mla_mfma_probe_flops((1 << 24) + 1, 0) == 0.0
-    assert mla.mla_mfma_probe_flops(1, 2) == 0.0
+    assert mla.mla_mfma_probe_flops(8, 2) == 8 * mla.mla_mfma_probe_flops(1, 0)
+    assert mla.mla_mfma_probe_flops(8, 3) == 8 * mla.mla_mfma_probe_flops(1, 1)
+    assert mla.mla_mfma_probe_flops(10, 2) == 0.0  # random-operand kinds: multiples of 8
+    assert mla.mla_mfma_probe_flops(8, 4) == 0.0
     assert L.mla_mfma_probe(None, 10, 0, None) == NULL
     assert L.mla_mfma_probe(A[0], 0, 0, None) == DIM
     assert L.mla_mfma_probe(A[0], (1 << 24) + 1, 0, None) == DIM
     assert L.mla_mfma_probe(A[0], 10, -1, None) == DIM
     assert L.mla_mfma_probe(A[0], 10, 2, None) == DIM
+    assert L.mla_mfma_probe(A[0], 12, 3, None) == DIM
+    assert L.mla_mfma_probe(A[0], 16, 4, None) == DIM
     assert L.mla_mfma_probe(ctypes.c_void_p(16 * GB + 4), 10, 0, None) == ALIGN
 
 

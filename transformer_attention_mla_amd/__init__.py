@@ -692,8 +692,10 @@ def mla_mfma_probe_flops(iters: int, kind: int = 0) -> float:
 def mla_mfma_probe(iters, kind=0, *, out=None, device=None, stream=None):
     """One launch of the matrix-core rate probe (a measurement helper, not a
     step of the path): mla_mfma_probe_flops(iters, kind) flops of MFMA chains
-    on every compute unit, kind 0 bf16 32x32x16, kind 1 e4m3 32x32x64.
-    Returns the out buffer (float32 per-thread sums of the products)."""
+    on every compute unit, kind 0 bf16 32x32x16, kind 1 e4m3 32x32x64 on fixed
+    operands; kinds 2 (bf16) and 3 (e4m3) on random operands that change with
+    every instruction (iters a multiple of 8).  Returns the out buffer
+    (float32 per-thread sums of the products)."""
     torch = _torch()
     dev = out.device if out is not None else torch.device(device or "cuda:0")
     if out is None:

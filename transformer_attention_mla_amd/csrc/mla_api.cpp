@@ -824,14 +824,14 @@ int mla_out_proj_fp8_dyn(const mla_bf16* x, const uint8_t* w8, const float* w_sc
 
 // ------------------------------------------------------ matrix-core probe
 double mla_mfma_probe_flops(int iters, int kind) {
-  if (iters < 1 || iters > (1 << 24) || kind < 0 || kind > 1) return 0.0;
+  if (!mla::probe_args_ok(iters, kind)) return 0.0;
   return (double)mla::kProbeBlocks * (mla::kProbeThreads / 64) * mla::kProbeChains * (double)iters *
          mla::kProbeFlopsPerMfma[kind];
 }
 
 int mla_mfma_probe(float* out, int iters, int kind, void* stream) {
   if (!out) return MLA_ERR_NULL;
-  if (iters < 1 || iters > (1 << 24) || kind < 0 || kind > 1) return MLA_ERR_DIM;
+  if (!mla::probe_args_ok(iters, kind)) return MLA_ERR_DIM;
   if (!aligned16(out)) return MLA_ERR_ALIGN;
   const int dev = check_device();
   if (dev != MLA_OK) return dev;
