@@ -556,9 +556,34 @@ __global__ __launch_bounds__(WNT) void oproj_wide_kernel(OprojParams p) {
 }
 
 // y = sum over splits of the float32 partials, in split order.
+// Sum of the split-K partials, in split order: four consecutive outputs per
+// thread with 16-byte loads (all splits' loads issued before the sums) when
+// M*N is a multiple of 4, one per thread otherwise.
 __global__ __launch_bounds__(256) void oproj_reduce_kernel(OprojParams p) {
   const size_t total = (size_t)p.M * p.N;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
+  if ((total & 3) == 0) {
+    const f32x4* part = reinterpret_cast<const f32x4*>(p.part);
+    const size_t total4 = total >> 2;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total4; i += stride) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      int s = 0;
+      for (; s + 4 <= p.splits; s += 4) {
+        f32x4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = part[(size_t)(s + j) * total4 + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc += v[j];
+      }
+      for (; s < p.splits; ++s) acc += part[(size_t)s * total4 + i];
+      if (p.out_f32) {
+        reinterpret_cast<f32x4*>(p.y)[i] = acc;
+      } else {
+        reinterpret_cast<u32x2*>(p.y)[i] = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+      }
+    }
+    return;
+  }
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
     float acc = 0.f;
     for (int s = 0; s < p.splits; ++s) acc += p.part[(size_t)s * total + i];
@@ -910,6 +935,14 @@ int oproj_choose_splits(int M, int K, int N, bool fp8) {
   return best;
 }
 
+static unsigned reduce_blocks(const OprojParams& p) {
+  const size_t total = (size_t)p.M * p.N;
+  const size_t items = (total & 3) == 0 ? total >> 2 : total;
+  size_t blocks = (items + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  return (unsigned)blocks;
+}
+
 hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
   OprojParams p = p_in;
   if (p.hd > 0 && (p.splits != 1 || p.w8 || p.T <= 0 || p.M % p.T != 0 || p.N % p.hd != 0 ||
@@ -941,10 +974,7 @@ hipError_t launch_oproj(const OprojParams& p_in, hipStream_t stream) {
     hipLaunchKernelGGL((oproj_kernel<false, OBM, OBK>), grid, dim3(ONT), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  const size_t total = (size_t)p.M * p.N;
-  size_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(oproj_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(oproj_reduce_kernel, dim3(reduce_blocks(p)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1013,10 +1043,7 @@ hipError_t launch_oproj_fp8dyn(const OprojParams& p_in, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  const size_t total = (size_t)p.M * p.N;
-  size_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(oproj_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(oproj_reduce_kernel, dim3(reduce_blocks(p)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
