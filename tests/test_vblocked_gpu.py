@@ -75,12 +75,14 @@ def test_prefill_vblocked_padding_never_read(T, fill, gpu_device):
     assert_same(got_lse, want_lse, "padding slots reached the lse")
 
 
-def test_prefill_vblocked_full_workload(gpu_device):
-    """B = 4, T = 4096, H = 64 (the paired launch that is timed with this
-    layout): bit-identical to the natural layout."""
-    B, H, T = 4, 64, 4096
+@pytest.mark.parametrize("B,T,workload", [(4, 4096, 3), (1, 16384, 4)])
+def test_prefill_vblocked_full_workload(B, T, workload, gpu_device):
+    """The timed workloads with this layout (B = 4, T = 4096 and B = 1,
+    T = 16384 with the YaRN table, 64 heads, paired launches): bit-identical
+    to the natural layout."""
+    H = 64
     say(f"prefill key-blocked v full B={B} H={H} T={T}")
-    g = inputs.prefill_inputs(B, H, T, workload=3, device=gpu_device)
+    g = inputs.prefill_inputs(B, H, T, workload=workload, device=gpu_device)
     vb = inputs.to_v_blocked(g["v"])
     want, want_lse = prefill(g, g["v"])
     got, got_lse = prefill(g, vb, v_blocked=True)
