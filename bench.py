@@ -36,22 +36,22 @@ CSRC = os.path.join(REPO, "transformer_attention_mla_amd", "csrc")
 # bytes written).  Each figure holds only for the kernel source it was taken on,
 # identified by a hash of its files; after any change the figure is dropped.
 MEASURED_TRAFFIC = {
-    "prefill_kernel": ("2478cc0ad31a8ba1", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
-                       1998480586, "profiles/prefill_kernel_B4_T4096_H64.txt"),
-    "decode_split_kernel": ("6931c1b00c67b632", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                            21477803704, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
-    "decode_split_kernel_shared_kpe": ("6931c1b00c67b632", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
-                                       17249617026, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
-    "latent_decode_kernel": ("772ba3d56ca0bcba", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
-                             657395000, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
+    "prefill_kernel": ("627c9cd07391280c", ("mla_prefill.hip", "mla_device.h", "mla_internal.h"),
+                       2000857886, "profiles/prefill_kernel_B4_T4096_H64.txt"),
+    "decode_split_kernel": ("b78a42ed2d076e13", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                            21477804714, "profiles/decode_split_kernel_B64_L8192_H64.txt"),
+    "decode_split_kernel_shared_kpe": ("b78a42ed2d076e13", ("mla_decode.hip", "mla_device.h", "mla_internal.h"),
+                                       17249596301, "profiles/decode_split_kernel_shared_kpe_B64_L8192_H64.txt"),
+    "latent_decode_kernel": ("cb36bcf1f93f9034", ("mla_latent.hip", "mla_device.h", "mla_internal.h"),
+                             657394973, "profiles/latent_decode_kernel_B64_L8192_H64.txt"),
 }
 # o_proj GEMM kernels at K = 8192, N = 7168 (the split-K reduce kernel, shared
 # by several paths, is left out), M = 16384 and M = 64.
-_OPROJ_SRC = ("aada04cf5917f854", ("mla_oproj.hip", "mla_device.h", "mla_internal.h"))
+_OPROJ_SRC = ("2c293fa82d067509", ("mla_oproj.hip", "mla_device.h", "mla_internal.h"))
 _OPROJ_PROFILE = "profiles/oproj_kernel_M16384_K8192_N7168_and_M64.txt"
-for _k, _v in {"oproj_bf16_M16384": 3198813897, "oproj_bf16_M64": 140684388,
-               "oproj_fp8_M16384": 176252165 + 3193205869, "oproj_fp8_M64": 81988146,
-               "oproj_fp8_dyn_M16384": 1728930554 + 411080085, "oproj_fp8_dyn_M64": 70562978 + 1647660}.items():
+for _k, _v in {"oproj_bf16_M16384": 3204206167, "oproj_bf16_M64": 140699657,
+               "oproj_fp8_M16384": 176252089 + 3193876463, "oproj_fp8_M64": 81981659,
+               "oproj_fp8_dyn_M16384": 1728777594 + 411079737, "oproj_fp8_dyn_M64": 70560848 + 1647659}.items():
     MEASURED_TRAFFIC[_k] = _OPROJ_SRC + (_v, _OPROJ_PROFILE)
 
 

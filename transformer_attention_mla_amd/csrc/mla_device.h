@@ -47,6 +47,20 @@ __device__ __forceinline__ u32x4 ld_stream_16(const void* p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// a / s rounded as the e4m3 quantizer needs it, from y = 1/s (correctly
+// rounded, computed once per block): q = a*y, the residual a - q*s exact by
+// FMA, one correction q + r*y (Markstein's iteration).  For every block scale
+// s = max(amax, 1e-4)/448 and every bf16 value |a| <= amax this equals the
+// correctly rounded a / s bit for bit wherever |a/s| > 2^-11, and elsewhere has
+// its sign and magnitude <= 2^-10 -- both round to the same e4m3 code (checked
+// exhaustively on the host over all bf16 amax and a).  An exact quotient (r = 0,
+// a = +-0 included) is returned as q, which keeps the sign of zero.
+__device__ __forceinline__ float div_by_scale(float a, float s, float y) {
+  const float q = __fmul_rn(a, y);
+  const float r = __fmaf_rn(-q, s, a);
+  return r == 0.0f ? q : __fmaf_rn(r, y, q);
+}
+
 // gfx950 transposing LDS read (ds_read_b64_tr_b16), per 16-lane group: each
 // lane addresses 8 bytes (four 16-bit elements); lane i receives element i%4
 // of the pieces that lanes i/4, i/4+4, i/4+8 and i/4+12 address, in that order.

@@ -613,8 +613,9 @@ __global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint8_t* __restr
 // Page "Block input", config.json quantization_config: e4m3 with the
 // activation scheme "dynamic".  One 128-column block per 16 lanes (8 values
 // per lane): block maximum by a 16-lane butterfly, scale = max(amax, 1e-4) /
-// 448 and codes e4m3(x / scale), the divisions correctly rounded float32 and
-// v_cvt_pk_fp8_f32 rounding to nearest even.  The scales are stored
+// 448 and codes e4m3(x / scale), the quotients those of correctly rounded
+// float32 divisions (one division per block for the reciprocal, then
+// div_by_scale per value) and v_cvt_pk_fp8_f32 rounding to nearest even.  The scales are stored
 // transposed, [K/128][M], so that one slab's scales for a tile of rows are
 // contiguous (the GEMM copies them into LDS with its tiles), row stride
 // act_scale_stride(M).
@@ -642,12 +643,15 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   for (int o = 1; o < 16; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, 16));
   a = fmaxf(a, 1e-4f);
   const float sc = a / 448.0f;
+  const float ry = 1.0f / sc;
   u32x2 q;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     int w = 0;
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h] / sc, v[4 * h + 1] / sc, w, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h + 2] / sc, v[4 * h + 3] / sc, w, true);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_scale(v[4 * h], sc, ry), div_by_scale(v[4 * h + 1], sc, ry),
+                                        w, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_scale(v[4 * h + 2], sc, ry),
+                                        div_by_scale(v[4 * h + 3], sc, ry), w, true);
     q[h] = (uint32_t)w;
   }
   *reinterpret_cast<u32x2*>(x8 + off) = q;

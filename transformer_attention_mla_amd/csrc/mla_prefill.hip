@@ -436,8 +436,9 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
       // FP8 output: the bf16-rounded outputs of this query and head (64 per
       // lane, the other 64 in lane ^ 32) are one 128-column block of the
       // o_proj input; scale = max(block amax, 1e-4) / 448, codes e4m3(x /
-      // scale) with the divisions correctly rounded -- the arithmetic of the
-      // activation quantizer, so the codes equal its codes of the bf16 output.
+      // scale) with the quotients those of correctly rounded divisions (via
+      // div_by_scale) -- the arithmetic of the activation quantizer, so the
+      // codes equal its codes of the bf16 output.
       const float l_tot = sum_halves(l_run);
       const float inv = 1.0f / l_tot;
       float amax = 0.f;
@@ -449,6 +450,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
           amax = fmaxf(amax, fabsf(acc[db][r]));
         }
       const float sc = fmaxf(max_halves(amax), 1e-4f) / 448.0f;
+      const float ry = 1.0f / sc;
       if (myq < T) {
         const size_t row = (size_t)b * T + myq;
         uint8_t* dst = p.out8 + row * ((size_t)H * kV) + (size_t)head * kV;
@@ -457,8 +459,10 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq) {
             int w = 0;
-            w = __builtin_amdgcn_cvt_pk_fp8_f32(acc[db][gq * 4 + 0] / sc, acc[db][gq * 4 + 1] / sc, w, false);
-            w = __builtin_amdgcn_cvt_pk_fp8_f32(acc[db][gq * 4 + 2] / sc, acc[db][gq * 4 + 3] / sc, w, true);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_scale(acc[db][gq * 4 + 0], sc, ry),
+                                                div_by_scale(acc[db][gq * 4 + 1], sc, ry), w, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(div_by_scale(acc[db][gq * 4 + 2], sc, ry),
+                                                div_by_scale(acc[db][gq * 4 + 3], sc, ry), w, true);
             *reinterpret_cast<uint32_t*>(dst + db * 32 + gq * 8 + hf * 4) = (uint32_t)w;
           }
         if (hf == 0) {
