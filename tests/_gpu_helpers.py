@@ -41,6 +41,7 @@ def check_bf16_is_rne_of_f32(out_bf16, out_f32):
 
 
 def check_close(got, want, tol, what):
+    assert got.shape == want.shape, f"{what}: shape {got.shape} against {want.shape}"
     err = np.max(np.abs(got - want)) if got.size else 0.0
     say(f"  {what}: max-abs {err:.3e} (tol {tol:.1e})")
     assert err <= tol, f"{what}: {err} > {tol}"
