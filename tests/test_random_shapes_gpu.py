@@ -1,6 +1,7 @@
 """Seeded random shapes through every entry point against the oracle, on top
-of the chosen shapes of the other parity tests: ragged sizes nobody picked,
-split counts, K depths, past offsets.  Gates as elsewhere: float32 outputs
+of the chosen shapes of the other parity tests (all three decode cache
+layouts included): ragged sizes nobody picked, split counts, K depths, past
+offsets.  Gates as elsewhere: float32 outputs
 and lse within 1e-2 of the fp64 oracle (the up-projection within 1e-4), the
 key-blocked value layout bit-identical to the natural one with NaN in its
 padding slots."""
@@ -27,6 +28,10 @@ OPROJ = [(_rng.choice([1, 3, 17, 33, 64, 65, 130, 300, _rng.randint(1, 1200)]), 
 CHUNK = [(_rng.choice([1, 2]), _rng.choice([1, 3, 8]), _rng.randint(1, 300), _rng.randint(0, 500))
          for _ in range(6)]
 UP = [(_rng.choice([1, 2, 3]), _rng.randint(1, 400), _rng.choice([1, 2, 4, 8])) for _ in range(6)]
+SHARED = [(_rng.choice([1, 2, 5]), _rng.choice([1, 4, 16, 64]), _rng.randint(1, 2000),
+           _rng.choice([0, 1, 3, 9])) for _ in range(6)]
+LATENT = [(_rng.choice([1, 3, 17]), _rng.choice([1, 5, 16, 33, 64]), _rng.randint(1, 1500),
+           _rng.choice([0, 1, 2, 7])) for _ in range(6)]
 
 
 @pytest.mark.parametrize("B,H,T", PREFILL)
@@ -109,3 +114,33 @@ def test_random_up_project(B, T, H, gpu_device):
     for a, w, name in zip(got, want, ("q_nope", "q_pe", "k_nope", "v")):
         check_close(to_host64(a), w, 1e-4, f"{name} vs oracle")
     assert torch.equal(inputs.from_v_blocked(gotb[3], T), got[3])
+
+
+@pytest.mark.parametrize("B,H,L,splits", SHARED)
+def test_random_decode_shared_kpe(B, H, L, splits, gpu_device):
+    say(f"random decode, shared rotary key, B={B} H={H} L={L} splits={splits}")
+    d = inputs.decode_shared_kpe_inputs(B, H, L, q_pos=L + 1)
+    want, want_lse = oracle.decode_shared_kpe(bits(d["q_nope"]), bits(d["q_pe"]), bits(d["k_nope_cache"]),
+                                              bits(d["kpe_cache"]), bits(d["v_cache"]), d["R"].numpy(),
+                                              d["q_pos"], SCALE)
+    g = {k: (v.to(gpu_device) if torch.is_tensor(v) else v) for k, v in d.items()}
+    out, lse = mla.mla_attend_decode_shared_kpe(g["q_nope"], g["q_pe"], g["k_nope_cache"], g["kpe_cache"],
+                                                g["v_cache"], g["R"], g["q_pos"], SCALE, num_splits=splits,
+                                                out_f32=True, want_lse=True)
+    torch.cuda.synchronize()
+    check_close(to_host64(out), want, TOL, "output vs oracle")
+    check_close(to_host64(lse), want_lse, TOL, "lse vs oracle")
+
+
+@pytest.mark.parametrize("B,H,L,splits", LATENT)
+def test_random_decode_latent(B, H, L, splits, gpu_device):
+    say(f"random decode, latent cache, B={B} H={H} L={L} splits={splits}")
+    d = inputs.decode_latent_inputs(B, H, L, q_pos=L + 2)
+    want, want_lse = oracle.decode_latent(bits(d["q_nope"]), bits(d["q_pe"]), bits(d["ckv"]), bits(d["kpe"]),
+                                          bits(d["w_kv_b"]), d["R"].numpy(), d["q_pos"], SCALE)
+    g = {k: (v.to(gpu_device) if torch.is_tensor(v) else v) for k, v in d.items()}
+    out, lse = mla.mla_attend_decode_latent(g["q_nope"], g["q_pe"], g["ckv"], g["kpe"], g["w_kv_b"], g["R"],
+                                            g["q_pos"], SCALE, num_splits=splits, out_f32=True, want_lse=True)
+    torch.cuda.synchronize()
+    check_close(to_host64(out), want, TOL, "output vs oracle")
+    check_close(to_host64(lse), want_lse, TOL, "lse vs oracle")
